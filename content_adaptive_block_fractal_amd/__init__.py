@@ -1,0 +1,265 @@
+"""Content-adaptive block-sparse video attention on MI355X (gfx950).
+
+Thin Python binding of libcabf.so, the C ABI declared in include/cabf.h.
+Each ``cabf_*`` function here has the same name and arguments as its C
+counterpart: it checks tensor shapes, dtypes and devices, passes raw device
+pointers and the current HIP stream, and raises ``CabfError`` on a non-zero
+status. Every step of the path runs in the HIP kernels; PyTorch only provides
+device memory and the stream. The helpers at the bottom (``permute``,
+``build_block_mask``, ``bsa_forward``, ``unpermute``, ``layer``) allocate the
+outputs and call the same entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcabf.so")
+
+CABF_OK, CABF_EINVAL, CABF_EUNSUPPORTED, CABF_EWORKSPACE, CABF_EHIP = 0, -1, -2, -3, -4
+CABF_BF16, CABF_F32 = 0, 1
+
+EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_unpermute", "cabf_mask_workspace_bytes",
+            "cabf_build_block_mask", "cabf_bsa_forward", "cabf_status_string")
+
+
+class CabfError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({cabf_status_string(status)})")
+        self.status = status
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("P", ctypes.c_int32)]
+
+
+class _Sta(ctypes.Structure):
+    _fields_ = [("enabled", ctypes.c_int32), ("dt", ctypes.c_int32), ("dy", ctypes.c_int32),
+                ("dx", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m content_adaptive_block_fractal_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    G = ctypes.POINTER(_Geom)
+    sig = {
+        "cabf_geom_sizes": (ctypes.c_int, [G, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                           ctypes.POINTER(I32)]),
+        "cabf_permute": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, P, P]),
+        "cabf_unpermute": (ctypes.c_int, [G, ctypes.c_int, P, P, P]),
+        "cabf_mask_workspace_bytes": (SZ, [G]),
+        "cabf_build_block_mask": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, F32,
+                                                 ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
+        "cabf_bsa_forward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, F32, P, P, P]),
+        "cabf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+@dataclass(frozen=True)
+class Geom:
+    """Layer geometry (cabf_geom): P x P patches of a T x H x W latent grid."""
+    batch: int
+    heads: int
+    head_dim: int
+    T: int
+    H: int
+    W: int
+    P: int = 8
+
+    def c(self) -> _Geom:
+        return _Geom(self.batch, self.heads, self.head_dim, self.T, self.H, self.W, self.P)
+
+    def sizes(self) -> dict:
+        """Derived sizes from the library: tokens (raster / padded), blocks, Hp, Wp."""
+        nr, npd = ctypes.c_int64(), ctypes.c_int64()
+        nb, hp, wp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        st = _lib.cabf_geom_sizes(ctypes.byref(self.c()), ctypes.byref(nr), ctypes.byref(npd),
+                                  ctypes.byref(nb), ctypes.byref(hp), ctypes.byref(wp))
+        _check("cabf_geom_sizes", st)
+        return dict(tokens_raster=nr.value, tokens_padded=npd.value, n_blocks=nb.value,
+                    Hp=hp.value, Wp=wp.value)
+
+
+def cabf_status_string(status: int) -> str:
+    return _lib.cabf_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != CABF_OK:
+        raise CabfError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CABF_BF16
+    if t.dtype == torch.float32:
+        return CABF_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, shape, dtype=None, name="tensor"):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def cabf_permute(geom: Geom, q, k, v, qp, kp, vp):
+    """Fractal reorder raster q, k, v [B, h, T*H*W, d] into qp, kp, vp [B, h, N, d]."""
+    s = geom.sizes()
+    rs = (geom.batch, geom.heads, s["tokens_raster"], geom.head_dim)
+    ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
+    first = next((t for t in (q, k, v) if t is not None), None)
+    if first is None:
+        return
+    dt = first.dtype
+    ptrs = []
+    for src, dst, n in ((q, qp, "q"), (k, kp, "k"), (v, vp, "v")):
+        if src is None and dst is None:
+            ptrs += [None, None]
+            continue
+        ptrs += [_dev(src, rs, dt, n), _dev(dst, ps, dt, n + "p")]
+    st = _lib.cabf_permute(ctypes.byref(geom.c()), _dtype_code(first), ptrs[0], ptrs[2], ptrs[4],
+                           ptrs[1], ptrs[3], ptrs[5], _stream(first))
+    _check("cabf_permute", st)
+
+
+def cabf_unpermute(geom: Geom, op, o):
+    """Restore raster order: op [B, h, N, d] -> o [B, h, T*H*W, d]."""
+    s = geom.sizes()
+    st = _lib.cabf_unpermute(
+        ctypes.byref(geom.c()), _dtype_code(op),
+        _dev(op, (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim), None, "op"),
+        _dev(o, (geom.batch, geom.heads, s["tokens_raster"], geom.head_dim), op.dtype, "o"),
+        _stream(op))
+    _check("cabf_unpermute", st)
+
+
+def cabf_mask_workspace_bytes(geom: Geom) -> int:
+    return int(_lib.cabf_mask_workspace_bytes(ctypes.byref(geom.c())))
+
+
+def cabf_build_block_mask(geom: Geom, qp, kp, scale: float, thr: float, sta, kv_count, kv_index,
+                          block_prob, workspace):
+    """Adaptive block mask into kv_count [B, h, nb] / kv_index [B, h, nb, nb] (int32)."""
+    s = geom.sizes()
+    nb = s["n_blocks"]
+    ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
+    lead = (geom.batch, geom.heads, nb)
+    sta_c = None
+    if sta is not None:
+        sta_c = ctypes.byref(_Sta(1, int(sta[0]), int(sta[1]), int(sta[2])))
+    bp = None
+    if block_prob is not None:
+        bp = _dev(block_prob, lead + (nb,), torch.float32, "block_prob")
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_cuda:
+        raise ValueError("workspace must be a 1-D uint8 device tensor")
+    st = _lib.cabf_build_block_mask(
+        ctypes.byref(geom.c()), _dtype_code(qp), _dev(qp, ps, None, "qp"),
+        _dev(kp, ps, qp.dtype, "kp"), float(scale), float(thr), sta_c,
+        _dev(kv_count, lead, torch.int32, "kv_count"),
+        _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), bp,
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(qp))
+    _check("cabf_build_block_mask", st)
+
+
+def cabf_bsa_forward(geom: Geom, qp, kp, vp, kv_count, kv_index, scale: float, op, lse=None):
+    """Block-sparse attention over the listed tiles: op [B, h, N, d] (+ lse [B, h, N])."""
+    s = geom.sizes()
+    nb = s["n_blocks"]
+    ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
+    lead = (geom.batch, geom.heads, nb)
+    lp = None if lse is None else _dev(lse, ps[:3], torch.float32, "lse")
+    st = _lib.cabf_bsa_forward(
+        ctypes.byref(geom.c()), _dtype_code(qp), _dev(qp, ps, None, "qp"),
+        _dev(kp, ps, qp.dtype, "kp"), _dev(vp, ps, qp.dtype, "vp"),
+        _dev(kv_count, lead, torch.int32, "kv_count"),
+        _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), float(scale),
+        _dev(op, ps, qp.dtype, "op"), lp, _stream(qp))
+    _check("cabf_bsa_forward", st)
+
+
+# --- allocating helpers -----------------------------------------------------------
+
+def default_scale(geom: Geom) -> float:
+    return 1.0 / math.sqrt(geom.head_dim)
+
+
+def permute(q, k, v, geom: Geom):
+    n = geom.sizes()["tokens_padded"]
+    shape = (geom.batch, geom.heads, n, geom.head_dim)
+    qp, kp, vp = (torch.empty(shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    cabf_permute(geom, q, k, v, qp, kp, vp)
+    return qp, kp, vp
+
+
+def unpermute(op, geom: Geom):
+    n = geom.sizes()["tokens_raster"]
+    o = torch.empty((geom.batch, geom.heads, n, geom.head_dim), dtype=op.dtype, device=op.device)
+    cabf_unpermute(geom, op, o)
+    return o
+
+
+def mask_workspace(geom: Geom, device) -> torch.Tensor:
+    return torch.empty(cabf_mask_workspace_bytes(geom), dtype=torch.uint8, device=device)
+
+
+def build_block_mask(qp, kp, geom: Geom, thr: float, sta=None, scale=None, return_probs=False,
+                     workspace=None):
+    nb = geom.sizes()["n_blocks"]
+    lead = (geom.batch, geom.heads, nb)
+    kv_count = torch.empty(lead, dtype=torch.int32, device=qp.device)
+    kv_index = torch.empty(lead + (nb,), dtype=torch.int32, device=qp.device)
+    probs = torch.empty(lead + (nb,), dtype=torch.float32, device=qp.device) if return_probs else None
+    ws = mask_workspace(geom, qp.device) if workspace is None else workspace
+    cabf_build_block_mask(geom, qp, kp, default_scale(geom) if scale is None else scale, thr, sta,
+                          kv_count, kv_index, probs, ws)
+    if return_probs:
+        return kv_count, kv_index, probs
+    return kv_count, kv_index
+
+
+def bsa_forward(qp, kp, vp, kv_count, kv_index, geom: Geom, scale=None, return_lse=False):
+    op = torch.empty_like(qp)
+    lse = torch.empty(qp.shape[:3], dtype=torch.float32, device=qp.device) if return_lse else None
+    cabf_bsa_forward(geom, qp, kp, vp, kv_count, kv_index,
+                     default_scale(geom) if scale is None else scale, op, lse)
+    return (op, lse) if return_lse else op
+
+
+def layer(q, k, v, geom: Geom, thr: float, sta=None, scale=None):
+    """One attention layer: reorder, mask, block-sparse attention, restore order."""
+    qp, kp, vp = permute(q, k, v, geom)
+    kv_count, kv_index = build_block_mask(qp, kp, geom, thr, sta, scale)
+    op = bsa_forward(qp, kp, vp, kv_count, kv_index, geom, scale)
+    return unpermute(op, geom), (kv_count, kv_index)

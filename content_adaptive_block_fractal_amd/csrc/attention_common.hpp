@@ -1,0 +1,64 @@
+// Shared pieces of the block-sparse attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "geometry.hpp"
+
+namespace cabf {
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const void* qp;
+  const void* kp;
+  const void* vp;
+  const int32_t* kv_count;
+  const int32_t* kv_index;
+  void* op;
+  float* lse;
+  float scale_log2;   // softmax scale times log2(e): logits are kept in base 2
+  int nb, Ty, Tx, H, W;
+  int64_t N;          // reordered tokens per (batch, head)
+  int64_t BH;         // batch * heads
+};
+
+// Real rows / columns of block b's 8x8 patch (pads sit at the bottom/right
+// edge of the padded frame).
+struct BlockExtent {
+  int vy, vx;
+  __device__ bool real(int k) const { return (k >> 3) < vy && (k & 7) < vx; }
+  __device__ bool full() const { return vy == kP && vx == kP; }
+};
+
+__device__ inline BlockExtent block_extent(int b, const AttnArgs& a) {
+  const int per_frame = a.Ty * a.Tx;
+  const int rem = b % per_frame;
+  const int ty = rem / a.Tx;
+  const int tx = rem - ty * a.Tx;
+  BlockExtent e;
+  e.vy = min(kP, a.H - ty * kP);
+  e.vx = min(kP, a.W - tx * kP);
+  return e;
+}
+
+__device__ inline float load_elem(const float* p) { return *p; }
+__device__ inline float load_elem(const uint16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even (finite inputs)
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ inline void store_elem(float* p, float v) { *p = v; }
+__device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
+
+void launch_bsa_forward_simple(const AttnArgs& a, bool bf16, int D, hipStream_t stream);
+
+}  // namespace cabf

@@ -1,0 +1,33 @@
+// Internal launcher declarations (one per kernel family). Arguments are
+// already validated by the C ABI layer when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "geometry.hpp"
+
+namespace cabf {
+
+// Fractal reorder of up to three tensors (src[i] -> dst[i], null pairs skipped).
+void launch_permute(const Geo& g, int elem_bytes, const void* const src[3], void* const dst[3],
+                    hipStream_t stream);
+// Inverse reorder of one tensor.
+void launch_unpermute(const Geo& g, int elem_bytes, const void* src, void* dst, hipStream_t stream);
+
+// Mask workspace layout (bytes from the workspace base).
+struct MaskWorkspace {
+  size_t qb_off, kb_off, z_off, total;
+  int ldz;  // row stride of the block-logit matrix, in floats
+};
+MaskWorkspace mask_workspace_layout(const Geo& g);
+
+void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void* kp, float scale,
+                             float thr, bool sta_on, int dt, int dy, int dx, int32_t* kv_count,
+                             int32_t* kv_index, float* block_prob, void* workspace,
+                             hipStream_t stream);
+
+void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
+                        const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
+                        float* lse, hipStream_t stream);
+
+}  // namespace cabf

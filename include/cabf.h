@@ -1,0 +1,156 @@
+/*
+ * cabf.h - C ABI of the content-adaptive block-sparse video attention library
+ * (libcabf.so, HIP for gfx950 / MI355X).
+ *
+ * The library runs one self-attention layer of a video diffusion transformer
+ * the NABLA way (NABLA technical summary, gist.science paper 2507.13546,
+ * "Methodology" items 1-3): reorder the (T, H, W) token grid so that every
+ * P x P spatial patch of a frame is one contiguous 64-token block, build a
+ * per-head block mask from mean-pooled Q and K (block softmax, descending
+ * CDF cut at 1 - thr, optional union with a sliding-tile window), attend over
+ * the kept (query block, key block) tiles only, and restore raster order.
+ *
+ * Conventions shared by every call
+ *  - Pointers are device pointers unless a parameter says "host".
+ *  - Token tensors are contiguous row-major [batch, heads, tokens, head_dim].
+ *    "Raster" tensors have tokens = T*H*W in (t, y, x) order; "reordered"
+ *    tensors have tokens = N = T*Hp*Wp with Hp = ceil(H/P)*P, Wp = ceil(W/P)*P.
+ *  - The caller owns and allocates every buffer, including the workspace.
+ *    The library never allocates, frees or synchronises; it keeps no state.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and is
+ *    asynchronous: faults surface at the caller's next synchronisation.
+ *  - Arguments are validated before anything is launched; on an error the
+ *    call returns a negative cabf_status and has no side effects.
+ *    CABF_EHIP reports a failed launch (hipGetLastError after the launch; an
+ *    error left pending by earlier HIP calls of the same thread is reported
+ *    the same way).
+ *  - Thread-safe: calls share no mutable state.
+ */
+#ifndef CABF_H
+#define CABF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as HIP's own; a compatible repeat of the typedef is legal. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  CABF_OK = 0,
+  CABF_EINVAL = -1,        /* bad argument: null pointer, size, range           */
+  CABF_EUNSUPPORTED = -2,  /* valid but not built: P != 8, head_dim, nb too big */
+  CABF_EWORKSPACE = -3,    /* workspace smaller than cabf_mask_workspace_bytes  */
+  CABF_EHIP = -4           /* the HIP runtime reported an error at launch       */
+} cabf_status;
+
+typedef enum {
+  CABF_BF16 = 0,           /* bfloat16 tensors, fp32 accumulation and softmax   */
+  CABF_F32 = 1             /* float32 tensors                                   */
+} cabf_dtype;
+
+/* Layer geometry. The padded grid and block count are derived:
+ *   Ty = ceil(H/P), Tx = ceil(W/P), Hp = Ty*P, Wp = Tx*P,
+ *   nb = T*Ty*Tx blocks of P*P tokens, N = nb*P*P.
+ * This build supports P = 8 (64-token blocks) and head_dim 64 or 128.
+ * Block b = (t*Ty + ty)*Tx + tx is patch (ty, tx) of frame t. */
+typedef struct {
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t T, H, W;   /* real latent grid: frames, rows, columns */
+  int32_t P;         /* patch side */
+} cabf_geom;
+
+/* Sliding-tile window (NABLA summary, Methodology item 3: the final mask is
+ * the adaptive mask OR a static sliding-tile-attention window). Query block
+ * (t, ty, tx) also keeps every key block within +-dt frames, +-dy patch rows
+ * and +-dx patch columns, clipped at the grid edges. enabled = 0 disables. */
+typedef struct {
+  int32_t enabled;
+  int32_t dt, dy, dx;
+} cabf_sta;
+
+/* Derived sizes of a geometry (host call, no GPU needed). Any output pointer
+ * (host) may be NULL. Returns CABF_OK, CABF_EINVAL or CABF_EUNSUPPORTED. */
+int cabf_geom_sizes(const cabf_geom* g, int64_t* tokens_raster, int64_t* tokens_padded,
+                    int32_t* n_blocks, int32_t* Hp, int32_t* Wp);
+
+/* Fractal flattening (NABLA summary, Methodology item 1): reorders the input
+ * sequence so the tokens of each P x P patch are contiguous while frames keep
+ * their order. Token (t, y, x) moves to
+ *   n' = ((t*Ty + y/P)*Tx + x/P)*P*P + (y%P)*P + x%P;
+ * the N - T*H*W pad slots are written with zeros.
+ * q, k, v: raster [B, heads, T*H*W, head_dim] of `dtype` (input);
+ * qp, kp, vp: reordered [B, heads, N, head_dim] (output, no overlap with the
+ * inputs). A (source, destination) pair may be skipped by passing NULL for
+ * both; one NULL of a pair is CABF_EINVAL. Bitwise copy. */
+int cabf_permute(const cabf_geom* g, cabf_dtype dtype,
+                 const void* q, const void* k, const void* v,
+                 void* qp, void* kp, void* vp, hipStream_t stream);
+
+/* Inverse of cabf_permute for the attention output (Sparse VideoGen2
+ * summary, section 2A: undoing the token permutation restores the original
+ * order). op: reordered [B, heads, N, head_dim] (input); o: raster
+ * [B, heads, T*H*W, head_dim] (output). Pad rows of op are ignored. */
+int cabf_unpermute(const cabf_geom* g, cabf_dtype dtype, const void* op, void* o,
+                   hipStream_t stream);
+
+/* Bytes of device workspace cabf_build_block_mask needs for `g` (0 on an
+ * invalid geometry). Holds the pooled Q and K blocks and the block logits. */
+size_t cabf_mask_workspace_bytes(const cabf_geom* g);
+
+/* Adaptive block mask (NABLA summary, Methodology items 2-3):
+ *  1. Qb_i, Kb_i = mean of the real tokens of block i of qp, kp (fp32);
+ *  2. z_ij = scale * <Qb_i, Kb_j>, p_i. = softmax_j(z_i.) (fp32);
+ *  3. order row i by p descending (ties: lower block index first) and keep
+ *     the shortest prefix whose mass reaches 1 - thr; thr <= 0 keeps every
+ *     block, thr >= 1 keeps one;
+ *  4. if sta is non-NULL and enabled, OR in the sliding-tile window;
+ *  5. write the kept blocks of row i in ascending order.
+ * qp, kp: reordered [B, heads, N, head_dim] (input; pad slots are ignored).
+ * scale > 0 (usually 1/sqrt(head_dim)); 0 <= thr <= 1.
+ * sta: host pointer, may be NULL.
+ * kv_count: [B, heads, nb] int32 (output) number of kept blocks per row, >= 1.
+ * kv_index: [B, heads, nb, nb] int32 (output) row i's kept block indices in
+ *   its first kv_count entries, ascending; later entries are left untouched.
+ * block_prob: NULL, or [B, heads, nb, nb] fp32 (output) the probabilities p.
+ * workspace: device buffer of at least cabf_mask_workspace_bytes(g) bytes,
+ *   256-byte aligned, not shared with a concurrent call.
+ * Supports nb <= 8192. */
+int cabf_build_block_mask(const cabf_geom* g, cabf_dtype dtype,
+                          const void* qp, const void* kp, float scale, float thr,
+                          const cabf_sta* sta, int32_t* kv_count, int32_t* kv_index,
+                          float* block_prob, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Block-sparse attention forward (NABLA summary, Methodology item 2,
+ * expansion bullet: the block mask, expanded to token resolution, decides
+ * which tiles of attention are computed). For every reordered query row n of
+ * block i, over the real keys m of the blocks kv_index[i][0 .. kv_count[i]):
+ *   o_n   = sum_m exp(scale q_n.k_m) v_m / sum_m exp(scale q_n.k_m)
+ *   lse_n = ln sum_m exp(scale q_n.k_m)
+ * computed with an fp32 online softmax. bf16: Q K^T and P V on bf16 matrix
+ * cores with fp32 accumulation, P rounded to bf16, o rounded to bf16.
+ * A row with kv_count = 0 gets o = 0, lse = -inf.
+ * qp, kp, vp: reordered [B, heads, N, head_dim] (input).
+ * kv_count [B, heads, nb], kv_index [B, heads, nb, nb] (input; entries must be
+ *   valid block indices; duplicates would be attended twice).
+ * op: reordered [B, heads, N, head_dim] (output, pad rows included).
+ * lse: NULL, or [B, heads, N] fp32 (output). scale > 0. */
+int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype,
+                     const void* qp, const void* kp, const void* vp,
+                     const int32_t* kv_count, const int32_t* kv_index, float scale,
+                     void* op, float* lse, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* cabf_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CABF_H */

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/cabf.h declares, derives the same geometry as the oracle, and rejects
+bad arguments before launching anything.
+
+The rejection cases pass dummy pointers, so they must never reach a launch;
+each case breaks exactly one rule. They are skipped where a GPU is present
+(there the GPU tests exercise real calls).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import content_adaptive_block_fractal_amd as cabf
+import oracle
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cabf.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cabf_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(cabf.EXPORTED), names
+    lib = ctypes.CDLL(cabf.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_geometry_matches_oracle_grid(name):
+    w = WORKLOADS[name]
+    g = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
+    s = g.sizes()
+    o = oracle.Grid(w.T, w.H, w.W, w.P)
+    assert s == dict(tokens_raster=o.n_valid, tokens_padded=o.N, n_blocks=o.nb, Hp=o.Hp, Wp=o.Wp)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(cabf.cabf_status_string(code), str)
+    assert cabf.cabf_status_string(-3) == "workspace too small"
+
+
+def test_workspace_bytes():
+    g = cabf.Geom(1, 2, 64, 4, 16, 16, 8)
+    n = cabf.cabf_mask_workspace_bytes(g)
+    nb = 16
+    assert n >= 2 * 2 * nb * 64 * 4 + 2 * nb * nb * 4
+    assert cabf.cabf_mask_workspace_bytes(cabf.Geom(1, 2, 64, 4, 16, 16, 4)) == 0
+    assert cabf.cabf_mask_workspace_bytes(cabf.Geom(1, 2, 96, 4, 16, 16, 8)) == 0
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="dummy-pointer checks run host-only")
+L = cabf._lib
+G = cabf._Geom
+DUMMY = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: every case below fails validation
+DUMMY2 = ctypes.c_void_p(0x200000)
+NULL = None
+
+
+def geom(**kw):
+    base = dict(batch=1, heads=2, head_dim=64, T=4, H=16, W=16, P=8)
+    base.update(kw)
+    return ctypes.byref(G(*base.values()))
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=4), cabf.CABF_EUNSUPPORTED), (dict(head_dim=96), cabf.CABF_EUNSUPPORTED),
+    (dict(T=0), cabf.CABF_EINVAL), (dict(heads=-1), cabf.CABF_EINVAL), (dict(W=0), cabf.CABF_EINVAL),
+])
+def test_bad_geometry_rejected(kw, code):
+    assert L.cabf_permute(geom(**kw), 0, DUMMY, DUMMY, DUMMY, DUMMY2, DUMMY2, DUMMY2, NULL) == code
+    assert L.cabf_unpermute(geom(**kw), 0, DUMMY, DUMMY2, NULL) == code
+    assert L.cabf_geom_sizes(geom(**kw), None, None, None, None, None) == code
+
+
+@no_gpu
+def test_permute_argument_checks():
+    g = geom()
+    assert L.cabf_permute(g, 0, DUMMY, NULL, NULL, NULL, NULL, NULL, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_permute(g, 5, DUMMY, NULL, NULL, DUMMY2, NULL, NULL, NULL) == cabf.CABF_EINVAL
+    mis = ctypes.c_void_p(0x100002)
+    assert L.cabf_permute(g, 0, mis, NULL, NULL, DUMMY2, NULL, NULL, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_permute(g, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == cabf.CABF_OK
+    assert L.cabf_unpermute(g, 0, NULL, DUMMY2, NULL) == cabf.CABF_EINVAL
+
+
+@no_gpu
+def test_mask_argument_checks():
+    g = geom()
+    need = L.cabf_mask_workspace_bytes(g)
+    sta_bad = ctypes.byref(cabf._Sta(1, -1, 1, 1))
+    def call(**kw):
+        a = dict(qp=DUMMY, kp=DUMMY, scale=0.125, thr=0.2, sta=None, cnt=DUMMY2, idx=DUMMY2,
+                 prob=None, ws=ctypes.c_void_p(0x300000), wsb=need, dt=0)
+        a.update(kw)
+        return L.cabf_build_block_mask(g, a["dt"], a["qp"], a["kp"], a["scale"], a["thr"], a["sta"],
+                                       a["cnt"], a["idx"], a["prob"], a["ws"], a["wsb"], NULL)
+    assert call(qp=NULL) == cabf.CABF_EINVAL
+    assert call(cnt=NULL) == cabf.CABF_EINVAL
+    assert call(ws=NULL) == cabf.CABF_EINVAL
+    assert call(scale=0.0) == cabf.CABF_EINVAL
+    assert call(scale=float("nan")) == cabf.CABF_EINVAL
+    assert call(thr=-0.1) == cabf.CABF_EINVAL
+    assert call(thr=1.5) == cabf.CABF_EINVAL
+    assert call(thr=float("nan")) == cabf.CABF_EINVAL
+    assert call(sta=sta_bad) == cabf.CABF_EINVAL
+    assert call(wsb=need - 1) == cabf.CABF_EWORKSPACE
+    assert call(ws=ctypes.c_void_p(0x300010)) == cabf.CABF_EINVAL   # not 256-byte aligned
+    assert call(dt=3) == cabf.CABF_EINVAL
+
+
+@no_gpu
+def test_mask_rejects_rows_longer_than_supported():
+    g = geom(T=129, H=64, W=64)      # 129 * 64 blocks > 8192
+    assert L.cabf_build_block_mask(g, 0, DUMMY, DUMMY, 0.1, 0.2, None, DUMMY2, DUMMY2, None,
+                                   ctypes.c_void_p(0x300000), 1 << 40, NULL) == cabf.CABF_EUNSUPPORTED
+
+
+@no_gpu
+def test_attention_argument_checks():
+    g = geom()
+    def call(**kw):
+        a = dict(q=DUMMY, k=DUMMY, v=DUMMY, cnt=DUMMY2, idx=DUMMY2, scale=0.125, op=DUMMY2,
+                 lse=None, dt=0)
+        a.update(kw)
+        return L.cabf_bsa_forward(g, a["dt"], a["q"], a["k"], a["v"], a["cnt"], a["idx"],
+                                  a["scale"], a["op"], a["lse"], NULL)
+    for key in ("q", "k", "v", "cnt", "idx", "op"):
+        assert call(**{key: NULL}) == cabf.CABF_EINVAL, key
+    assert call(scale=-1.0) == cabf.CABF_EINVAL
+    assert call(scale=float("inf")) == cabf.CABF_EINVAL
+    assert call(lse=ctypes.c_void_p(0x400002)) == cabf.CABF_EINVAL
+    assert call(dt=2) == cabf.CABF_EINVAL

@@ -1,0 +1,199 @@
+"""GPU parity at sizes the oracle finishes in seconds: every stage of the HIP
+path against the CPU oracle on the same seeded inputs, through the C ABI.
+
+Grids include ragged ones (H, W not multiples of 8) so that partially padded
+blocks, several tiles and a ragged tail are covered.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import content_adaptive_block_fractal_amd as cabf
+import oracle
+from synth import fourier_video_qkv
+from tests.parity import compare_attention, compare_masks, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (T, H, W, heads, d, dtype, amplitude)
+GRIDS = {
+    "tiny-f32-d64": (4, 16, 16, 2, 64, "f32", 1.0),
+    "ragged-bf16-d128": (3, 21, 35, 3, 128, "bf16", 0.7),
+    "ragged-f32-d128": (2, 13, 27, 2, 128, "f32", 0.7),
+    "ragged-bf16-d64": (5, 9, 17, 2, 64, "bf16", 1.0),
+    "wide-bf16-d128": (3, 24, 88, 2, 128, "bf16", 0.7),
+}
+
+
+def make(name, seed=0):
+    T, H, W, heads, d, dt, amp = GRIDS[name]
+    q, k, v = fourier_video_qkv(T, H, W, heads, d, amp, seed=seed, dtype=dt)
+    g = cabf.Geom(1, heads, d, T, H, W, 8)
+    og = oracle.Grid(T, H, W, 8)
+    return g, og, q.to(DEV), k.to(DEV), v.to(DEV)
+
+
+@pytest.mark.parametrize("name", sorted(GRIDS))
+def test_permute_unpermute_bitexact(name):
+    say(f"permute {name}")
+    g, og, q, k, v = make(name)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    torch.cuda.synchronize()
+    for src, dst in ((q, qp), (k, kp), (v, vp)):
+        want = oracle.permute(src.cpu().view(torch.int16 if src.dtype == torch.bfloat16 else torch.int32).numpy(), og)
+        got = dst.cpu().view(torch.int16 if dst.dtype == torch.bfloat16 else torch.int32).numpy()
+        assert np.array_equal(got, want)
+    back = cabf.unpermute(vp, g)
+    torch.cuda.synchronize()
+    assert torch.equal(back.cpu().view(torch.int16 if v.dtype == torch.bfloat16 else torch.int32),
+                       v.cpu().view(torch.int16 if v.dtype == torch.bfloat16 else torch.int32))
+
+
+def test_permute_skips_null_pairs():
+    g, og, q, k, v = make("ragged-bf16-d64")
+    n = g.sizes()["tokens_padded"]
+    kp = torch.full((1, g.heads, n, g.head_dim), 7.0, dtype=q.dtype, device=DEV)
+    cabf.cabf_permute(g, None, k, None, None, kp, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(kp), oracle.permute(to_np(k), og))
+
+
+MASK_CASES = [
+    ("tiny-f32-d64", 0.2, (1, 1, 1), None),
+    ("tiny-f32-d64", 0.5, None, None),
+    ("ragged-bf16-d128", 0.3, None, None),
+    ("ragged-bf16-d128", 0.75, (1, 1, 1), None),
+    ("ragged-bf16-d128", 0.6, None, 1.0),          # unit scale: sharper block softmax
+    ("ragged-f32-d128", 0.4, (0, 1, 2), None),
+    ("ragged-bf16-d64", 0.9, (1, 0, 0), 1.0),
+    ("wide-bf16-d128", 0.8, None, 1.0),
+]
+
+
+@pytest.mark.parametrize("name,thr,sta,scale", MASK_CASES)
+def test_block_mask_matches_oracle(name, thr, sta, scale):
+    say(f"mask {name} thr={thr} sta={sta} scale={scale}")
+    g, og, q, k, v = make(name)
+    s = cabf.default_scale(g) if scale is None else scale
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    cnt, idx, probs = cabf.build_block_mask(qp, kp, g, thr, sta, s, return_probs=True)
+    torch.cuda.synchronize()
+    info = oracle.build_block_mask(to_np(qp), to_np(kp), og, s, thr, sta)
+    p_gpu = probs.cpu().numpy().astype(np.float64)
+    rel = np.abs(p_gpu - info["p"]) / info["p"]
+    say(f"block prob max rel err {rel.max():.3e}")
+    assert rel.max() < 2e-5
+    compare_masks(cnt, idx, info, thr, label=f"{name} thr={thr} sta={sta}")
+    # the same decision taken by the oracle in fp32 as well
+    info32 = oracle.build_block_mask(to_np(qp), to_np(kp), og, s, thr, sta, precision=np.float32)
+    info32.update({kk: info[kk] for kk in ("s_prev", "s_k", "p_k", "p_next", "k")})
+    compare_masks(cnt, idx, info32, thr, label=f"{name} (fp32 oracle)")
+
+
+@pytest.mark.parametrize("thr", [0.0, 1.0])
+def test_block_mask_threshold_extremes(thr):
+    g, og, q, k, v = make("ragged-bf16-d128")
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, thr)
+    torch.cuda.synchronize()
+    info = oracle.build_block_mask(to_np(qp), to_np(kp), og, cabf.default_scale(g), thr)
+    c = cnt.cpu().numpy()
+    if thr == 0.0:
+        assert np.all(c == og.nb)
+    else:
+        assert np.all(c == 1)
+    compare_masks(cnt, idx, info, thr, label=f"thr={thr}")
+
+
+@pytest.mark.parametrize("n_blocks_t,thr", [(4, 0.2), (6, 0.37)])
+def test_block_mask_uniform_rows_keep_lowest_indices(n_blocks_t, thr):
+    """Constant K: every block probability is equal, so the cut keeps the
+    ceil((1-thr) nb) lowest block indices (NABLA CDF cut with index tie-break)."""
+    T, H, W, d = n_blocks_t, 16, 16, 64
+    g = cabf.Geom(1, 1, d, T, H, W, 8)
+    torch.manual_seed(3)
+    q = torch.randn(1, 1, T * H * W, d, device=DEV).to(torch.bfloat16)
+    k = torch.full((1, 1, T * H * W, d), 0.25, device=DEV).to(torch.bfloat16)
+    qp, kp, _ = cabf.permute(q, k, k, g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, thr)
+    torch.cuda.synchronize()
+    nb = g.sizes()["n_blocks"]
+    want = math.ceil((1 - thr) * nb)
+    assert np.all(cnt.cpu().numpy() == want)
+    assert np.all(idx.cpu().numpy()[..., :want] == np.arange(want))
+
+
+ATTN_CASES = [
+    ("tiny-f32-d64", 0.2, (1, 1, 1)),
+    ("ragged-f32-d128", 0.4, None),
+    ("ragged-bf16-d128", 0.3, (1, 1, 1)),
+    ("ragged-bf16-d64", 0.5, None),
+    ("wide-bf16-d128", 0.8, None),
+    ("ragged-bf16-d128", 0.0, None),
+]
+
+
+@pytest.mark.parametrize("name,thr,sta", ATTN_CASES)
+def test_attention_on_oracle_lists(name, thr, sta):
+    """bsa_forward fed the oracle's own block lists equals the oracle's attention."""
+    say(f"attention {name} thr={thr} sta={sta}")
+    g, og, q, k, v = make(name)
+    s = cabf.default_scale(g)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    torch.cuda.synchronize()
+    qn, kn, vn = to_np(qp), to_np(kp), to_np(vp)
+    info = oracle.build_block_mask(qn, kn, og, s, thr, sta)
+    cnt = torch.from_numpy(info["kv_count"]).to(DEV)
+    idx = torch.from_numpy(info["kv_index"]).to(DEV)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle.bsa_forward(qn, kn, vn, info["kv_count"], info["kv_index"], og, s)
+    compare_attention(op, ref_o, q.dtype == torch.bfloat16, lse, ref_lse, label=name)
+
+
+def test_attention_rows_with_no_blocks_and_arbitrary_lists():
+    g, og, q, k, v = make("ragged-bf16-d128")
+    nb = og.nb
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    rng = np.random.default_rng(5)
+    mask = rng.random((1, g.heads, nb, nb)) < 0.3
+    mask[0, 0, 3] = False            # a row that keeps nothing
+    mask[0, 1, :5] = False
+    cnt_np, idx_np = oracle.mask_to_lists(mask)
+    op, lse = cabf.bsa_forward(qp, kp, vp, torch.from_numpy(cnt_np).to(DEV),
+                               torch.from_numpy(idx_np).to(DEV), g, return_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle.bsa_forward(to_np(qp), to_np(kp), to_np(vp), cnt_np, idx_np, og,
+                                        cabf.default_scale(g))
+    compare_attention(op, ref_o, True, lse, ref_lse, label="arbitrary lists")
+    assert torch.all(op[0, 0, 3 * 64:4 * 64] == 0)
+    assert torch.all(torch.isneginf(lse[0, 0, 3 * 64:4 * 64]))
+
+
+@pytest.mark.parametrize("name,thr,sta", [("tiny-f32-d64", 0.2, (1, 1, 1)),
+                                          ("ragged-bf16-d128", 0.5, (1, 1, 1))])
+def test_layer_end_to_end(name, thr, sta):
+    """permute -> build_block_mask -> bsa_forward -> unpermute on the GPU against
+    the oracle's layer; query blocks whose lists differ (exempt rows) are excluded."""
+    say(f"layer {name}")
+    g, og, q, k, v = make(name)
+    s = cabf.default_scale(g)
+    o, (cnt, idx) = cabf.layer(q, k, v, g, thr, sta, s)
+    torch.cuda.synchronize()
+    ref_o, info = oracle.layer(to_np(q), to_np(k), to_np(v), og, s, thr, sta)
+    gmask = oracle.lists_to_mask(cnt.cpu().numpy(), idx.cpu().numpy(), og.nb)
+    same_blocks = ~(gmask != info["mask"]).any(-1)                   # [B, h, nb]
+    # raster rows whose block kept the same list
+    blk_of_row = oracle.fractal_positions(og) // og.block
+    rows = same_blocks[..., blk_of_row]
+    say(f"layer rows compared: {int(rows.sum())} of {rows.size}")
+    o_np, r_np = to_np(o)[rows], ref_o[rows]
+    err = np.abs(o_np - r_np)
+    if q.dtype == torch.bfloat16:
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    else:
+        assert err.max() <= 1e-4
