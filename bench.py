@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of one content-adaptive block-sparse attention layer on one MI355X.
+
+A step is the whole path on one batch of synthetic input already resident in
+HBM: fractal permute of Q, K, V -> block mask (pool, block softmax, CDF cut)
+-> block-sparse attention over the kept tiles -> unpermute of the output.
+The default workload is the Wan-2.1-14B-like 720p layer (40 heads, head_dim
+128, 21 x 45x80 latent grid padded to 48x80, bf16) with the threshold
+calibrated to 80% block sparsity.
+
+Prints one JSON line. ``value`` is the effective TFLOP/s of the whole step,
+counting 4*64*64*head_dim flops per kept (query block, key block) tile.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn effective TFLOP/s + ms/layer, Wan-14B 720p shape, 80% sparse"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan14b-720p")
+    ap.add_argument("--sparsity", type=float, default=0.80)
+    ap.add_argument("--sta", action="store_true", help="union the +-1 sliding-tile window")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--variants", type=int, default=1,
+                    help="also time the 90%% and window variants (0 to skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the oracle CPU-baseline sample (0 to skip)")
+    return ap.parse_args()
+
+
+def calibrate_thr(cabf, qp, kp, geom, target, sta, ws, kv_count, kv_index, iters=30):
+    """Bisection on thr so that the final mask's block sparsity meets the target."""
+    import torch
+    nb = geom.sizes()["n_blocks"]
+    total = geom.batch * geom.heads * nb * nb
+    scale = cabf.default_scale(geom)
+
+    def sparsity(thr):
+        cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, kv_count, kv_index, None, ws)
+        return 1.0 - kv_count.sum(dtype=torch.int64).item() / total
+
+    lo, hi = 0.0, 1.0
+    best = (1.0, abs(sparsity(1.0) - target))
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        sp = sparsity(mid)
+        if abs(sp - target) < best[1]:
+            best = (mid, abs(sp - target))
+        if sp < target:
+            lo = mid
+        else:
+            hi = mid
+    return best[0]
+
+
+def run_steps(cabf, geom, bufs, thr, sta, n, timed):
+    """n steps of the whole path; returns per-stage event times (ms) if timed."""
+    import torch
+    q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
+    scale = cabf.default_scale(geom)
+    stage = {"permute": [], "mask": [], "attention": [], "unpermute": []}
+    for _ in range(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
+        if timed:
+            ev[0].record()
+        cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
+        if timed:
+            ev[1].record()
+        cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
+        if timed:
+            ev[2].record()
+        cabf.cabf_bsa_forward(geom, qp, kp, vp, cnt, idx, scale, op, None)
+        if timed:
+            ev[3].record()
+        cabf.cabf_unpermute(geom, op, o)
+        if timed:
+            ev[4].record()
+            stage["_ev"] = stage.get("_ev", []) + [ev]
+    if timed:
+        torch.cuda.synchronize()
+        for ev in stage.pop("_ev"):
+            for i, name in enumerate(("permute", "mask", "attention", "unpermute")):
+                stage[name].append(ev[i].elapsed_time(ev[i + 1]))
+    return stage
+
+
+def cpu_baseline(q, k, v, w, thr, sta, budget_s):
+    """The CPU oracle on a bounded sample of the same layer: head 0's permute and
+    block mask (all rows) plus attention for the first query blocks that fit the
+    time budget. Single thread (BLAS pinned to one thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    g = oracle.Grid(w.T, w.H, w.W, w.P)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    f = lambda t: t[0, 0].float().cpu().numpy().astype(np.float64)
+    qh, kh, vh = f(q), f(k), f(v)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        qp, kp, vp = oracle.permute(qh, g), oracle.permute(kh, g), oracle.permute(vh, g)
+        info = oracle.build_block_mask(qp, kp, g, scale, thr, sta)
+        t_mask = time.perf_counter() - t0
+        cnt_all = info["kv_count"]
+        done, t_attn, tiles = 0, 0.0, 0
+        while done < g.nb and t_attn + t_mask * done / g.nb < budget_s:
+            cnt = np.zeros_like(cnt_all)
+            cnt[done] = cnt_all[done]
+            t1 = time.perf_counter()
+            oracle.bsa_forward(qp, kp, vp, cnt, info["kv_index"], g, scale)
+            t_attn += time.perf_counter() - t1
+            tiles += int(cnt_all[done])
+            done += 1
+    flops = 4.0 * 64 * 64 * w.head_dim * tiles
+    t_equiv = t_attn + t_mask * done / g.nb     # mask cost of the sampled rows
+    per_layer_s = (t_mask + t_attn / done * g.nb) * w.heads * w.batch
+    return {
+        "value": flops / t_equiv / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.heads}: permute + block mask of all {g.nb} rows ({t_mask:.2f} s, "
+                   f"charged pro rata) + attention of the first {done} query blocks "
+                   f"({tiles} kept tiles, {t_attn:.2f} s); fp64 numpy, 1 thread"),
+        "extrapolated_s_per_layer": per_layer_s,
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the block-sparse attention path has no "
+              f"multi-GPU mode (asked for --gpus {args.gpus}, WORLD_SIZE {world}). "
+              f"Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import content_adaptive_block_fractal_amd as cabf
+    from synth import WORKLOADS, fourier_video_qkv
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    geom = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
+    sizes = geom.sizes()
+    nb = sizes["n_blocks"]
+    q, k, v = fourier_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, w.amplitude, seed=args.seed,
+                                dtype=w.dtype, batch=w.batch, device=dev)
+    pshape = (w.batch, w.heads, sizes["tokens_padded"], w.head_dim)
+    qp, kp, vp, op = (torch.empty(pshape, dtype=q.dtype, device=dev) for _ in range(4))
+    o = torch.empty_like(q)
+    cnt = torch.empty((w.batch, w.heads, nb), dtype=torch.int32, device=dev)
+    idx = torch.empty((w.batch, w.heads, nb, nb), dtype=torch.int32, device=dev)
+    ws = cabf.mask_workspace(geom, dev)
+    bufs = (q, k, v, qp, kp, vp, op, o, cnt, idx, ws)
+
+    def measure(sparsity, sta, steps, warmup):
+        cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
+        thr = calibrate_thr(cabf, qp, kp, geom, sparsity, sta, ws, cnt, idx)
+        run_steps(cabf, geom, bufs, thr, sta, warmup, timed=False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(cabf, geom, bufs, thr, sta, steps, timed=False)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        stages = run_steps(cabf, geom, bufs, thr, sta, steps, timed=True)
+        kept = int(cnt.sum(dtype=torch.int64).item())
+        flops = 4.0 * 64 * 64 * w.head_dim * kept
+        med = {kk: statistics.median(vv) for kk, vv in stages.items()}
+        mean = {kk: statistics.fmean(vv) for kk, vv in stages.items()}
+        return dict(thr=thr, sta=sta, kept_tiles=kept,
+                    sparsity=1.0 - kept / (w.batch * w.heads * nb * nb), flops=flops,
+                    wall_ms=wall_ms, stage_ms_median=med, stage_ms_mean=mean,
+                    stage_ms_min={kk: min(vv) for kk, vv in stages.items()})
+
+    sta = (1, 1, 1) if args.sta else None
+    main_run = measure(args.sparsity, sta, args.steps, args.warmup)
+    ms = main_run["wall_ms"]
+    attn_ms = main_run["stage_ms_mean"]["attention"]
+    mask_ms = main_run["stage_ms_mean"]["mask"]
+    attn_tflops = main_run["flops"] / (attn_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": main_run["flops"] / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded smooth Fourier field + noise Q/K/V, no model weights)",
+        "config": {
+            "workload": f"{w.name}: 1x{w.heads} heads, head_dim {w.head_dim}, "
+                        f"T={w.T} x {w.H}x{w.W} (padded {sizes['Hp']}x{sizes['Wp']}), "
+                        f"N={sizes['tokens_padded']}, {nb} blocks of 64",
+            "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+            "grid": [w.T, w.H, w.W], "patch": w.P,
+            "target_sparsity": args.sparsity, "sparsity": main_run["sparsity"],
+            "thr": main_run["thr"], "sta_window": list(sta) if sta else None,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bsa_fwd_mfma (cabf_bsa_forward)",
+            "achieved": attn_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "algorithmic_unit": "4*64*64*head_dim flops per kept 64x64 tile",
+            "avg_launch_ms": attn_ms,
+        },
+        "stages_ms": main_run["stage_ms_mean"],
+        "stages_ms_median": main_run["stage_ms_median"],
+        "ms_per_layer": mask_ms + attn_ms,
+        "mask_share": mask_ms / (mask_ms + attn_ms),
+        "kept_tiles": main_run["kept_tiles"],
+    }
+    if args.variants:
+        var = {}
+        for sp, st in ((0.90, None), (0.80, (1, 1, 1)), (0.90, (1, 1, 1))):
+            if sp == args.sparsity and st == sta:
+                continue
+            r = measure(sp, st, max(3, args.steps // 4), 2)
+            a = r["stage_ms_mean"]["attention"]
+            var[f"{int(sp * 100)}%{'+window' if st else ''}"] = dict(
+                thr=r["thr"], sparsity=r["sparsity"], ms_per_step=r["wall_ms"],
+                attention_ms=a, mask_ms=r["stage_ms_mean"]["mask"],
+                attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
+                step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
+        line["variants"] = var
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_run["thr"], sta, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,7 +26,10 @@ void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp,
   a.W = g.W;
   a.N = g.N;
   a.BH = g.BH;
-  launch_bsa_forward_simple(a, bf16, g.D, stream);
+  if (bf16)
+    launch_bsa_forward_mfma(a, g.D, stream);      // bf16 matrix cores
+  else
+    launch_bsa_forward_simple(a, false, g.D, stream);
 }
 
 }  // namespace cabf

@@ -60,5 +60,6 @@ __device__ inline void store_elem(float* p, float v) { *p = v; }
 __device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
 void launch_bsa_forward_simple(const AttnArgs& a, bool bf16, int D, hipStream_t stream);
+void launch_bsa_forward_mfma(const AttnArgs& a, int D, hipStream_t stream);
 
 }  // namespace cabf
