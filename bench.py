@@ -44,6 +44,9 @@ def parse():
                     help="also time the 90%% and window variants (0 to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle CPU-baseline sample (0 to skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps "
+                         "(reference dispatch for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -196,6 +199,13 @@ def main():
                     wall_ms=wall_ms, stage_ms_median=med, stage_ms_mean=mean,
                     stage_ms_min={kk: min(vv) for kk, vv in stages.items()})
 
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     sta = (1, 1, 1) if args.sta else None
     main_run = measure(args.sparsity, sta, args.steps, args.warmup)
     ms = main_run["wall_ms"]

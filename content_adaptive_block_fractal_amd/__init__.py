@@ -19,7 +19,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcabf.so")
+# CABF_LIB may point at another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("CABF_LIB") or os.path.join(_HERE, "libcabf.so")
 
 CABF_OK, CABF_EINVAL, CABF_EUNSUPPORTED, CABF_EWORKSPACE, CABF_EHIP = 0, -1, -2, -3, -4
 CABF_BF16, CABF_F32 = 0, 1

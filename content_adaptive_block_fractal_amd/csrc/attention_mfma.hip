@@ -21,7 +21,11 @@
 //   online softmax in base 2 on the fp32 accumulators; the running max is
 //   only raised (and the output rescaled) when a row's max grows by more than
 //   2^8, so the numerators stay below 2^8 and most tiles skip the rescale
-//   O^T += V^T P^T A = V^T (LDS, stored transposed, 8-byte chunks swizzled)
+//   O^T += V^T P^T A = V^T, read from the row-major V tile in LDS with the
+//                  transposing LDS read (ds_read_b64_tr_b16: within a
+//                  16-lane group, lane i receives element i%4 of the
+//                  8-byte rows read by lanes 4e + i/4, e = 0..3), so each
+//                  lane gets 4 consecutive keys of one head-dim column
 //                  B = P^T (the softmax numerators, rounded to bf16)
 // The contraction index of each product only has to be spread over the
 // lanes the same way in both operands; V^T is read with the key order the
@@ -53,6 +57,9 @@ constexpr float kRescaleSlack = 8.0f;   // base-2 headroom before the running ma
 // Workgroup id -> query block: XCD x (which receives ids x, x+8, ...) gets
 // the contiguous range [start_x, start_x + count_x).
 __device__ inline int64_t xcd_order(int64_t wg, int64_t total) {
+#if defined(CABF_WG_ORDER) && CABF_WG_ORDER == 1
+  return wg;   // plain dispatch order: all XCDs sweep the same head together
+#endif
   const int64_t xcd = wg % kXcds, local = wg / kXcds;
   const int64_t per = total / kXcds, rem = total % kXcds;
   return xcd * per + (xcd < rem ? xcd : rem) + local;
@@ -68,25 +75,31 @@ __device__ inline int k_chunk_slot(int key, int chunk) {
   return key * kChunks + (chunk ^ swz);
 }
 
-// V^T tile: D rows (one per head-dim index) x 64 keys = 16 chunks of 8 bytes.
-__device__ inline int vt_swizzle(int d) { return (d >> 1) & 15; }
-
-__device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) {  // (a.lo, b.lo)
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+// V tile: 64 rows x D bf16, row-major like K. The transposing read fetches
+// 4 consecutive rows x 32 bytes per 16-lane group; XOR-ing the 16-byte chunk
+// index with an even rotation keeps each 32-byte pair intact and puts the 4
+// (D = 128: 8) rows of one read on distinct banks.
+template <int D>
+__device__ inline int v_chunk_slot(int key, int chunk) {
+  constexpr int kChunks = D / 8;
+  const int swz = (D == 128) ? 2 * (key & 7) : 2 * ((key >> 1) & 3);
+  return key * kChunks + (chunk ^ swz);
 }
-__device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) {  // (a.hi, b.hi)
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 4 consecutive keys of one head-dim column of the V tile (see above).
+__device__ inline s16x4 read_v_transposed(const uint16_t* sv_row_chunk) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_row_chunk));
 }
 
 template <int D>
 struct TileRegs {
-  static constexpr int kChunks = D / 8;                        // 16-byte chunks per K row
-  static constexpr int kKIters = kBlock * kChunks / kThreads;  // K chunks per thread
-  static constexpr int kDP = D / 2;                            // d pairs per V row
-  static constexpr int kOG = kThreads / kDP;                   // key-octet groups
-  static constexpr int kOct = 8 / kOG;                         // key octets per thread
-  u32x4 k[kKIters];
-  uint32_t v[kOct * 8];
+  static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
+  static constexpr int kIters = kBlock * kChunks / kThreads;   // chunks per thread per tensor
+  u32x4 k[kIters];
+  u32x4 v[kIters];
 };
 
 template <int D>
@@ -94,45 +107,21 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& t, const uint16_t* __rest
                                           const uint16_t* __restrict__ vb, int tid) {
   using R = TileRegs<D>;
 #pragma unroll
-  for (int i = 0; i < R::kKIters; ++i)
+  for (int i = 0; i < R::kIters; ++i) {
     t.k[i] = *reinterpret_cast<const u32x4*>(kb + (tid + kThreads * i) * 8);
-  const int dp = tid % R::kDP, og = tid / R::kDP;
-#pragma unroll
-  for (int i = 0; i < R::kOct; ++i) {
-    const int oct = og + R::kOG * i;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      t.v[i * 8 + e] = *reinterpret_cast<const uint32_t*>(vb + (oct * 8 + e) * D + 2 * dp);
+    t.v[i] = *reinterpret_cast<const u32x4*>(vb + (tid + kThreads * i) * 8);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& t, u32x4* sk, uint4* svt, int tid) {
+__device__ __forceinline__ void store_tile(const TileRegs<D>& t, u32x4* sk, u32x4* sv, int tid) {
   using R = TileRegs<D>;
 #pragma unroll
-  for (int i = 0; i < R::kKIters; ++i) {
+  for (int i = 0; i < R::kIters; ++i) {
     const int cidx = tid + kThreads * i;
-    sk[k_chunk_slot<D>(cidx / R::kChunks, cidx % R::kChunks)] = t.k[i];
-  }
-  const int dp = tid % R::kDP, og = tid / R::kDP;
-#pragma unroll
-  for (int i = 0; i < R::kOct; ++i) {
-    const int oct = og + R::kOG * i;
-    const int b = i * 8;
-    uint4 lo = make_uint4(pack_lo(t.v[b + 0], t.v[b + 1]), pack_lo(t.v[b + 2], t.v[b + 3]),
-                          pack_lo(t.v[b + 4], t.v[b + 5]), pack_lo(t.v[b + 6], t.v[b + 7]));
-    uint4 hi = make_uint4(pack_hi(t.v[b + 0], t.v[b + 1]), pack_hi(t.v[b + 2], t.v[b + 3]),
-                          pack_hi(t.v[b + 4], t.v[b + 5]), pack_hi(t.v[b + 6], t.v[b + 7]));
-    // rows 2dp (low halves) and 2dp+1 (high halves) have swizzles s and s
-    // (same d >> 1); an odd swizzle swaps the two 8-byte halves of the unit
-    const int sw = vt_swizzle(2 * dp);
-    if (sw & 1) {
-      lo = make_uint4(lo.z, lo.w, lo.x, lo.y);
-      hi = make_uint4(hi.z, hi.w, hi.x, hi.y);
-    }
-    const int unit = oct ^ (sw >> 1);
-    svt[(2 * dp) * 8 + unit] = lo;
-    svt[(2 * dp + 1) * 8 + unit] = hi;
+    const int row = cidx / R::kChunks, chunk = cidx % R::kChunks;
+    sk[k_chunk_slot<D>(row, chunk)] = t.k[i];
+    sv[v_chunk_slot<D>(row, chunk)] = t.v[i];
   }
 }
 
@@ -140,12 +129,12 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t n_qblocks) {
   constexpr int kKS = D / 16;   // MFMA k-steps over d
   constexpr int kDT = D / 32;   // 32-row d subtiles of O^T
-  constexpr int kTileBytes = kBlock * D * 2 * 2;                       // K + V^T
+  constexpr int kTileBytes = kBlock * D * 2 * 2;                       // K + V
   constexpr int kMergeBytes = 2 * 64 * (kDT * 16 + 2) * 4;             // 2 waves' partials
   constexpr int kSmemBytes = kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes;
   __shared__ uint4 smem[kSmemBytes / 16];
   u32x4* sk = reinterpret_cast<u32x4*>(smem);
-  uint4* svt = smem + kBlock * D / 8;
+  u32x4* sv = sk + kBlock * D / 8;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   const int cnt = min(max(a.kv_count[qblk], 0), a.nb);
   const int32_t* __restrict__ list = a.kv_index + qblk * a.nb;
   const unsigned nbu = static_cast<unsigned>(a.nb);
-  const char* svt_bytes = reinterpret_cast<const char*>(svt);
+  const uint16_t* sv_elems = reinterpret_cast<const uint16_t*>(sv);
   const int key0 = 32 * wk;     // first key of this wave's half
 
   TileRegs<D> regs;
@@ -196,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
     int en = e + 1;
     while (en < cnt && static_cast<unsigned>(list[en]) >= nbu) ++en;
     __syncthreads();            // every wave is done with the previous tile
-    store_tile<D>(regs, sk, svt, tid);
+    store_tile<D>(regs, sk, sv, tid);
     __syncthreads();
     if (en < cnt) {
       const int64_t off = static_cast<int64_t>(list[en]) * kBlock * D;
@@ -238,26 +227,44 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
     }
     const float msub = (m == -INFINITY) ? 0.0f : m;
     bf16x8 pb[2];
+    float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = exp2f(fmaf(s[r], c, -msub));
-      l += p;
-      pb[r >> 3][r & 7] = static_cast<__bf16>(p);
+      // v_exp_f32 directly: arguments are <= 2^3 above the running max and
+      // results below the fp32 normal range are flushed, which bf16 P and the
+      // fp32 sums tolerate
+      p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
+      pb[r >> 3][r & 7] = static_cast<__bf16>(p[r]);
     }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) p[r] += p[r + w];
+    l += p[0];
     // ---- O^T += V^T P^T over this wave's 32 keys ------------------------
+    // lane (d = 32 dt + li, h): A elements 0..3 = keys k0 .. k0+3 and 4..7 =
+    // keys k0+8 .. k0+11 with k0 = key0 + 16 st + 4 h, the order in which the
+    // S^T accumulator holds P. Source lane s of a 16-lane group reads row
+    // k0 + s/4 at columns base + 4 (s % 4), base = 32 dt + 16 ((lane / 16) % 2).
+    {
+      const int grp = lane >> 4, sl = lane & 15;
+      const int col = 16 * (grp & 1) + 4 * (sl & 3);     // + 32 dt
+      const int rsub = 4 * (grp >> 1) + (sl >> 2);        // + key0 + 16 st (+ 8)
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
-      const int d = 32 * dt + li;
-      const int sw = vt_swizzle(d);
-      const char* row = svt_bytes + d * 128;
+      for (int dt = 0; dt < kDT; ++dt) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int q8 = 8 * wk + 4 * st + h;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + ((q8 ^ sw) * 8));
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + (((q8 + 2) ^ sw) * 8));
-        const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[st],
-                                                        o[dt], 0, 0, 0);
+        for (int st = 0; st < 2; ++st) {
+          const int r0 = key0 + 16 * st + rsub;
+          const int cc = 32 * dt + col;
+          const uint16_t* a0 = sv_elems + v_chunk_slot<D>(r0, cc >> 3) * 8 + (cc & 7);
+          const uint16_t* a1 = sv_elems + v_chunk_slot<D>(r0 + 8, cc >> 3) * 8 + (cc & 7);
+          const s16x4 lo = read_v_transposed(a0);
+          const s16x4 hi = read_v_transposed(a1);
+          const s16x4 both[2] = {lo, hi};
+          bf16x8 av;
+          __builtin_memcpy(&av, both, sizeof(av));
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[st], o[dt], 0, 0, 0);
+        }
       }
     }
     e = en;
