@@ -6,7 +6,7 @@
 #include <cstdint>
 #include <limits>
 
-#include "../../include/cabf.h"
+#include "cabf.h"
 #include "geometry.hpp"
 #include "launch.hpp"
 

@@ -9,9 +9,7 @@
 //   halves of a query row are merged once at the end through LDS (the merge
 //   of two partial softmax sums is exact). The workgroup walks its kept key
 //   blocks in list order. Workgroup ids are remapped so that each XCD (its
-//   own L2) processes a contiguous run of query blocks of the same head:
-//   neighbouring blocks keep overlapping key blocks, so K/V tiles are shared
-//   in that XCD's L2.
+//   own L2) processes a contiguous run of query blocks of the same head.
 //
 // Per kept tile, per wave, with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T    A = K (LDS, row-major, 16-byte chunks XOR-swizzled by row)
@@ -31,12 +29,16 @@
 // lanes the same way in both operands; V^T is read with the key order the
 // S^T accumulator layout gives P.
 //
-// Pipelining: while a tile is multiplied out of LDS, the next tile's K and V
-// are already in flight from global memory into registers.
+// Pipeline: K and V tiles stream straight from global memory into a
+// two-slot LDS ring (global_load_lds_dwordx4), one LDS object per slot so
+// that reads of the current tile never wait for the tiles in flight. K runs
+// one tile ahead of V: S^T of tile e+1 is issued on the matrix cores before
+// the softmax of tile e runs on the vector ALUs. One barrier per tile.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attention_common.hpp"
 #include "geometry.hpp"
@@ -75,14 +77,16 @@ __device__ inline int k_chunk_slot(int key, int chunk) {
   return key * kChunks + (chunk ^ swz);
 }
 
-// V tile: 64 rows x D bf16, row-major like K. The transposing read fetches
-// 4 consecutive rows x 32 bytes per 16-lane group; XOR-ing the 16-byte chunk
-// index with an even rotation keeps each 32-byte pair intact and puts the 4
-// (D = 128: 8) rows of one read on distinct banks.
+// V tile: 64 rows x D bf16, row-major like K. A transposing read fetches,
+// per 16-lane group, 4 consecutive rows x 32 bytes; the two groups of a
+// 32-lane half read the same rows at neighbouring 32-byte columns. XOR-ing
+// the 16-byte chunk index with 4 * (row % 4) (D = 64: 4 * ((row / 2) % 2))
+// keeps every 32-byte pair intact and gives the 8 (row, pair) reads of a
+// half distinct banks.
 template <int D>
 __device__ inline int v_chunk_slot(int key, int chunk) {
   constexpr int kChunks = D / 8;
-  const int swz = (D == 128) ? 2 * (key & 7) : 2 * ((key >> 1) & 3);
+  const int swz = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
   return key * kChunks + (chunk ^ swz);
 }
 
@@ -95,46 +99,71 @@ __device__ inline s16x4 read_v_transposed(const uint16_t* sv_row_chunk) {
 }
 
 template <int D>
-struct TileRegs {
+struct Stage {
   static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
   static constexpr int kIters = kBlock * kChunks / kThreads;   // chunks per thread per tensor
-  u32x4 k[kIters];
-  u32x4 v[kIters];
+  static constexpr int kTile = kBlock * kChunks;               // 16-byte chunks per K (or V) tile
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& t, const uint16_t* __restrict__ kb,
-                                          const uint16_t* __restrict__ vb, int tid) {
-  using R = TileRegs<D>;
+// Direct-to-LDS copy of one K or V tile into a ring slot: each wave
+// instruction fills 64 consecutive 16-byte LDS chunks (lane l -> chunk base +
+// l); the lane fetches the global chunk that the swizzle places there. The
+// byte offsets of those chunks inside a tile are the same for every tile.
+template <int D, bool IS_V>
+__device__ inline void tile_load_offsets(uint32_t (&off)[Stage<D>::kIters], int wave, int lane) {
+  using S = Stage<D>;
 #pragma unroll
-  for (int i = 0; i < R::kIters; ++i) {
-    t.k[i] = *reinterpret_cast<const u32x4*>(kb + (tid + kThreads * i) * 8);
-    t.v[i] = *reinterpret_cast<const u32x4*>(vb + (tid + kThreads * i) * 8);
+  for (int i = 0; i < S::kIters; ++i) {
+    const int phys = (i * kWaves + wave) * 64 + lane;
+    const int row = phys / S::kChunks;
+    const int pc = phys % S::kChunks;
+    // the swizzle is an XOR with a function of the row: its own inverse
+    const int chunk = IS_V ? (v_chunk_slot<D>(row, pc) - row * S::kChunks)
+                           : (k_chunk_slot<D>(row, pc) - row * S::kChunks);
+    off[i] = static_cast<uint32_t>((row * D + chunk * 8) * 2);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& t, u32x4* sk, u32x4* sv, int tid) {
-  using R = TileRegs<D>;
+__device__ __forceinline__ void issue_tile_load(const uint16_t* __restrict__ tile_src, u32x4* slot,
+                                                const uint32_t (&off)[Stage<D>::kIters], int wave) {
+  using S = Stage<D>;
+  const char* base = reinterpret_cast<const char*>(tile_src);
 #pragma unroll
-  for (int i = 0; i < R::kIters; ++i) {
-    const int cidx = tid + kThreads * i;
-    const int row = cidx / R::kChunks, chunk = cidx % R::kChunks;
-    sk[k_chunk_slot<D>(row, chunk)] = t.k[i];
-    sv[v_chunk_slot<D>(row, chunk)] = t.v[i];
+  for (int i = 0; i < S::kIters; ++i)
+    __builtin_amdgcn_global_load_lds(base + off[i], slot + (i * kWaves + wave) * 64, 16, 0, 0);
+}
+
+// List entry t -> element offset of its K/V block and whether it is a real
+// block; entries outside [0, nb) load block 0 and are masked out entirely.
+struct TileRef {
+  int64_t off;
+  int jb;
+  bool real;
+};
+
+// Bit r of the mask: key 8 * (4 wk + r / 4) + 4 h + r % 4 of the lane's
+// accumulator is a real token of the block.
+__device__ inline uint32_t real_key_bits(const BlockExtent& ext, int wk, int h) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int iy = 4 * wk + (r >> 2), ix = 4 * h + (r & 3);
+    bits |= (iy < ext.vy && ix < ext.vx) ? (1u << r) : 0u;
   }
+  return bits;
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t n_qblocks) {
+  using S = Stage<D>;
   constexpr int kKS = D / 16;   // MFMA k-steps over d
   constexpr int kDT = D / 32;   // 32-row d subtiles of O^T
-  constexpr int kTileBytes = kBlock * D * 2 * 2;                       // K + V
-  constexpr int kMergeBytes = 2 * 64 * (kDT * 16 + 2) * 4;             // 2 waves' partials
-  constexpr int kSmemBytes = kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes;
-  __shared__ uint4 smem[kSmemBytes / 16];
-  u32x4* sk = reinterpret_cast<u32x4*>(smem);
-  u32x4* sv = sk + kBlock * D / 8;
+  // Ring slots are separate LDS objects so that the compiler can tell the
+  // tile being read from the tiles still streaming in (no wait on them).
+  __shared__ u32x4 k_slot0[S::kTile], k_slot1[S::kTile];
+  __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile];
+  __shared__ float merge_ml[2 * 2 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,124 +198,147 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
 
   const int cnt = min(max(a.kv_count[qblk], 0), a.nb);
   const int32_t* __restrict__ list = a.kv_index + qblk * a.nb;
-  const unsigned nbu = static_cast<unsigned>(a.nb);
-  const uint16_t* sv_elems = reinterpret_cast<const uint16_t*>(sv);
   const int key0 = 32 * wk;     // first key of this wave's half
-
-  TileRegs<D> regs;
-  int e = 0;
-  while (e < cnt && static_cast<unsigned>(list[e]) >= nbu) ++e;
-  if (e < cnt) {
-    const int64_t off = static_cast<int64_t>(list[e]) * kBlock * D;
-    load_tile<D>(regs, K + off, V + off, tid);
-  }
-  while (e < cnt) {
-    const int jb = list[e];
-    int en = e + 1;
-    while (en < cnt && static_cast<unsigned>(list[en]) >= nbu) ++en;
-    __syncthreads();            // every wave is done with the previous tile
-    store_tile<D>(regs, sk, sv, tid);
-    __syncthreads();
-    if (en < cnt) {
-      const int64_t off = static_cast<int64_t>(list[en]) * kBlock * D;
-      load_tile<D>(regs, K + off, V + off, tid);
-    }
-
-    // ---- S^T = K Q^T for keys key0 .. key0+31 ---------------------------
-    f32x16 s;
+  // list entry t, clamped to the last entry (loads past the end are redundant
+  // but in bounds, and their results are never used)
+  auto tile = [&](int t) {
+    TileRef r;
+    r.jb = list[t < cnt ? t : cnt - 1];
+    r.real = static_cast<unsigned>(r.jb) < static_cast<unsigned>(a.nb);
+    r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
+    return r;
+  };
+  // S^T of this wave's 32 keys from the K tile in `kb`
+  auto scores = [&](const u32x4* kb) {
+    f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const u32x4 u = sk[k_chunk_slot<D>(key0 + li, 2 * ks + h)];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), qf[ks], s, 0, 0, 0);
+      const u32x4 u = kb[k_chunk_slot<D>(key0 + li, 2 * ks + h)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), qf[ks], acc,
+                                                    0, 0, 0);
     }
-    // ---- pad keys of a partial patch -----------------------------------
-    const BlockExtent ext = block_extent(jb, a);
-    if (!ext.full()) {
+    return acc;
+  };
+  // V^T fragment addressing (see read_v_transposed): constant per lane
+  const int vgrp = lane >> 4, vsl = lane & 15;
+  const int vcol = 16 * (vgrp & 1) + 4 * (vsl & 3);     // + 32 dt
+  const int vrow = key0 + 4 * (vgrp >> 1) + (vsl >> 2);  // + 16 st (+ 8)
+
+  if (cnt > 0) {
+    // ---- prologue: K/V of tile 0 and K of tile 1 in LDS, S^T of tile 0 ----
+    uint32_t koff[S::kIters], voff[S::kIters];
+    tile_load_offsets<D, false>(koff, wave, lane);
+    tile_load_offsets<D, true>(voff, wave, lane);
+    const TileRef t0 = tile(0);
+    issue_tile_load<D>(K + t0.off, k_slot0, koff, wave);
+    issue_tile_load<D>(V + t0.off, v_slot0, voff, wave);
+    issue_tile_load<D>(K + tile(1).off, k_slot1, koff, wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 s_cur = scores(k_slot0);
+    TileRef t_cur = t0;
+    TileRef t_next = tile(1);
+    __syncthreads();            // tile 0's K slot is refilled next
+
+    // tile e: K of e+1 is in k_slot[(e+1)%2], V of e in v_slot[e%2]; K of e+2
+    // streams into k_slot[e%2] and V of e+1 into v_slot[(e+1)%2]
+    auto body = [&](int e, auto parity) {
+      constexpr int kOdd = decltype(parity)::value;
+      u32x4* const k_here = kOdd ? k_slot1 : k_slot0;    // slot e % 2
+      u32x4* const k_next = kOdd ? k_slot0 : k_slot1;    // slot (e + 1) % 2
+      u32x4* const v_here = kOdd ? v_slot1 : v_slot0;
+      u32x4* const v_next = kOdd ? v_slot0 : v_slot1;
+      const TileRef t2 = tile(e + 2);
+      issue_tile_load<D>(K + t2.off, k_here, koff, wave);
+      issue_tile_load<D>(V + t_next.off, v_next, voff, wave);
+
+      // S^T of tile e+1 goes to the matrix cores first; nothing below
+      // depends on it until the end of the tile
+      const f32x16 s_nxt = scores(k_next);
+
+      // ---- softmax of tile e ------------------------------------------------
+      f32x16& s = s_cur;
+      const BlockExtent ext = t_cur.real ? block_extent(t_cur.jb, a) : BlockExtent{0, 0};
+      if (!ext.full()) {
+        const uint32_t bits = real_key_bits(ext, wk, h);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
+      }
+      float mt = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+      if (__any(mt > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mt);
+        const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);   // m = -inf gives 0
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      const float msub = (m == -INFINITY) ? 0.0f : m;
+      bf16x8 pb[2];
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (!ext.real(key)) s[r] = -INFINITY;
+        // v_exp_f32 directly: arguments are <= 2^3 above the running max and
+        // results below the fp32 normal range are flushed, which bf16 P and the
+        // fp32 sums tolerate
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
+        ps[r & 3] += pr;
+        pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
       }
-    }
-    // ---- online softmax (base 2, lazily rescaled) -----------------------
-    float mt = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
-    if (__any(mt > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);   // m = -inf gives 0
-      m = mn;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    const float msub = (m == -INFINITY) ? 0.0f : m;
-    bf16x8 pb[2];
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // v_exp_f32 directly: arguments are <= 2^3 above the running max and
-      // results below the fp32 normal range are flushed, which bf16 P and the
-      // fp32 sums tolerate
-      p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
-      pb[r >> 3][r & 7] = static_cast<__bf16>(p[r]);
-    }
-#pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-      for (int r = 0; r < w; ++r) p[r] += p[r + w];
-    l += p[0];
-    // ---- O^T += V^T P^T over this wave's 32 keys ------------------------
-    // lane (d = 32 dt + li, h): A elements 0..3 = keys k0 .. k0+3 and 4..7 =
-    // keys k0+8 .. k0+11 with k0 = key0 + 16 st + 4 h, the order in which the
-    // S^T accumulator holds P. Source lane s of a 16-lane group reads row
-    // k0 + s/4 at columns base + 4 (s % 4), base = 32 dt + 16 ((lane / 16) % 2).
-    {
-      const int grp = lane >> 4, sl = lane & 15;
-      const int col = 16 * (grp & 1) + 4 * (sl & 3);     // + 32 dt
-      const int rsub = 4 * (grp >> 1) + (sl >> 2);        // + key0 + 16 st (+ 8)
+      l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+
+      // ---- O^T += V^T P^T over this wave's 32 keys --------------------------
+      const uint16_t* sv = reinterpret_cast<const uint16_t*>(v_here);
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const int r0 = key0 + 16 * st + rsub;
-          const int cc = 32 * dt + col;
-          const uint16_t* a0 = sv_elems + v_chunk_slot<D>(r0, cc >> 3) * 8 + (cc & 7);
-          const uint16_t* a1 = sv_elems + v_chunk_slot<D>(r0 + 8, cc >> 3) * 8 + (cc & 7);
-          const s16x4 lo = read_v_transposed(a0);
-          const s16x4 hi = read_v_transposed(a1);
+          const int r0 = vrow + 16 * st;
+          const int cc = 32 * dt + vcol;
+          const s16x4 lo = read_v_transposed(sv + v_chunk_slot<D>(r0, cc >> 3) * 8 + (cc & 7));
+          const s16x4 hi = read_v_transposed(sv + v_chunk_slot<D>(r0 + 8, cc >> 3) * 8 + (cc & 7));
           const s16x4 both[2] = {lo, hi};
           bf16x8 av;
           __builtin_memcpy(&av, both, sizeof(av));
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[st], o[dt], 0, 0, 0);
         }
       }
+      s_cur = s_nxt;
+      t_cur = t_next;
+      t_next = t2;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int e = 0; e < cnt; e += 2) {
+      body(e, std::integral_constant<int, 0>{});
+      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
     }
-    e = en;
   }
 
   // ---- merge the two key halves of every query row -----------------------
   l += __shfl_xor(l, 32);       // both lanes of a row hold the same m
-  __syncthreads();              // tile buffers are free
-  float* part = reinterpret_cast<float*>(smem) + wq * 64 * (kDT * 16 + 2);
-  constexpr int kStride = 64;   // lane-major: element j of lane x at part[j * 64 + x]
+  // lane-major partials of query half wq: element j of lane x at part[j * 64 + x]
+  float* const part = reinterpret_cast<float*>(wq ? k_slot1 : k_slot0);
+  static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
   if (wk == 1) {
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * kStride + lane] = o[dt][r];
-    part[(kDT * 16) * kStride + lane] = m;
-    part[(kDT * 16 + 1) * kStride + lane] = l;
+      for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * 64 + lane] = o[dt][r];
+    merge_ml[wq * 64 + lane] = m;
+    merge_ml[(2 + wq) * 64 + lane] = l;
   }
   __syncthreads();
   if (wk == 1) return;
-  const float m1 = part[(kDT * 16) * kStride + lane];
-  const float l1 = part[(kDT * 16 + 1) * kStride + lane];
+  const float m1 = merge_ml[wq * 64 + lane];
+  const float l1 = merge_ml[(2 + wq) * 64 + lane];
   const float mm = fmaxf(m, m1);
   const float a0 = (m == -INFINITY) ? 0.0f : exp2f(m - mm);
   const float a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - mm);
@@ -303,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * g + x;
-        v[x] = o[dt][r] * w0 + part[(dt * 16 + r) * kStride + lane] * w1;
+        v[x] = o[dt][r] * w0 + part[(dt * 16 + r) * 64 + lane] * w1;
       }
       uint2 w;
       w.x = static_cast<uint32_t>(f32_to_bf16_rne(v[0])) |
