@@ -26,6 +26,9 @@ GRIDS = {
     "ragged-f32-d128": (2, 13, 27, 2, 128, "f32", 0.7),
     "ragged-bf16-d64": (5, 9, 17, 2, 64, "bf16", 1.0),
     "wide-bf16-d128": (3, 24, 88, 2, 128, "bf16", 0.7),
+    "one-block-bf16": (1, 8, 8, 2, 64, "bf16", 1.0),
+    "one-partial-block-f32": (1, 3, 5, 2, 128, "f32", 1.0),
+    "one-row-high-bf16": (7, 1, 40, 1, 128, "bf16", 1.0),
 }
 
 
@@ -71,6 +74,9 @@ MASK_CASES = [
     ("ragged-f32-d128", 0.4, (0, 1, 2), None),
     ("ragged-bf16-d64", 0.9, (1, 0, 0), 1.0),
     ("wide-bf16-d128", 0.8, None, 1.0),
+    ("one-block-bf16", 0.5, None, None),
+    ("one-partial-block-f32", 0.5, (1, 1, 1), None),
+    ("one-row-high-bf16", 0.3, (1, 0, 1), 1.0),
 ]
 
 
@@ -134,6 +140,9 @@ ATTN_CASES = [
     ("ragged-bf16-d64", 0.5, None),
     ("wide-bf16-d128", 0.8, None),
     ("ragged-bf16-d128", 0.0, None),
+    ("one-block-bf16", 0.5, None),
+    ("one-partial-block-f32", 0.5, None),
+    ("one-row-high-bf16", 0.3, (1, 0, 1)),
 ]
 
 
