@@ -106,6 +106,36 @@ def run_steps(cabf, geom, bufs, thr, sta, n, timed):
     return stage
 
 
+def kernel_source_digest() -> str:
+    """sha256 of the attention kernel's sources (ties a counter profile to a kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attention_mfma.hip", "attention_common.hpp", "geometry.hpp"):
+        with open(os.path.join(ROOT, "content_adaptive_block_fractal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    or None when that summary was taken on a different kernel source or workload."""
+    path = os.path.join(ROOT, "profiles", f"bsa_fwd_mfma.{workload}.hbm.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                fields[k.strip("`")] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(q, k, v, w, thr, sta, budget_s):
     """The CPU oracle on a bounded sample of the same layer: head 0's permute and
     block mask (all rows) plus attention for the first query blocks that fit the
@@ -242,7 +272,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": profiled_traffic(w.name),
+            "traffic_unit": "bytes per launch (2 x FETCH_SIZE + WRITE_SIZE)",
             "algorithmic_unit": "4*64*64*head_dim flops per kept 64x64 tile",
             "avg_launch_ms": attn_ms,
         },
