@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--sparsity", type=float, default=0.80)
     ap.add_argument("--sta", action="store_true", help="union the +-1 sliding-tile window")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--deterministic", action="store_true",
+                    help="walk every block list from its first entry (bit-reproducible attention)")
     ap.add_argument("--variants", type=int, default=1,
                     help="also time the 90%% and window variants (0 to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -75,7 +77,7 @@ def calibrate_thr(cabf, qp, kp, geom, target, sta, ws, kv_count, kv_index, iters
     return best[0]
 
 
-def run_steps(cabf, geom, bufs, thr, sta, n, timed):
+def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0):
     """n steps of the whole path; returns per-stage event times (ms) if timed."""
     import torch
     q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
@@ -91,7 +93,7 @@ def run_steps(cabf, geom, bufs, thr, sta, n, timed):
         cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
         if timed:
             ev[2].record()
-        cabf.cabf_bsa_forward(geom, qp, kp, vp, cnt, idx, scale, op, None)
+        cabf.cabf_bsa_forward(geom, qp, kp, vp, cnt, idx, scale, op, None, flags)
         if timed:
             ev[3].record()
         cabf.cabf_unpermute(geom, op, o)
@@ -210,16 +212,16 @@ def main():
     ws = cabf.mask_workspace(geom, dev)
     bufs = (q, k, v, qp, kp, vp, op, o, cnt, idx, ws)
 
-    def measure(sparsity, sta, steps, warmup):
+    def measure(sparsity, sta, steps, warmup, flags):
         cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
         thr = calibrate_thr(cabf, qp, kp, geom, sparsity, sta, ws, cnt, idx)
-        run_steps(cabf, geom, bufs, thr, sta, warmup, timed=False)
+        run_steps(cabf, geom, bufs, thr, sta, warmup, timed=False, flags=flags)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run_steps(cabf, geom, bufs, thr, sta, steps, timed=False)
+        run_steps(cabf, geom, bufs, thr, sta, steps, timed=False, flags=flags)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        stages = run_steps(cabf, geom, bufs, thr, sta, steps, timed=True)
+        stages = run_steps(cabf, geom, bufs, thr, sta, steps, timed=True, flags=flags)
         kept = int(cnt.sum(dtype=torch.int64).item())
         flops = 4.0 * 64 * 64 * w.head_dim * kept
         med = {kk: statistics.median(vv) for kk, vv in stages.items()}
@@ -237,7 +239,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     sta = (1, 1, 1) if args.sta else None
-    main_run = measure(args.sparsity, sta, args.steps, args.warmup)
+    flags = cabf.BSA_DETERMINISTIC if args.deterministic else 0
+    main_run = measure(args.sparsity, sta, args.steps, args.warmup, flags)
     ms = main_run["wall_ms"]
     attn_ms = main_run["stage_ms_mean"]["attention"]
     mask_ms = main_run["stage_ms_mean"]["mask"]
@@ -264,6 +267,8 @@ def main():
             "target_sparsity": args.sparsity, "sparsity": main_run["sparsity"],
             "thr": main_run["thr"], "sta_window": list(sta) if sta else None,
             "parallelism": "single GPU",
+            "attention_order": "list order (deterministic)" if args.deterministic
+                               else "clock-phased start (default)",
         },
         "roofline": {
             "bound": "mfma",
@@ -285,12 +290,17 @@ def main():
     }
     if args.variants:
         var = {}
-        for sp, st in ((0.90, None), (0.80, (1, 1, 1)), (0.90, (1, 1, 1))):
-            if sp == args.sparsity and st == sta:
+        cases = [(0.90, None, flags), (0.80, (1, 1, 1), flags), (0.90, (1, 1, 1), flags),
+                 (args.sparsity, sta, flags ^ cabf.BSA_DETERMINISTIC)]
+        for sp, st, fl in cases:
+            if sp == args.sparsity and st == sta and fl == flags:
                 continue
-            r = measure(sp, st, max(3, args.steps // 4), 2)
+            r = measure(sp, st, max(3, args.steps // 4), 2, fl)
             a = r["stage_ms_mean"]["attention"]
-            var[f"{int(sp * 100)}%{'+window' if st else ''}"] = dict(
+            name = f"{int(round(sp * 100))}%{'+window' if st else ''}"
+            if fl != flags:
+                name += " deterministic" if fl else " clock-phased"
+            var[name] = dict(
                 thr=r["thr"], sparsity=r["sparsity"], ms_per_step=r["wall_ms"],
                 attention_ms=a, mask_ms=r["stage_ms_mean"]["mask"],
                 attention_tflops=r["flops"] / (a * 1e-3) / 1e12,

@@ -64,7 +64,8 @@ def _load():
         "cabf_mask_workspace_bytes": (SZ, [G]),
         "cabf_build_block_mask": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, F32,
                                                  ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
-        "cabf_bsa_forward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, F32, P, P, P]),
+        "cabf_bsa_forward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, F32, P, P,
+                                            ctypes.c_uint, P]),
         "cabf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -194,7 +195,11 @@ def cabf_build_block_mask(geom: Geom, qp, kp, scale: float, thr: float, sta, kv_
     _check("cabf_build_block_mask", st)
 
 
-def cabf_bsa_forward(geom: Geom, qp, kp, vp, kv_count, kv_index, scale: float, op, lse=None):
+BSA_DETERMINISTIC = 1    # cabf_bsa_forward flag: walk every list from its first entry
+
+
+def cabf_bsa_forward(geom: Geom, qp, kp, vp, kv_count, kv_index, scale: float, op, lse=None,
+                     flags: int = 0):
     """Block-sparse attention over the listed tiles: op [B, h, N, d] (+ lse [B, h, N])."""
     s = geom.sizes()
     nb = s["n_blocks"]
@@ -206,7 +211,7 @@ def cabf_bsa_forward(geom: Geom, qp, kp, vp, kv_count, kv_index, scale: float, o
         _dev(kp, ps, qp.dtype, "kp"), _dev(vp, ps, qp.dtype, "vp"),
         _dev(kv_count, lead, torch.int32, "kv_count"),
         _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), float(scale),
-        _dev(op, ps, qp.dtype, "op"), lp, _stream(qp))
+        _dev(op, ps, qp.dtype, "op"), lp, int(flags), _stream(qp))
     _check("cabf_bsa_forward", st)
 
 
@@ -250,11 +255,13 @@ def build_block_mask(qp, kp, geom: Geom, thr: float, sta=None, scale=None, retur
     return kv_count, kv_index
 
 
-def bsa_forward(qp, kp, vp, kv_count, kv_index, geom: Geom, scale=None, return_lse=False):
+def bsa_forward(qp, kp, vp, kv_count, kv_index, geom: Geom, scale=None, return_lse=False,
+                deterministic=False):
     op = torch.empty_like(qp)
     lse = torch.empty(qp.shape[:3], dtype=torch.float32, device=qp.device) if return_lse else None
     cabf_bsa_forward(geom, qp, kp, vp, kv_count, kv_index,
-                     default_scale(geom) if scale is None else scale, op, lse)
+                     default_scale(geom) if scale is None else scale, op, lse,
+                     BSA_DETERMINISTIC if deterministic else 0)
     return (op, lse) if return_lse else op
 
 

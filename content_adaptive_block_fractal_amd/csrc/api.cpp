@@ -152,7 +152,7 @@ int cabf_build_block_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, 
 
 int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp,
                      const void* vp, const int32_t* kv_count, const int32_t* kv_index,
-                     float scale, void* op, float* lse, hipStream_t stream) {
+                     float scale, void* op, float* lse, unsigned flags, hipStream_t stream) {
   Geo geo;
   const int st = make_geo(g, &geo);
   if (st != CABF_OK) return st;
@@ -161,13 +161,14 @@ int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const
       kv_index == nullptr || op == nullptr)
     return CABF_EINVAL;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
+  if ((flags & ~static_cast<unsigned>(CABF_BSA_DETERMINISTIC)) != 0) return CABF_EINVAL;
   if (reinterpret_cast<uintptr_t>(qp) % 16 || reinterpret_cast<uintptr_t>(kp) % 16 ||
       reinterpret_cast<uintptr_t>(vp) % 16 || reinterpret_cast<uintptr_t>(op) % 16 ||
       reinterpret_cast<uintptr_t>(kv_count) % 4 || reinterpret_cast<uintptr_t>(kv_index) % 4 ||
       reinterpret_cast<uintptr_t>(lse) % 4)
     return CABF_EINVAL;
   cabf::launch_bsa_forward(geo, dtype == CABF_BF16, qp, kp, vp, kv_count, kv_index, scale, op,
-                           lse, stream);
+                           lse, (flags & CABF_BSA_DETERMINISTIC) == 0, stream);
   return launched();
 }
 

@@ -9,7 +9,7 @@ namespace cabf {
 
 void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
-                        float* lse, hipStream_t stream) {
+                        float* lse, bool phased, hipStream_t stream) {
   AttnArgs a{};
   a.qp = qp;
   a.kp = kp;
@@ -27,9 +27,9 @@ void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp,
   a.N = g.N;
   a.BH = g.BH;
   if (bf16)
-    launch_bsa_forward_mfma(a, g.D, stream);      // bf16 matrix cores
+    launch_bsa_forward_mfma(a, g.D, phased, stream);   // bf16 matrix cores
   else
-    launch_bsa_forward_simple(a, false, g.D, stream);
+    launch_bsa_forward_simple(a, false, g.D, stream);  // always walks lists in order
 }
 
 }  // namespace cabf

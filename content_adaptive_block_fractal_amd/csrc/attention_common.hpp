@@ -24,6 +24,14 @@ struct AttnArgs {
   int nb, Ty, Tx, H, W;
   int64_t N;          // reordered tokens per (batch, head)
   int64_t BH;         // batch * heads
+  // Device-clock ticks (100 MHz) a workgroup is expected to spend per kept
+  // tile, or 0. Nonzero: a workgroup starts its pass over its (ascending) list
+  // at the key block a clock-driven sweep of the key range has reached, and
+  // wraps around, so that concurrent workgroups read the same K/V tiles
+  // together and find them in L2. Only the summation order changes: results
+  // agree to rounding but may differ bitwise between runs. 0 walks every list
+  // from its first entry (bit-reproducible).
+  uint32_t sweep_ticks;
 };
 
 // Real rows / columns of block b's 8x8 patch (pads sit at the bottom/right
@@ -60,6 +68,6 @@ __device__ inline void store_elem(float* p, float v) { *p = v; }
 __device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
 void launch_bsa_forward_simple(const AttnArgs& a, bool bf16, int D, hipStream_t stream);
-void launch_bsa_forward_mfma(const AttnArgs& a, int D, hipStream_t stream);
+void launch_bsa_forward_mfma(const AttnArgs& a, int D, bool phased, hipStream_t stream);
 
 }  // namespace cabf

@@ -7,9 +7,13 @@
 //   32*(w&1) .. +31 and the key half 32*(w>>1) .. +31 of every kept tile; it
 //   keeps its own running max, sum and output for that half, and the two
 //   halves of a query row are merged once at the end through LDS (the merge
-//   of two partial softmax sums is exact). The workgroup walks its kept key
-//   blocks in list order. Workgroup ids are remapped so that each XCD (its
-//   own L2) processes a contiguous run of query blocks of the same head.
+//   of two partial softmax sums is exact). Workgroup ids are remapped so
+//   that each XCD (its own L2) processes a contiguous run of query blocks of
+//   the same head, and by default each workgroup starts its pass over its
+//   ascending list where a clock-driven sweep of the key range stands, so
+//   that the workgroups of a head sweep the key range together and read the
+//   same K/V tiles at about the same time (in deterministic mode the list is
+//   walked from its first entry).
 //
 // Per kept tile, per wave, with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T    A = K (LDS, row-major, 16-byte chunks XOR-swizzled by row)
@@ -199,11 +203,40 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   const int cnt = min(max(a.kv_count[qblk], 0), a.nb);
   const int32_t* __restrict__ list = a.kv_index + qblk * a.nb;
   const int key0 = 32 * wk;     // first key of this wave's half
-  // list entry t, clamped to the last entry (loads past the end are redundant
-  // but in bounds, and their results are never used)
+
+  // Where the pass over the list starts (AttnArgs::sweep_ticks): at the
+  // fraction (clock mod P) / P of the list. Lists of a head spread their
+  // entries over the key range alike (or are shifted copies of each other),
+  // so equal fractions mean nearby key blocks. The period P must be the same
+  // for every workgroup of a head, or clock mod P would not be coherent:
+  // P = sweep_ticks * the mean list length of 64 rows spread evenly over the
+  // head, which all of them sample alike. Wave 0 computes the start and
+  // shares it through LDS, so that all waves agree on it.
+  __shared__ int start_shared;
+  if (wave == 0) {
+    int start = 0;
+    if (a.sweep_ticks != 0 && cnt > 1) {
+      const int32_t* head_counts = a.kv_count + bh * a.nb;
+      int total = min(max(head_counts[(lane * a.nb) >> 6], 1), a.nb);
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) total += __shfl_xor(total, sh);
+      // 32 clock bits wrap every 43 s: one incoherent moment, harmless
+      const uint32_t period = static_cast<uint32_t>(max(total >> 6, 1)) * a.sweep_ticks;
+      const uint32_t now = static_cast<uint32_t>(__builtin_amdgcn_s_memrealtime());
+      start = static_cast<int>(static_cast<uint64_t>(now % period) * cnt / period);
+    }
+    if (lane == 0) start_shared = start;
+  }
+  __syncthreads();
+  const int start = __builtin_amdgcn_readfirstlane(start_shared);
+  // list entry t of the pass (entry start + t, wrapped), clamped to the last
+  // one (loads past the end are redundant but in bounds, and their results are
+  // never used)
   auto tile = [&](int t) {
     TileRef r;
-    r.jb = list[t < cnt ? t : cnt - 1];
+    int pos = (t < cnt ? t : cnt - 1) + start;
+    pos -= pos >= cnt ? cnt : 0;
+    r.jb = list[pos];
     r.real = static_cast<unsigned>(r.jb) < static_cast<unsigned>(a.nb);
     r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
     return r;
@@ -370,9 +403,13 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
 
 }  // namespace
 
-void launch_bsa_forward_mfma(const AttnArgs& a, int D, hipStream_t stream) {
-  const int64_t n = a.BH * a.nb;
+void launch_bsa_forward_mfma(const AttnArgs& args, int D, bool phased, hipStream_t stream) {
+  const int64_t n = args.BH * args.nb;
   const unsigned grid = static_cast<unsigned>(n);
+  AttnArgs a = args;
+  // measured time per kept tile at two workgroups per CU (about 1.5 us at
+  // head_dim 128); the L2 reuse tolerates an error of a few tens of percent
+  a.sweep_ticks = phased ? (D == 64 ? 90u : 150u) : 0u;
   if (D == 64)
     hipLaunchKernelGGL((bsa_fwd_mfma<64>), dim3(grid), dim3(kThreads), 0, stream, a, n);
   else

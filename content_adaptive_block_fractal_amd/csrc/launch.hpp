@@ -28,6 +28,6 @@ void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void
 
 void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
-                        float* lse, hipStream_t stream);
+                        float* lse, bool phased, hipStream_t stream);
 
 }  // namespace cabf

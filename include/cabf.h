@@ -52,6 +52,11 @@ typedef enum {
   CABF_F32 = 1             /* float32 tensors                                   */
 } cabf_dtype;
 
+/* Flags of cabf_bsa_forward. */
+enum {
+  CABF_BSA_DETERMINISTIC = 1u   /* visit each row's blocks in list order */
+};
+
 /* Layer geometry. The padded grid and block count are derived:
  *   Ty = ceil(H/P), Tx = ceil(W/P), Hp = Ty*P, Wp = Tx*P,
  *   nb = T*Ty*Tx blocks of P*P tokens, N = nb*P*P.
@@ -140,11 +145,18 @@ int cabf_build_block_mask(const cabf_geom* g, cabf_dtype dtype,
  * kv_count [B, heads, nb], kv_index [B, heads, nb, nb] (input; entries must be
  *   valid block indices; duplicates would be attended twice).
  * op: reordered [B, heads, N, head_dim] (output, pad rows included).
- * lse: NULL, or [B, heads, N] fp32 (output). scale > 0. */
+ * lse: NULL, or [B, heads, N] fp32 (output). scale > 0.
+ * flags: 0 or CABF_BSA_DETERMINISTIC (other bits give CABF_EINVAL). With 0, a
+ *   bf16 row may start its pass anywhere in its list (chosen from the device
+ *   clock so that concurrently running rows read the same K/V blocks, which
+ *   then stay in L2) and wraps around; the result is the same softmax sum in
+ *   another order, so it may differ from run to run in the last bits.
+ *   CABF_BSA_DETERMINISTIC walks every list from its first entry and gives
+ *   bit-identical results on every run. fp32 is always deterministic. */
 int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype,
                      const void* qp, const void* kp, const void* vp,
                      const int32_t* kv_count, const int32_t* kv_index, float scale,
-                     void* op, float* lse, hipStream_t stream);
+                     void* op, float* lse, unsigned flags, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* cabf_status_string(int status);

@@ -132,13 +132,15 @@ def test_attention_argument_checks():
     g = geom()
     def call(**kw):
         a = dict(q=DUMMY, k=DUMMY, v=DUMMY, cnt=DUMMY2, idx=DUMMY2, scale=0.125, op=DUMMY2,
-                 lse=None, dt=0)
+                 lse=None, dt=0, flags=0)
         a.update(kw)
         return L.cabf_bsa_forward(g, a["dt"], a["q"], a["k"], a["v"], a["cnt"], a["idx"],
-                                  a["scale"], a["op"], a["lse"], NULL)
+                                  a["scale"], a["op"], a["lse"], a["flags"], NULL)
     for key in ("q", "k", "v", "cnt", "idx", "op"):
         assert call(**{key: NULL}) == cabf.CABF_EINVAL, key
     assert call(scale=-1.0) == cabf.CABF_EINVAL
     assert call(scale=float("inf")) == cabf.CABF_EINVAL
     assert call(lse=ctypes.c_void_p(0x400002)) == cabf.CABF_EINVAL
     assert call(dt=2) == cabf.CABF_EINVAL
+    assert call(flags=2) == cabf.CABF_EINVAL
+    assert call(flags=cabf.BSA_DETERMINISTIC | 4) == cabf.CABF_EINVAL

@@ -6,7 +6,8 @@ mask of two heads (every row of them) and the attention of query blocks spread
 over those heads, chosen to include padded patches and the first and last
 blocks. Attention rows are compared where the GPU kept the same blocks as the
 oracle (rows of ill-posed cuts are counted by the mask check); a second check
-feeds the oracle's own lists of the sampled heads to cabf_bsa_forward.
+feeds the oracle's own lists of the sampled heads to cabf_bsa_forward (in
+deterministic list order; the first check uses the default clock-phased order).
 """
 import math
 
@@ -101,11 +102,12 @@ def test_full_size_layer(name, target, sta):
         assert torch.equal(o[0, hd, torch.from_numpy(inv[real_rows]).to(DEV)],
                            op[0, hd, torch.from_numpy(real_rows).to(DEV)])
 
-        # attention fed the oracle's lists for this head (the rest keeps the GPU's)
+        # attention fed the oracle's lists for this head (the rest keeps the
+        # GPU's), in deterministic list order
         cnt2, idx2 = cnt.clone(), idx.clone()
         cnt2[0, hd] = torch.from_numpy(info["kv_count"]).to(DEV)
         idx2[0, hd] = torch.from_numpy(info["kv_index"]).to(DEV)
-        op2 = cabf.bsa_forward(qp, kp, vp, cnt2, idx2, g, scale)
+        op2 = cabf.bsa_forward(qp, kp, vp, cnt2, idx2, g, scale, deterministic=True)
         torch.cuda.synchronize()
         sub_cnt = np.zeros_like(info["kv_count"])
         sub_cnt[blocks] = info["kv_count"][blocks]

@@ -164,6 +164,33 @@ def test_attention_on_oracle_lists(name, thr, sta):
     compare_attention(op, ref_o, q.dtype == torch.bfloat16, lse, ref_lse, label=name)
 
 
+@pytest.mark.parametrize("name", ["wide-bf16-d128", "ragged-bf16-d64"])
+def test_attention_visit_orders(name):
+    """Deterministic mode (lists walked from their first entry) is bit-identical
+    run to run; the default clock-phased start (a rotation of each list, which
+    varies between runs) stays within the same tolerance of the oracle."""
+    say(f"attention visit orders {name}")
+    g, og, q, k, v = make(name)
+    s = cabf.default_scale(g)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    torch.cuda.synchronize()
+    qn, kn, vn = to_np(qp), to_np(kp), to_np(vp)
+    info = oracle.build_block_mask(qn, kn, og, s, 0.3, None)
+    cnt = torch.from_numpy(info["kv_count"]).to(DEV)
+    idx = torch.from_numpy(info["kv_index"]).to(DEV)
+    ref_o, ref_lse = oracle.bsa_forward(qn, kn, vn, info["kv_count"], info["kv_index"], og, s)
+    o1, l1 = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=True)
+    o2, l2 = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    compare_attention(o1, ref_o, True, l1, ref_lse, label=f"{name} deterministic")
+    for rep in range(3):
+        o3, l3 = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True)
+        torch.cuda.synchronize()
+        compare_attention(o3, ref_o, True, l3, ref_lse, label=f"{name} clock-phased #{rep}")
+
+
 def test_attention_rows_with_no_blocks_and_arbitrary_lists():
     g, og, q, k, v = make("ragged-bf16-d128")
     nb = og.nb
