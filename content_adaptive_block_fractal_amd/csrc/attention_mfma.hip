@@ -96,6 +96,15 @@ __device__ inline int v_chunk_slot(int key, int chunk) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// max of v over lanes l and l ^ 32 (v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second: with both set
+// to v, the two results hold v of lane l and of lane l ^ 32 in every lane)
+__device__ inline float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // 4 consecutive keys of one head-dim column of the V tile (see above).
 __device__ inline s16x4 read_v_transposed(const uint16_t* sv_row_chunk) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -107,35 +116,38 @@ struct Stage {
   static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
   static constexpr int kIters = kBlock * kChunks / kThreads;   // chunks per thread per tensor
   static constexpr int kTile = kBlock * kChunks;               // 16-byte chunks per K (or V) tile
+  static constexpr int kRowsPerIter = kThreads / kChunks;      // rows one pass of the workgroup fills
 };
 
 // Direct-to-LDS copy of one K or V tile into a ring slot: each wave
 // instruction fills 64 consecutive 16-byte LDS chunks (lane l -> chunk base +
-// l); the lane fetches the global chunk that the swizzle places there. The
-// byte offsets of those chunks inside a tile are the same for every tile.
+// l); the lane fetches the global chunk that the swizzle places there. Pass i
+// covers the rows of pass 0 moved down by i * kRowsPerIter, a multiple of the
+// swizzle's period in the row, so a lane's source offset in pass i is its
+// offset in pass 0 plus a constant (added to the scalar base). The offsets are
+// the same for every tile.
 template <int D, bool IS_V>
-__device__ inline void tile_load_offsets(uint32_t (&off)[Stage<D>::kIters], int wave, int lane) {
+__device__ inline uint32_t tile_load_offset(int wave, int lane) {
   using S = Stage<D>;
-#pragma unroll
-  for (int i = 0; i < S::kIters; ++i) {
-    const int phys = (i * kWaves + wave) * 64 + lane;
-    const int row = phys / S::kChunks;
-    const int pc = phys % S::kChunks;
-    // the swizzle is an XOR with a function of the row: its own inverse
-    const int chunk = IS_V ? (v_chunk_slot<D>(row, pc) - row * S::kChunks)
-                           : (k_chunk_slot<D>(row, pc) - row * S::kChunks);
-    off[i] = static_cast<uint32_t>((row * D + chunk * 8) * 2);
-  }
+  static_assert(S::kRowsPerIter % 16 == 0, "swizzle period");
+  const int phys = wave * 64 + lane;
+  const int row = phys / S::kChunks;
+  const int pc = phys % S::kChunks;
+  // the swizzle is an XOR with a function of the row: its own inverse
+  const int chunk = IS_V ? (v_chunk_slot<D>(row, pc) - row * S::kChunks)
+                         : (k_chunk_slot<D>(row, pc) - row * S::kChunks);
+  return static_cast<uint32_t>((row * D + chunk * 8) * 2);
 }
 
 template <int D>
 __device__ __forceinline__ void issue_tile_load(const uint16_t* __restrict__ tile_src, u32x4* slot,
-                                                const uint32_t (&off)[Stage<D>::kIters], int wave) {
+                                                uint32_t off, int wave) {
   using S = Stage<D>;
-  const char* base = reinterpret_cast<const char*>(tile_src);
 #pragma unroll
-  for (int i = 0; i < S::kIters; ++i)
-    __builtin_amdgcn_global_load_lds(base + off[i], slot + (i * kWaves + wave) * 64, 16, 0, 0);
+  for (int i = 0; i < S::kIters; ++i) {
+    const char* base = reinterpret_cast<const char*>(tile_src + i * S::kRowsPerIter * D);
+    __builtin_amdgcn_global_load_lds(base + off, slot + (i * kWaves + wave) * 64, 16, 0, 0);
+  }
 }
 
 // List entry t -> element offset of its K/V block and whether it is a real
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int wq = wave & 1;      // query half of the block
   const int wk = wave >> 1;     // key half of every tile
   const int li = lane & 31;
@@ -229,14 +241,21 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   }
   __syncthreads();
   const int start = __builtin_amdgcn_readfirstlane(start_shared);
-  // list entry t of the pass (entry start + t, wrapped), clamped to the last
-  // one (loads past the end are redundant but in bounds, and their results are
-  // never used)
-  auto tile = [&](int t) {
-    TileRef r;
-    int pos = (t < cnt ? t : cnt - 1) + start;
+  // Entries of the pass are fetched 64 at a time, one per lane, a batch ahead
+  // of use, and read out with readlane: no list load is waited on per tile.
+  // Entry t of the pass is list entry start + t (wrapped); t is clamped to the
+  // last one (loads past the end are redundant but in bounds, and their
+  // results are never used).
+  auto load_batch = [&](int b) {
+    int pos = min(b * 64 + lane, cnt - 1) + start;
     pos -= pos >= cnt ? cnt : 0;
-    r.jb = list[pos];
+    return list[pos];
+  };
+  int batch_cur = 0, batch_nxt = 0;     // entries 64 B .. and 64 (B + 1) .. of the pass
+  auto tile = [&](int t) {
+    const int p = t < cnt ? t : cnt - 1;
+    TileRef r;
+    r.jb = __builtin_amdgcn_readlane(batch_cur, p & 63);
     r.real = static_cast<unsigned>(r.jb) < static_cast<unsigned>(a.nb);
     r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
     return r;
@@ -254,16 +273,26 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
     }
     return acc;
   };
-  // V^T fragment addressing (see read_v_transposed): constant per lane
+  // V^T fragment addressing (see read_v_transposed): the lane reads rows
+  // vrow + 16 st (+ 8), columns 32 dt + vcol. Rows 8 and 16 further down have
+  // the same swizzle, so one element offset per dt serves all four reads
+  // (the rest are constant offsets).
   const int vgrp = lane >> 4, vsl = lane & 15;
-  const int vcol = 16 * (vgrp & 1) + 4 * (vsl & 3);     // + 32 dt
-  const int vrow = key0 + 4 * (vgrp >> 1) + (vsl >> 2);  // + 16 st (+ 8)
+  const int vcol = 16 * (vgrp & 1) + 4 * (vsl & 3);
+  const int vrow = key0 + 4 * (vgrp >> 1) + (vsl >> 2);
+  int vaddr[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) {
+    const int cc = 32 * dt + vcol;
+    vaddr[dt] = v_chunk_slot<D>(vrow, cc >> 3) * 8 + (cc & 7);
+  }
 
   if (cnt > 0) {
     // ---- prologue: K/V of tile 0 and K of tile 1 in LDS, S^T of tile 0 ----
-    uint32_t koff[S::kIters], voff[S::kIters];
-    tile_load_offsets<D, false>(koff, wave, lane);
-    tile_load_offsets<D, true>(voff, wave, lane);
+    const uint32_t koff = tile_load_offset<D, false>(wave, lane);
+    const uint32_t voff = tile_load_offset<D, true>(wave, lane);
+    batch_cur = load_batch(0);
+    batch_nxt = load_batch(1);
     const TileRef t0 = tile(0);
     issue_tile_load<D>(K + t0.off, k_slot0, koff, wave);
     issue_tile_load<D>(V + t0.off, v_slot0, voff, wave);
@@ -283,13 +312,35 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
       u32x4* const k_next = kOdd ? k_slot0 : k_slot1;    // slot (e + 1) % 2
       u32x4* const v_here = kOdd ? v_slot1 : v_slot0;
       u32x4* const v_next = kOdd ? v_slot0 : v_slot1;
+      if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
+        batch_cur = batch_nxt;
+        batch_nxt = load_batch(((e + 2) >> 6) + 1);
+      }
       const TileRef t2 = tile(e + 2);
       issue_tile_load<D>(K + t2.off, k_here, koff, wave);
       issue_tile_load<D>(V + t_next.off, v_next, voff, wave);
 
+      // V^T fragments of tile e (16 transposing reads)
+      bf16x8 vf[kDT][2];
+      auto read_v = [&]() {
+        const uint16_t* sv = reinterpret_cast<const uint16_t*>(v_here);
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const uint16_t* p = sv + vaddr[dt] + 16 * st * D;
+            const s16x4 both[2] = {read_v_transposed(p), read_v_transposed(p + 8 * D)};
+            __builtin_memcpy(&vf[dt][st], both, sizeof(bf16x8));
+          }
+      };
       // S^T of tile e+1 goes to the matrix cores first; nothing below
-      // depends on it until the end of the tile
+      // depends on it until the end of the tile. The V reads are issued
+      // right behind it and kept there (the scheduler would otherwise sink
+      // each pair next to its product and wait on it), so that their LDS
+      // latency hides behind the matrix work and the softmax.
       const f32x16 s_nxt = scores(k_next);
+      read_v();
+      __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax of tile e ------------------------------------------------
       f32x16& s = s_cur;
@@ -302,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
       float mt = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+      mt = pair_max(mt) * c;
       if (__any(mt > m + kRescaleSlack)) {
         const float mn = fmaxf(m, mt);
         const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);   // m = -inf gives 0
@@ -328,21 +379,11 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
       l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
       // ---- O^T += V^T P^T over this wave's 32 keys --------------------------
-      const uint16_t* sv = reinterpret_cast<const uint16_t*>(v_here);
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
+      for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r0 = vrow + 16 * st;
-          const int cc = 32 * dt + vcol;
-          const s16x4 lo = read_v_transposed(sv + v_chunk_slot<D>(r0, cc >> 3) * 8 + (cc & 7));
-          const s16x4 hi = read_v_transposed(sv + v_chunk_slot<D>(r0 + 8, cc >> 3) * 8 + (cc & 7));
-          const s16x4 both[2] = {lo, hi};
-          bf16x8 av;
-          __builtin_memcpy(&av, both, sizeof(av));
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[st], o[dt], 0, 0, 0);
-        }
-      }
+        for (int st = 0; st < 2; ++st)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][st], pb[st], o[dt], 0, 0, 0);
       s_cur = s_nxt;
       t_cur = t_next;
       t_next = t2;
