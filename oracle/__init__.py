@@ -25,7 +25,10 @@ from .nabla import (  # noqa: F401
     block_probs,
     cdf_cut,
     cdf_cut_details,
+    topk_cut,
+    topk_cut_details,
     sta_mask,
+    sta_only_lists,
     build_block_mask,
     mask_to_lists,
     lists_to_mask,

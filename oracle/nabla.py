@@ -196,6 +196,35 @@ def cdf_cut(p_row: np.ndarray, thr: float) -> np.ndarray:
     return cdf_cut_details(p_row, thr)[0]
 
 
+def topk_cut_details(p_row: np.ndarray, k: int):
+    """Fixed-budget selection of one row: the k most probable blocks.
+
+    Source: DynamicRad summary, "Dual-Mode Strategy", Static-Ratio mode: a
+    fixed ratio of the candidates is kept, for throughput. The page gives
+    neither the candidate set nor the ranking; the reading taken here keeps a
+    fixed count k = ceil(ratio * nb) per row, ranked by the same block
+    probabilities as the CDF cut (descending, ties: lower index first). k >= n
+    keeps every block.
+
+    Returns (kept_indices, k_eff, p_(k), p_(k+1)) with p_(n+1) = 0.
+    Pinned by: uniform rows (the k lowest indices), k = 1 equals argmax,
+    brute-force maximum-mass subsets for n <= 10, invariants.
+    """
+    p_row = np.asarray(p_row)
+    n = p_row.shape[0]
+    kk = max(1, min(int(k), n))
+    order = _descending_order(p_row)
+    ps = p_row[order]
+    p_k = float(ps[kk - 1])
+    p_next = float(ps[kk]) if kk < n else 0.0
+    return np.sort(order[:kk]), kk, p_k, p_next
+
+
+def topk_cut(p_row: np.ndarray, k: int) -> np.ndarray:
+    """Kept block indices (ascending) of one row; see ``topk_cut_details``."""
+    return topk_cut_details(p_row, k)[0]
+
+
 # ----------------------------------------------------------------------------
 # Methodology item 3: union with Sliding Tile Attention
 # ----------------------------------------------------------------------------
@@ -239,17 +268,22 @@ def mask_to_lists(mask: np.ndarray):
     return kv_count, kv_index
 
 
-def build_block_mask(qp, kp, g: Grid, scale: float, thr: float, sta=None, precision=np.float64):
+def build_block_mask(qp, kp, g: Grid, scale: float, thr: float, sta=None, precision=np.float64,
+                     topk=None):
     """Methodology items 2-3: pooled block attention -> CDF cut -> OR STA window.
 
-    qp, kp: reordered [..., N, d]. sta: None or (dt, dy, dx).
+    qp, kp: reordered [..., N, d]. sta: None or (dt, dy, dx). With ``topk`` set,
+    the CDF cut is replaced by the fixed-budget selection of ``topk_cut_details``
+    (thr is then unused).
     Returns a dict with
       mask       bool [..., nb, nb]  final kept blocks (M = M_nabla OR M_STA)
-      adaptive   bool [..., nb, nb]  the CDF part alone
+      adaptive   bool [..., nb, nb]  the CDF (or top-k) part alone
       p          [..., nb, nb]       block probabilities
-      k, s_prev, s_k, p_k, p_next    per-row cut quantities (see cdf_cut_details)
+      k, s_prev, s_k, p_k, p_next    per-row cut quantities (see cdf_cut_details;
+                                     s_prev and s_k are NaN for top-k)
       kv_count, kv_index             ascending per-row lists of ``mask``
-    The CDF runs over all blocks; the window is OR-ed in afterwards.
+      mode                           "cdf" or "topk"
+    The selection runs over all blocks; the window is OR-ed in afterwards.
     """
     qb = pool_blocks(qp, g, precision)
     kb = pool_blocks(kp, g, precision)
@@ -263,7 +297,11 @@ def build_block_mask(qp, kp, g: Grid, scale: float, thr: float, sta=None, precis
     p_next = np.zeros(lead + (g.nb,))
     for pos in np.ndindex(*lead):
         for i in range(g.nb):
-            kept, kk, a, b, c, d = cdf_cut_details(p[pos][i], thr)
+            if topk is None:
+                kept, kk, a, b, c, d = cdf_cut_details(p[pos][i], thr)
+            else:
+                kept, kk, c, d = topk_cut_details(p[pos][i], topk)
+                a = b = math.nan
             adaptive[pos][i][kept] = True
             k[pos][i], s_prev[pos][i], s_k[pos][i], p_k[pos][i], p_next[pos][i] = kk, a, b, c, d
     mask = adaptive.copy()
@@ -271,7 +309,15 @@ def build_block_mask(qp, kp, g: Grid, scale: float, thr: float, sta=None, precis
         mask |= sta_mask(g, *sta)
     kv_count, kv_index = mask_to_lists(mask)
     return dict(mask=mask, adaptive=adaptive, p=p, k=k, s_prev=s_prev, s_k=s_k,
-                p_k=p_k, p_next=p_next, kv_count=kv_count, kv_index=kv_index)
+                p_k=p_k, p_next=p_next, kv_count=kv_count, kv_index=kv_index,
+                mode="cdf" if topk is None else "topk")
+
+
+def sta_only_lists(g: Grid, dt: int, dy: int, dx: int):
+    """The pure sliding-tile configuration (NABLA summary, comparison with
+    static methods: an STA-only mask): every row keeps exactly its window.
+    Returns (kv_count int32 [nb], kv_index int32 [nb, nb]), ascending lists."""
+    return mask_to_lists(sta_mask(g, dt, dy, dx))
 
 
 def exempt_rows(info: dict, thr: float, e1: float = BLOCK_E1_WINDOW, e2: float = BLOCK_E2_RATIO):
@@ -281,9 +327,13 @@ def exempt_rows(info: dict, thr: float, e1: float = BLOCK_E1_WINDOW, e2: float =
         or |S_k - (1-thr)| <= e1 (rounding can move the cut by one block).
     E2: the k-th and (k+1)-th probabilities differ by at most e2 * p_(k)
         (rounding can swap which of the two is kept).
-    thr <= 0 rows are never exempt (every block is kept by definition).
+    thr <= 0 rows are never exempt (every block is kept by definition). For a
+    top-k selection (info["mode"] == "topk") only E2 applies: the count is fixed.
     Returns (e1_rows, e2_rows) as bool arrays over the rows.
     """
+    if info.get("mode") == "topk":
+        r2 = (info["p_k"] - info["p_next"]) <= e2 * info["p_k"]
+        return np.zeros(info["k"].shape, dtype=bool), r2
     if thr <= 0:
         z = np.zeros(info["k"].shape, dtype=bool)
         return z, z.copy()
@@ -390,6 +440,21 @@ def layer(q, k, v, g: Grid, scale: float, thr: float, sta=None):
     info = build_block_mask(qp, kp, g, scale, thr, sta)
     op, _ = bsa_forward(qp, kp, vp, info["kv_count"], info["kv_index"], g, scale)
     return unpermute(op, g), info
+
+
+def brute_force_topk(p_row, k: int):
+    """Exhaustive reference for the top-k selection on small rows (n <= ~12):
+    the size-k subset of largest mass, ties broken by the lexicographically
+    smallest sorted index tuple. Returns ascending indices."""
+    p_row = np.asarray(p_row, dtype=np.float64)
+    n = p_row.shape[0]
+    k = max(1, min(int(k), n))
+    best = None
+    for comb in itertools.combinations(range(n), k):
+        mass = float(sum(p_row[list(comb)]))
+        if best is None or mass > best[0]:
+            best = (mass, comb)
+    return np.array(best[1])
 
 
 def brute_force_cut(p_row, thr: float):

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.nabla import brute_force_cut
+from oracle.nabla import brute_force_cut, brute_force_topk
 
 RNG = np.random.default_rng(1234)
 
@@ -168,6 +168,70 @@ def test_exempt_rows_classification():
     e1, e2 = oracle.exempt_rows(info, 0.2)
     assert e1.tolist() == [True, True, False]
     assert e2.tolist() == [False, False, True]
+
+
+# --- fixed-budget (top-k) selection ------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(16, 3), (64, 64), (1260, 252), (4026, 604), (10, 25)])
+def test_topk_uniform_rows_keep_lowest_k(n, k):
+    p = np.full(n, 1.0 / n)
+    assert oracle.topk_cut(p, k).tolist() == list(range(min(k, n)))
+
+
+def test_topk_one_is_argmax_lowest_index():
+    for trial in range(50):
+        n = int(RNG.integers(1, 200))
+        p = RNG.integers(0, 5, n).astype(np.float64) + 1.0   # many exact ties
+        p /= p.sum()
+        assert oracle.topk_cut(p, 1).tolist() == [int(np.argmax(p))]
+
+
+def test_topk_matches_brute_force_subsets():
+    for trial in range(120):
+        n = int(RNG.integers(1, 11))
+        p = RNG.uniform(0.05, 1.0, n)
+        p /= p.sum()
+        k = int(RNG.integers(1, n + 1))
+        assert oracle.topk_cut(p, k).tolist() == brute_force_topk(p, k).tolist(), (p, k)
+
+
+def test_topk_invariants_random_rows():
+    for trial in range(200):
+        n = int(RNG.integers(1, 300))
+        z = RNG.standard_normal(n) * RNG.uniform(0.01, 5)
+        p = np.exp(z - z.max()); p /= p.sum()
+        k = int(RNG.integers(1, n + 3))
+        kept, kk, p_k, p_next = oracle.topk_cut_details(p, k)
+        assert kept.size == kk == min(k, n)
+        assert np.all(np.diff(kept) > 0)
+        dropped = np.setdiff1d(np.arange(n), kept)
+        if dropped.size:
+            assert p[dropped].max() <= p[kept].min() == p_k
+            assert p_next == p[dropped].max()
+
+
+def test_topk_mask_exempts_only_near_ties():
+    g = oracle.Grid(2, 16, 24, 8)
+    q = RNG.standard_normal((1, g.n_valid, 16))
+    k = RNG.standard_normal((1, g.n_valid, 16))
+    qp, kp = oracle.permute(q, g), oracle.permute(k, g)
+    info = oracle.build_block_mask(qp, kp, g, 0.25, 0.0, sta=(0, 1, 1), topk=4)
+    assert info["mode"] == "topk"
+    assert np.all(info["adaptive"].sum(-1) == 4)
+    assert np.array_equal(info["mask"], info["adaptive"] | oracle.sta_mask(g, 0, 1, 1)[None])
+    e1, e2 = oracle.exempt_rows(info, 0.0)
+    assert not e1.any()
+    assert np.array_equal(e2, (info["p_k"] - info["p_next"]) <= 1e-6 * info["p_k"])
+
+
+def test_sta_only_lists_are_the_window():
+    g = oracle.Grid(5, 24, 40, 8)
+    cnt, idx = oracle.sta_only_lists(g, 1, 1, 2)
+    m = oracle.sta_mask(g, 1, 1, 2)
+    assert np.array_equal(cnt, m.sum(-1))
+    assert np.array_equal(oracle.lists_to_mask(cnt, idx, g.nb), m)
+    for i in range(g.nb):
+        assert np.all(np.diff(idx[i][: cnt[i]]) > 0)
 
 
 # --- sliding tile window ----------------------------------------------------------
