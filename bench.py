@@ -77,7 +77,7 @@ def calibrate_thr(cabf, qp, kp, geom, target, sta, ws, kv_count, kv_index, iters
     return best[0]
 
 
-def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0):
+def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0, select="cdf", topk=0):
     """n steps of the whole path; returns per-stage event times (ms) if timed."""
     import torch
     q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
@@ -90,7 +90,12 @@ def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0):
         cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
         if timed:
             ev[1].record()
-        cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
+        if select == "cdf":
+            cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
+        elif select == "topk":
+            cabf.cabf_build_block_mask(geom, qp, kp, scale, 0.0, sta, cnt, idx, None, ws, topk=topk)
+        else:
+            cabf.cabf_build_sta_mask(geom, sta, cnt, idx)
         if timed:
             ev[2].record()
         cabf.cabf_bsa_forward(geom, qp, kp, vp, cnt, idx, scale, op, None, flags)
@@ -212,16 +217,18 @@ def main():
     ws = cabf.mask_workspace(geom, dev)
     bufs = (q, k, v, qp, kp, vp, op, o, cnt, idx, ws)
 
-    def measure(sparsity, sta, steps, warmup, flags):
+    def measure(sparsity, sta, steps, warmup, flags, select="cdf", topk=0):
         cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
-        thr = calibrate_thr(cabf, qp, kp, geom, sparsity, sta, ws, cnt, idx)
-        run_steps(cabf, geom, bufs, thr, sta, warmup, timed=False, flags=flags)
+        thr = (calibrate_thr(cabf, qp, kp, geom, sparsity, sta, ws, cnt, idx) if select == "cdf"
+               else None)
+        kw = dict(flags=flags, select=select, topk=topk)
+        run_steps(cabf, geom, bufs, thr, sta, warmup, timed=False, **kw)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run_steps(cabf, geom, bufs, thr, sta, steps, timed=False, flags=flags)
+        run_steps(cabf, geom, bufs, thr, sta, steps, timed=False, **kw)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        stages = run_steps(cabf, geom, bufs, thr, sta, steps, timed=True, flags=flags)
+        stages = run_steps(cabf, geom, bufs, thr, sta, steps, timed=True, **kw)
         kept = int(cnt.sum(dtype=torch.int64).item())
         flops = 4.0 * 64 * 64 * w.head_dim * kept
         med = {kk: statistics.median(vv) for kk, vv in stages.items()}
@@ -305,6 +312,17 @@ def main():
                 attention_ms=a, mask_ms=r["stage_ms_mean"]["mask"],
                 attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
                 step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
+        # the other selection rules at the same shape: a static keep ratio of
+        # 20% (top-k per row) and the sliding-tile window alone
+        k20 = cabf.topk_for_ratio(geom, 0.20)
+        for name, sel, st, kk in (("static top-k 20%", "topk", None, k20),
+                                  ("STA-only +-1", "sta", (1, 1, 1), 0)):
+            r = measure(None, st, max(3, args.steps // 4), 2, flags, select=sel, topk=kk)
+            a = r["stage_ms_mean"]["attention"]
+            var[name] = dict(k=kk or None, sparsity=r["sparsity"], ms_per_step=r["wall_ms"],
+                             attention_ms=a, mask_ms=r["stage_ms_mean"]["mask"],
+                             attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
+                             step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
         line["variants"] = var
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_run["thr"], sta, args.cpu_seconds)

@@ -26,7 +26,8 @@ CABF_OK, CABF_EINVAL, CABF_EUNSUPPORTED, CABF_EWORKSPACE, CABF_EHIP = 0, -1, -2,
 CABF_BF16, CABF_F32 = 0, 1
 
 EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_unpermute", "cabf_mask_workspace_bytes",
-            "cabf_build_block_mask", "cabf_bsa_forward", "cabf_status_string")
+            "cabf_build_block_mask", "cabf_build_block_mask_topk", "cabf_build_sta_mask",
+            "cabf_bsa_forward", "cabf_status_string")
 
 
 class CabfError(RuntimeError):
@@ -50,7 +51,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -m content_adaptive_block_fractal_amd.build)")
+            "(python content_adaptive_block_fractal_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
@@ -64,6 +65,9 @@ def _load():
         "cabf_mask_workspace_bytes": (SZ, [G]),
         "cabf_build_block_mask": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, F32,
                                                  ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
+        "cabf_build_block_mask_topk": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, I32,
+                                                      ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
+        "cabf_build_sta_mask": (ctypes.c_int, [G, ctypes.POINTER(_Sta), P, P, P]),
         "cabf_bsa_forward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, F32, P, P,
                                             ctypes.c_uint, P]),
         "cabf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -172,8 +176,9 @@ def cabf_mask_workspace_bytes(geom: Geom) -> int:
 
 
 def cabf_build_block_mask(geom: Geom, qp, kp, scale: float, thr: float, sta, kv_count, kv_index,
-                          block_prob, workspace):
-    """Adaptive block mask into kv_count [B, h, nb] / kv_index [B, h, nb, nb] (int32)."""
+                          block_prob, workspace, topk=None):
+    """Adaptive block mask into kv_count [B, h, nb] / kv_index [B, h, nb, nb] (int32).
+    With ``topk`` set, calls cabf_build_block_mask_topk (thr unused)."""
     s = geom.sizes()
     nb = s["n_blocks"]
     ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
@@ -186,13 +191,26 @@ def cabf_build_block_mask(geom: Geom, qp, kp, scale: float, thr: float, sta, kv_
         bp = _dev(block_prob, lead + (nb,), torch.float32, "block_prob")
     if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_cuda:
         raise ValueError("workspace must be a 1-D uint8 device tensor")
-    st = _lib.cabf_build_block_mask(
-        ctypes.byref(geom.c()), _dtype_code(qp), _dev(qp, ps, None, "qp"),
-        _dev(kp, ps, qp.dtype, "kp"), float(scale), float(thr), sta_c,
-        _dev(kv_count, lead, torch.int32, "kv_count"),
-        _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), bp,
-        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(qp))
-    _check("cabf_build_block_mask", st)
+    fn, sel = ((_lib.cabf_build_block_mask, float(thr)) if topk is None
+               else (_lib.cabf_build_block_mask_topk, int(topk)))
+    st = fn(ctypes.byref(geom.c()), _dtype_code(qp), _dev(qp, ps, None, "qp"),
+            _dev(kp, ps, qp.dtype, "kp"), float(scale), sel, sta_c,
+            _dev(kv_count, lead, torch.int32, "kv_count"),
+            _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), bp,
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(qp))
+    _check("cabf_build_block_mask" if topk is None else "cabf_build_block_mask_topk", st)
+
+
+def cabf_build_sta_mask(geom: Geom, sta, kv_count, kv_index):
+    """Sliding-tile window lists alone into kv_count / kv_index (int32)."""
+    nb = geom.sizes()["n_blocks"]
+    lead = (geom.batch, geom.heads, nb)
+    sta_c = None if sta is None else ctypes.byref(_Sta(1, int(sta[0]), int(sta[1]), int(sta[2])))
+    st = _lib.cabf_build_sta_mask(ctypes.byref(geom.c()), sta_c,
+                                  _dev(kv_count, lead, torch.int32, "kv_count"),
+                                  _dev(kv_index, lead + (nb,), torch.int32, "kv_index"),
+                                  _stream(kv_count))
+    _check("cabf_build_sta_mask", st)
 
 
 BSA_DETERMINISTIC = 1    # cabf_bsa_forward flag: walk every list from its first entry
@@ -241,7 +259,8 @@ def mask_workspace(geom: Geom, device) -> torch.Tensor:
 
 
 def build_block_mask(qp, kp, geom: Geom, thr: float, sta=None, scale=None, return_probs=False,
-                     workspace=None):
+                     workspace=None, topk=None):
+    """(kv_count, kv_index) of the CDF cut at thr, or of the top-``topk`` blocks per row."""
     nb = geom.sizes()["n_blocks"]
     lead = (geom.batch, geom.heads, nb)
     kv_count = torch.empty(lead, dtype=torch.int32, device=qp.device)
@@ -249,9 +268,24 @@ def build_block_mask(qp, kp, geom: Geom, thr: float, sta=None, scale=None, retur
     probs = torch.empty(lead + (nb,), dtype=torch.float32, device=qp.device) if return_probs else None
     ws = mask_workspace(geom, qp.device) if workspace is None else workspace
     cabf_build_block_mask(geom, qp, kp, default_scale(geom) if scale is None else scale, thr, sta,
-                          kv_count, kv_index, probs, ws)
+                          kv_count, kv_index, probs, ws, topk=topk)
     if return_probs:
         return kv_count, kv_index, probs
+    return kv_count, kv_index
+
+
+def topk_for_ratio(geom: Geom, ratio: float) -> int:
+    """Blocks kept per row for a static keep ratio: ceil(ratio * nb), at least 1."""
+    nb = geom.sizes()["n_blocks"]
+    return max(1, min(nb, math.ceil(ratio * nb - 1e-9)))
+
+
+def build_sta_mask(geom: Geom, sta, device):
+    nb = geom.sizes()["n_blocks"]
+    lead = (geom.batch, geom.heads, nb)
+    kv_count = torch.empty(lead, dtype=torch.int32, device=device)
+    kv_index = torch.empty(lead + (nb,), dtype=torch.int32, device=device)
+    cabf_build_sta_mask(geom, sta, kv_count, kv_index)
     return kv_count, kv_index
 
 

@@ -1,6 +1,7 @@
 """Build libcabf.so (HIP for gfx950) in-tree.
 
-Every call recompiles every source: ``python -m content_adaptive_block_fractal_amd.build``.
+Every call recompiles every source: ``python content_adaptive_block_fractal_amd/build.py``
+(run as a file: importing the package first would load the library it builds).
 """
 from __future__ import annotations
 

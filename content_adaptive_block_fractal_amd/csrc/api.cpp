@@ -58,6 +58,39 @@ int launched() {
   return e == hipSuccess ? CABF_OK : CABF_EHIP;
 }
 
+// Shared by the CDF (topk = 0) and the top-k entry points.
+int build_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp, float scale,
+               float thr, int topk, const cabf_sta* sta, int32_t* kv_count, int32_t* kv_index,
+               float* block_prob, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Geo geo;
+  const int st = make_geo(g, &geo);
+  if (st != CABF_OK) return st;
+  if (elem_bytes(dtype) == 0) return CABF_EINVAL;
+  if (qp == nullptr || kp == nullptr || kv_count == nullptr || kv_index == nullptr ||
+      workspace == nullptr)
+    return CABF_EINVAL;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
+  if (!(thr >= 0.0f && thr <= 1.0f)) return CABF_EINVAL;
+  if (reinterpret_cast<uintptr_t>(qp) % 16 || reinterpret_cast<uintptr_t>(kp) % 16 ||
+      reinterpret_cast<uintptr_t>(workspace) % 256 || reinterpret_cast<uintptr_t>(kv_count) % 4 ||
+      reinterpret_cast<uintptr_t>(kv_index) % 4 || reinterpret_cast<uintptr_t>(block_prob) % 4)
+    return CABF_EINVAL;
+  bool sta_on = false;
+  int dt = 0, dy = 0, dx = 0;
+  if (sta != nullptr && sta->enabled) {
+    if (sta->dt < 0 || sta->dy < 0 || sta->dx < 0) return CABF_EINVAL;
+    sta_on = true;
+    dt = sta->dt;
+    dy = sta->dy;
+    dx = sta->dx;
+  }
+  if (geo.nb > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
+  if (workspace_bytes < cabf::mask_workspace_layout(geo).total) return CABF_EWORKSPACE;
+  cabf::launch_build_block_mask(geo, dtype == CABF_BF16, qp, kp, scale, thr, topk, sta_on, dt, dy,
+                                dx, kv_count, kv_index, block_prob, workspace, stream);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,32 +154,30 @@ int cabf_build_block_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, 
                           float scale, float thr, const cabf_sta* sta, int32_t* kv_count,
                           int32_t* kv_index, float* block_prob, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
+  return build_mask(g, dtype, qp, kp, scale, thr, 0, sta, kv_count, kv_index, block_prob,
+                    workspace, workspace_bytes, stream);
+}
+
+int cabf_build_block_mask_topk(const cabf_geom* g, cabf_dtype dtype, const void* qp,
+                               const void* kp, float scale, int32_t k, const cabf_sta* sta,
+                               int32_t* kv_count, int32_t* kv_index, float* block_prob,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (k < 1) return CABF_EINVAL;
+  return build_mask(g, dtype, qp, kp, scale, 0.0f, k, sta, kv_count, kv_index, block_prob,
+                    workspace, workspace_bytes, stream);
+}
+
+int cabf_build_sta_mask(const cabf_geom* g, const cabf_sta* sta, int32_t* kv_count,
+                        int32_t* kv_index, hipStream_t stream) {
   Geo geo;
   const int st = make_geo(g, &geo);
   if (st != CABF_OK) return st;
-  if (elem_bytes(dtype) == 0) return CABF_EINVAL;
-  if (qp == nullptr || kp == nullptr || kv_count == nullptr || kv_index == nullptr ||
-      workspace == nullptr)
+  if (sta == nullptr || !sta->enabled || sta->dt < 0 || sta->dy < 0 || sta->dx < 0 ||
+      kv_count == nullptr || kv_index == nullptr)
     return CABF_EINVAL;
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
-  if (!(thr >= 0.0f && thr <= 1.0f)) return CABF_EINVAL;
-  if (reinterpret_cast<uintptr_t>(qp) % 16 || reinterpret_cast<uintptr_t>(kp) % 16 ||
-      reinterpret_cast<uintptr_t>(workspace) % 256 || reinterpret_cast<uintptr_t>(kv_count) % 4 ||
-      reinterpret_cast<uintptr_t>(kv_index) % 4 || reinterpret_cast<uintptr_t>(block_prob) % 4)
+  if (reinterpret_cast<uintptr_t>(kv_count) % 4 || reinterpret_cast<uintptr_t>(kv_index) % 4)
     return CABF_EINVAL;
-  bool sta_on = false;
-  int dt = 0, dy = 0, dx = 0;
-  if (sta != nullptr && sta->enabled) {
-    if (sta->dt < 0 || sta->dy < 0 || sta->dx < 0) return CABF_EINVAL;
-    sta_on = true;
-    dt = sta->dt;
-    dy = sta->dy;
-    dx = sta->dx;
-  }
-  if (geo.nb > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
-  if (workspace_bytes < cabf::mask_workspace_layout(geo).total) return CABF_EWORKSPACE;
-  cabf::launch_build_block_mask(geo, dtype == CABF_BF16, qp, kp, scale, thr, sta_on, dt, dy, dx,
-                                kv_count, kv_index, block_prob, workspace, stream);
+  cabf::launch_build_sta_mask(geo, sta->dt, sta->dy, sta->dx, kv_count, kv_index, stream);
   return launched();
 }
 

@@ -21,10 +21,14 @@ struct MaskWorkspace {
 };
 MaskWorkspace mask_workspace_layout(const Geo& g);
 
+// topk > 0 replaces the CDF cut (thr unused) by the topk most probable blocks
 void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void* kp, float scale,
-                             float thr, bool sta_on, int dt, int dy, int dx, int32_t* kv_count,
-                             int32_t* kv_index, float* block_prob, void* workspace,
-                             hipStream_t stream);
+                             float thr, int topk, bool sta_on, int dt, int dy, int dx,
+                             int32_t* kv_count, int32_t* kv_index, float* block_prob,
+                             void* workspace, hipStream_t stream);
+
+void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_count,
+                           int32_t* kv_index, hipStream_t stream);
 
 void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,

@@ -4,8 +4,11 @@
 //                 block (one wave per block; reads Qp/Kp once, HBM-bound).
 //  block_logits   Z = scale * Qb Kb^T per (batch, head), fp32 register-tiled
 //                 GEMM through LDS (nb x nb x head_dim).
-//  select_rows    one wave per block row: softmax of the row, the CDF cut,
-//                 the sliding-tile window and ascending compaction.
+//  select_rows    one wave per block row: softmax of the row, the CDF cut
+//                 (or a fixed-budget top-k), the sliding-tile window and
+//                 ascending compaction.
+//  sta_rows       the sliding-tile window alone (no scores), one row per
+//                 thread.
 //
 // The CDF cut keeps the shortest prefix of the row sorted by probability
 // (descending, ties to the lower index) whose mass reaches 1 - thr. Instead
@@ -16,7 +19,8 @@
 // Every block above p* is kept, and of the blocks equal to p* the lowest
 // indices are kept until the mass reaches 1 - thr. In exact arithmetic this
 // is the same set the sorted prefix gives; only the fp32 summation order
-// differs.
+// differs. The top-k selection uses the same search with the count of blocks
+// at or above u in place of their mass (exact integers).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -193,6 +197,7 @@ struct SelectArgs {
   int nb;
   int64_t rows_total;
   float thr;
+  int topk;             // > 0: keep the topk most probable blocks instead of the CDF cut
   int sta_on, dt, dy, dx;
   int Ty, Tx;
   int32_t* kv_count;
@@ -245,11 +250,43 @@ __global__ __launch_bounds__(256) void select_rows(SelectArgs a) {
     }
   }
 
-  // --- the CDF cut ---------------------------------------------------------
-  bool keep_all = !(a.thr > 0.0f);
+  // --- the cut: ustar = bits of the last kept value, need = how many blocks
+  // equal to it are kept (lowest indices first) ---------------------------
+  bool keep_all = a.topk > 0 ? a.topk >= nb : !(a.thr > 0.0f);
   uint32_t ustar = 0;
   int need = 0;
-  if (!keep_all) {
+  if (!keep_all && a.topk > 0) {
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const int j = r * kWave + lane;
+      if (r < nr && j < nb) {
+        lo = min(lo, __float_as_uint(p[r]));
+        hi = max(hi, __float_as_uint(p[r]));
+      }
+    }
+    lo = uniform(wave_min_u32(lo));
+    hi = uniform(wave_max_u32(hi));
+    auto count_ge = [&](uint32_t u) {
+      int acc = 0;
+#pragma unroll
+      for (int r = 0; r < EPL; ++r) {
+        const int j = r * kWave + lane;
+        acc += __popcll(__ballot(r < nr && j < nb && __float_as_uint(p[r]) >= u));
+      }
+      return acc;   // uniform
+    };
+    // largest u with at least topk blocks at or above it (count_ge(lo) = nb)
+    while (lo < hi) {
+      const uint32_t mid = lo + (hi - lo + 1u) / 2u;
+      if (count_ge(mid) >= a.topk) lo = mid; else hi = mid - 1u;
+      lo = uniform(lo);
+      hi = uniform(hi);
+    }
+    ustar = lo;
+    const int above = ustar == 0xffffffffu ? 0 : count_ge(ustar + 1u);
+    need = uniform(static_cast<uint32_t>(a.topk - above));
+  } else if (!keep_all) {
     const float target = 1.0f - a.thr;
     uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
@@ -347,6 +384,27 @@ __global__ __launch_bounds__(256) void select_rows(SelectArgs a) {
   if (lane == 0) a.kv_count[row] = count;
 }
 
+// Sliding-tile window alone: one thread per block row writes the ascending
+// indices of its clipped box (frames, then patch rows, then patch columns).
+__global__ __launch_bounds__(256) void sta_rows(int64_t rows_total, int nb, int T, int Ty, int Tx,
+                                                int dt, int dy, int dx, int32_t* __restrict__ kv_count,
+                                                int32_t* __restrict__ kv_index) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (row >= rows_total) return;
+  const int i = static_cast<int>(row % nb);
+  const int per_frame = Ty * Tx;
+  const int ti = i / per_frame;
+  const int tyi = (i - ti * per_frame) / Tx;
+  const int txi = i - ti * per_frame - tyi * Tx;
+  int32_t* __restrict__ out = kv_index + row * nb;
+  int count = 0;
+  for (int t = max(ti - dt, 0); t <= min(ti + dt, T - 1); ++t)
+    for (int ty = max(tyi - dy, 0); ty <= min(tyi + dy, Ty - 1); ++ty)
+      for (int tx = max(txi - dx, 0); tx <= min(txi + dx, Tx - 1); ++tx)
+        out[count++] = (t * Ty + ty) * Tx + tx;
+  kv_count[row] = count;
+}
+
 template <int EPL>
 void launch_select(const SelectArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>((a.rows_total + 3) / 4);
@@ -367,10 +425,17 @@ MaskWorkspace mask_workspace_layout(const Geo& g) {
   return w;
 }
 
+void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_count,
+                           int32_t* kv_index, hipStream_t stream) {
+  const int64_t rows = g.BH * g.nb;
+  hipLaunchKernelGGL(sta_rows, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0,
+                     stream, rows, g.nb, g.T, g.Ty, g.Tx, dt, dy, dx, kv_count, kv_index);
+}
+
 void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void* kp, float scale,
-                             float thr, bool sta_on, int dt, int dy, int dx, int32_t* kv_count,
-                             int32_t* kv_index, float* block_prob, void* workspace,
-                             hipStream_t stream) {
+                             float thr, int topk, bool sta_on, int dt, int dy, int dx,
+                             int32_t* kv_count, int32_t* kv_index, float* block_prob,
+                             void* workspace, hipStream_t stream) {
   const MaskWorkspace w = mask_workspace_layout(g);
   char* ws = static_cast<char*>(workspace);
   float* qb = reinterpret_cast<float*>(ws + w.qb_off);
@@ -405,6 +470,7 @@ void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void
   a.nb = g.nb;
   a.rows_total = blocks_total;
   a.thr = thr;
+  a.topk = topk;
   a.sta_on = sta_on ? 1 : 0;
   a.dt = dt;
   a.dy = dy;

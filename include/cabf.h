@@ -132,6 +132,29 @@ int cabf_build_block_mask(const cabf_geom* g, cabf_dtype dtype,
                           float* block_prob, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Fixed-budget variant of cabf_build_block_mask (DynamicRad summary,
+ * "Dual-Mode Strategy", Static-Ratio mode: a fixed ratio of blocks is kept
+ * per row; the page gives no ranking, so the blocks are ranked by the same
+ * pooled block probabilities). Steps 1, 2, 4 and 5 of cabf_build_block_mask;
+ * step 3 keeps the k most probable blocks of the row (ties to the lower
+ * index; k >= nb keeps every block). For a keep ratio r use k = ceil(r * nb).
+ * k >= 1, else CABF_EINVAL. Other arguments, outputs, workspace and limits
+ * as for cabf_build_block_mask. */
+int cabf_build_block_mask_topk(const cabf_geom* g, cabf_dtype dtype,
+                               const void* qp, const void* kp, float scale, int32_t k,
+                               const cabf_sta* sta, int32_t* kv_count, int32_t* kv_index,
+                               float* block_prob, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Pure sliding-tile block lists (NABLA summary, comparison with static
+ * methods: the STA-only configuration), with no content scores: row i keeps
+ * exactly the window of cabf_build_block_mask step 4, ascending.
+ * sta: host pointer, required and enabled, dt, dy, dx >= 0 (else
+ * CABF_EINVAL). kv_count [B, heads, nb] and kv_index [B, heads, nb, nb] int32
+ * (outputs, 4-byte aligned). No workspace; any nb the geometry allows. */
+int cabf_build_sta_mask(const cabf_geom* g, const cabf_sta* sta,
+                        int32_t* kv_count, int32_t* kv_index, hipStream_t stream);
+
 /* Block-sparse attention forward (NABLA summary, Methodology item 2,
  * expansion bullet: the block mask, expanded to token resolution, decides
  * which tiles of attention are computed). For every reordered query row n of

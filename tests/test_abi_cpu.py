@@ -121,6 +121,32 @@ def test_mask_argument_checks():
 
 
 @no_gpu
+def test_topk_and_sta_mask_argument_checks():
+    g = geom()
+    need = L.cabf_mask_workspace_bytes(g)
+    ws = ctypes.c_void_p(0x300000)
+    def topk(k, **kw):
+        a = dict(qp=DUMMY, scale=0.125, wsb=need)
+        a.update(kw)
+        return L.cabf_build_block_mask_topk(g, 0, a["qp"], DUMMY, a["scale"], k, None, DUMMY2,
+                                            DUMMY2, None, ws, a["wsb"], NULL)
+    assert topk(0) == cabf.CABF_EINVAL
+    assert topk(-3) == cabf.CABF_EINVAL
+    assert topk(4, qp=NULL) == cabf.CABF_EINVAL
+    assert topk(4, scale=-1.0) == cabf.CABF_EINVAL
+    assert topk(4, wsb=need - 1) == cabf.CABF_EWORKSPACE
+    on = ctypes.byref(cabf._Sta(1, 1, 1, 1))
+    off = ctypes.byref(cabf._Sta(0, 1, 1, 1))
+    neg = ctypes.byref(cabf._Sta(1, 0, -1, 0))
+    assert L.cabf_build_sta_mask(g, None, DUMMY2, DUMMY2, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_build_sta_mask(g, off, DUMMY2, DUMMY2, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_build_sta_mask(g, neg, DUMMY2, DUMMY2, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_build_sta_mask(g, on, NULL, DUMMY2, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_build_sta_mask(g, on, ctypes.c_void_p(0x200002), DUMMY2, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_build_sta_mask(geom(P=4), on, DUMMY2, DUMMY2, NULL) == cabf.CABF_EUNSUPPORTED
+
+
+@no_gpu
 def test_mask_rejects_rows_longer_than_supported():
     g = geom(T=129, H=64, W=64)      # 129 * 64 blocks > 8192
     assert L.cabf_build_block_mask(g, 0, DUMMY, DUMMY, 0.1, 0.2, None, DUMMY2, DUMMY2, None,

@@ -142,3 +142,37 @@ def test_longest_supported_rows():
     sel = torch.tensor(rows, device=DEV)
     compare_masks(cnt[0, 0, sel], idx[0, 0, sel], info, thr, label=f"nb={og.nb}")
     assert not math.isnan(float(cnt.float().mean()))
+
+
+@pytest.mark.parametrize("ratio,sta", [(0.20, None), (0.10, (1, 1, 1))])
+def test_full_size_topk_static_ratio(ratio, sta):
+    """Static-ratio selection at the Wan-14B 720p shape: k = ceil(ratio * nb)
+    per row, both edge heads' lists against the oracle, and the attention of
+    sampled query blocks on those lists."""
+    w = WORKLOADS["wan14b-720p"]
+    g = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
+    og = oracle.Grid(w.T, w.H, w.W, w.P)
+    k = cabf.topk_for_ratio(g, ratio)
+    say(f"full-size top-k {w.name} ratio {ratio} k {k} sta {sta}")
+    q, kk, v = fourier_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, w.amplitude, seed=3,
+                                 dtype=w.dtype, device=DEV)
+    scale = cabf.default_scale(g)
+    qp, kp, vp = cabf.permute(q, kk, v, g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, 0.0, sta, scale, topk=k)
+    op = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, scale)
+    torch.cuda.synchronize()
+    if sta is None:
+        assert np.all(cnt.cpu().numpy() == k)
+    blocks = sample_blocks(og, 4)
+    for hd in (0, w.heads - 1):
+        qh, kh, vh = (to_np(t[0, hd]) for t in (qp, kp, vp))
+        info = oracle.build_block_mask(qh, kh, og, scale, 0.0, sta, topk=k)
+        compare_masks(cnt[0, hd], idx[0, hd], info, 0.0, label=f"top-k head {hd}")
+        gmask = oracle.lists_to_mask(cnt[0, hd].cpu().numpy(), idx[0, hd].cpu().numpy(), og.nb)
+        same = ~(gmask != info["mask"]).any(-1)
+        use = [b for b in blocks if same[b]]
+        sub = np.zeros_like(info["kv_count"])
+        sub[use] = info["kv_count"][use]
+        ref_o, _ = oracle.bsa_forward(qh, kh, vh, sub, info["kv_index"], og, scale)
+        rows = np.concatenate([np.arange(b * 64, (b + 1) * 64) for b in use])
+        compare_attention(op[0, hd], ref_o, True, rows=rows, label=f"top-k head {hd}")

@@ -133,6 +133,50 @@ def test_block_mask_uniform_rows_keep_lowest_indices(n_blocks_t, thr):
     assert np.all(idx.cpu().numpy()[..., :want] == np.arange(want))
 
 
+TOPK_CASES = [
+    ("tiny-f32-d64", 3, None, None),
+    ("ragged-bf16-d128", 1, None, None),
+    ("ragged-bf16-d128", 17, (1, 1, 1), None),
+    ("ragged-bf16-d128", 10_000, None, None),        # k >= nb keeps every block
+    ("ragged-f32-d128", 9, (0, 1, 2), 1.0),
+    ("wide-bf16-d128", 40, None, 1.0),
+    ("one-block-bf16", 1, None, None),
+    ("one-row-high-bf16", 5, (1, 0, 1), 1.0),
+]
+
+
+@pytest.mark.parametrize("name,k,sta,scale", TOPK_CASES)
+def test_topk_mask_matches_oracle(name, k, sta, scale):
+    """Fixed-budget selection: the k most probable blocks (ties to the lower
+    index) OR the window; rows with a near-tie at the k-th block are exempt."""
+    say(f"topk mask {name} k={k} sta={sta} scale={scale}")
+    g, og, q, k_, v = make(name)
+    s = cabf.default_scale(g) if scale is None else scale
+    qp, kp, vp = cabf.permute(q, k_, v, g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, 0.0, sta, s, topk=k)
+    torch.cuda.synchronize()
+    info = oracle.build_block_mask(to_np(qp), to_np(kp), og, s, 0.0, sta, topk=k)
+    compare_masks(cnt, idx, info, 0.0, label=f"{name} topk={k} sta={sta}")
+    if sta is None:
+        assert np.all(cnt.cpu().numpy() == min(k, og.nb))
+
+
+@pytest.mark.parametrize("grid,win", [((4, 16, 16, 8), (1, 1, 1)), ((5, 24, 40, 8), (1, 1, 2)),
+                                      ((3, 21, 35, 8), (0, 2, 1)), ((7, 1, 40, 8), (2, 0, 0))])
+def test_sta_only_lists_match_oracle(grid, win):
+    T, H, W, P = grid
+    g = cabf.Geom(2, 3, 64, T, H, W, P)
+    og = oracle.Grid(T, H, W, P)
+    cnt, idx = cabf.build_sta_mask(g, win, DEV)
+    torch.cuda.synchronize()
+    want_cnt, want_idx = oracle.sta_only_lists(og, *win)
+    c, ix = cnt.cpu().numpy(), idx.cpu().numpy()
+    for pos in np.ndindex(*c.shape):
+        assert np.array_equal(c[pos], want_cnt[pos[-1]])
+        n = c[pos]
+        assert np.array_equal(ix[pos][:n], want_idx[pos[-1]][:n])
+
+
 ATTN_CASES = [
     ("tiny-f32-d64", 0.2, (1, 1, 1)),
     ("ragged-f32-d128", 0.4, None),
