@@ -38,3 +38,4 @@ from .nabla import (  # noqa: F401
     masked_attention_bruteforce,
     layer,
 )
+from . import svg2  # noqa: F401,E402

@@ -16,6 +16,8 @@ from __future__ import annotations
 
 import math
 
+import numpy as np
+
 import torch
 
 
@@ -61,13 +63,14 @@ def fourier_video_qkv(T: int, H: int, W: int, heads: int, d: int, amplitude: flo
 
 
 def gaussian_mixture_qk(n: int, heads: int, d: int, components: int = 64, spread: float = 0.15,
-                        seed: int = 0, dtype: str = "bf16", device: str | torch.device = "cpu"):
+                        amplitude: float = 1.0, seed: int = 0, dtype: str = "bf16",
+                        device: str | torch.device = "cpu"):
     """Q and K drawn from a seeded Gaussian mixture in R^d (recoverable clusters).
 
-    Per head: ``components`` unit-norm centres c_m; every token picks a centre
-    uniformly and adds N(0, spread^2 / d) per coordinate. Q and K share the
-    centres of their head but draw memberships and noise independently.
-    Returns (q, k) [1, heads, n, d].
+    Per head: ``components`` centres c_m of norm ``amplitude`` (random
+    directions); every token picks a centre uniformly and adds N(0, (amplitude
+    * spread)^2 / d) per coordinate. Q and K share the centres of their head
+    but draw memberships and noise independently. Returns (q, k) [1, heads, n, d].
     """
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -78,9 +81,17 @@ def gaussian_mixture_qk(n: int, heads: int, d: int, components: int = 64, spread
     k = torch.empty(1, heads, n, d, dtype=out_dtype, device=dev)
     for h in range(heads):
         c = torch.randn(components, d, generator=gen, dtype=f64, device=dev)
-        c = c / c.norm(dim=1, keepdim=True)
+        c = amplitude * c / c.norm(dim=1, keepdim=True)
         for dst in (q, k):
             member = torch.randint(0, components, (n,), generator=gen, device=dev)
-            noise = torch.randn(n, d, generator=gen, dtype=f64, device=dev) * (spread / math.sqrt(d))
+            noise = torch.randn(n, d, generator=gen, dtype=f64, device=dev) * (
+                amplitude * spread / math.sqrt(d))
             dst[0, h] = (c[member] + noise).to(torch.float32).to(out_dtype)
     return q, k
+
+
+def kmeans_init_indices(n: int, clusters: int, heads: int, seed: int = 0) -> np.ndarray:
+    """Seeded k-means initialisation draw: ``clusters`` distinct token indices
+    per head, int32 [heads, clusters] (numpy PCG64)."""
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.choice(n, clusters, replace=False) for _ in range(heads)]).astype(np.int32)

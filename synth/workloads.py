@@ -40,3 +40,32 @@ WORKLOADS = {
                                   sparsity=(0.85,),
                                   notes="61 x 48x84 padded to 48x88, N=257,664, 4,026 blocks"),
 }
+
+
+@dataclass(frozen=True)
+class SemanticWorkload:
+    """Semantic-permutation (k-means + top-p) variant: n tokens per head, Q and
+    K from a Gaussian mixture (``synth.gaussian_mixture_qk``), V standard
+    normal, seeded k-means initial indices (``synth.kmeans_init_indices``)."""
+    name: str
+    heads: int
+    head_dim: int
+    n: int
+    cq: int               # query clusters
+    ck: int               # key clusters
+    iters: int            # Lloyd iterations
+    top_p: float
+    components: int
+    spread: float
+    amplitude: float
+    notes: str = ""
+
+
+SEMANTIC_WORKLOADS = {
+    "svg2-tiny": SemanticWorkload("svg2-tiny", 2, 128, 3000, 12, 40, 5, 0.9, 10, 0.15, 8.5,
+                                  notes="oracle finishes in seconds"),
+    "svg2-wan14b-720p": SemanticWorkload(
+        "svg2-wan14b-720p", 40, 128, 21 * 45 * 80, 100, 500, 10, 0.9, 64, 0.15, 8.5,
+        notes="Wan-14B 720p token count (21 x 45x80 = 75,600), 100 query / 500 key clusters, "
+              "10 Lloyd iterations, top-p 0.9; amplitude 8.5 puts the kept density near 16%"),
+}
