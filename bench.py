@@ -44,6 +44,8 @@ def parse():
                     help="walk every block list from its first entry (bit-reproducible attention)")
     ap.add_argument("--variants", type=int, default=1,
                     help="also time the 90%% and window variants (0 to skip)")
+    ap.add_argument("--semantic", type=int, default=1,
+                    help="also time the semantic-permutation (k-means + top-p) variant (0 to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle CPU-baseline sample (0 to skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -141,6 +143,99 @@ def profiled_traffic(workload: str):
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def measure_semantic(cabf, steps: int, warmup: int, seed: int):
+    """The semantic-permutation layer at the Wan-14B 720p token count: every
+    stage timed with HIP events on the current stream. The attention's work is
+    4 * head_dim flops per kept (query, key) token pair."""
+    import torch
+    from synth import SEMANTIC_WORKLOADS, gaussian_mixture_qk, kmeans_init_indices
+
+    w = SEMANTIC_WORKLOADS["svg2-wan14b-720p"]
+    dev = torch.device("cuda:0")
+    n, h, d = w.n, w.heads, w.head_dim
+    q, k = gaussian_mixture_qk(n, h, d, components=w.components, spread=w.spread,
+                               amplitude=w.amplitude, seed=seed, dtype="bf16", device=dev)
+    v = torch.randn(1, h, n, d, generator=torch.Generator(device=dev).manual_seed(seed + 1),
+                    device=dev).to(torch.bfloat16)
+    init_q = torch.from_numpy(kmeans_init_indices(n, w.cq, h, seed + 2)[None]).to(dev)
+    init_k = torch.from_numpy(kmeans_init_indices(n, w.ck, h, seed + 3)[None]).to(dev)
+    seq = cabf.Seq(1, h, d, n)
+    rows = n + cabf.SEQ_PAD_ROWS
+    scale = 1.0 / math.sqrt(d)
+    B = 1
+    km = {}
+    for name, C in (("q", w.cq), ("k", w.ck)):
+        km[name] = dict(centroids=torch.empty(B, h, C, d, dtype=torch.float32, device=dev),
+                        counts=torch.empty(B, h, C, dtype=torch.int32, device=dev),
+                        labels=torch.empty(B, h, n, dtype=torch.int32, device=dev),
+                        perm=torch.empty(B, h, n, dtype=torch.int32, device=dev),
+                        offsets=torch.empty(B, h, C + 1, dtype=torch.int32, device=dev),
+                        ws=cabf._ws(cabf._lib.cabf_kmeans_workspace_bytes(
+                            cabf.ctypes.byref(seq.c()), C), dev))
+    qp, kp, vp, op = (torch.empty(B, h, rows, d, dtype=torch.bfloat16, device=dev) for _ in range(4))
+    o = torch.empty_like(q)
+    cnt = torch.empty(B, h, w.cq, dtype=torch.int32, device=dev)
+    idx = torch.empty(B, h, w.cq, w.ck, dtype=torch.int32, device=dev)
+    ws_sel = cabf._ws(cabf._lib.cabf_cluster_select_workspace_bytes(
+        cabf.ctypes.byref(seq.c()), w.cq, w.ck), dev)
+    ws_att = cabf._ws(cabf._lib.cabf_cluster_attention_workspace_bytes(
+        cabf.ctypes.byref(seq.c()), w.cq, w.ck), dev)
+    names = ("kmeans_q", "kmeans_k", "gather", "select", "attention", "scatter")
+
+    def step(ev):
+        ev[0].record()
+        for i, (name, x, C, init) in enumerate((("q", q, w.cq, init_q), ("k", k, w.ck, init_k))):
+            m = km[name]
+            cabf.cabf_kmeans(seq, x, C, init, w.iters, m["centroids"], m["counts"], m["labels"],
+                             m["perm"], m["offsets"], m["ws"])
+            ev[1 + i].record()
+        cabf.cabf_gather_rows(seq, q, km["q"]["perm"], qp, rows)
+        cabf.cabf_gather_rows(seq, k, km["k"]["perm"], kp, rows)
+        cabf.cabf_gather_rows(seq, v, km["k"]["perm"], vp, rows)
+        ev[3].record()
+        cabf.cabf_cluster_select(seq, w.cq, w.ck, km["q"]["centroids"], km["k"]["centroids"],
+                                 km["k"]["counts"], scale, w.top_p, cnt, idx, None, ws_sel)
+        ev[4].record()
+        cabf.cabf_cluster_attention(seq, w.cq, w.ck, qp, kp, vp, km["q"]["offsets"],
+                                    km["k"]["offsets"], cnt, idx, scale, op, None, ws_att)
+        ev[5].record()
+        cabf.cabf_scatter_rows(seq, op, rows, km["q"]["perm"], o)
+        ev[6].record()
+
+    times = {nm: [] for nm in names}
+    for it in range(warmup + steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        step(ev)
+        torch.cuda.synchronize()
+        if it >= warmup:
+            for i, nm in enumerate(names):
+                times[nm].append(ev[i].elapsed_time(ev[i + 1]))
+    mean = {nm: statistics.fmean(t) for nm, t in times.items()}
+    # kept (query, key) token pairs of the selection, from the cluster sizes
+    qs = torch.diff(km["q"]["offsets"].long(), dim=-1)            # [1, h, cq]
+    ks = torch.diff(km["k"]["offsets"].long(), dim=-1)            # [1, h, ck]
+    # entries past kv_count are undefined: replace them by 0 before indexing
+    valid = torch.arange(w.ck, device=dev).view(1, 1, 1, -1) < cnt.long().unsqueeze(-1)
+    safe = torch.where(valid, idx.long(), torch.zeros_like(idx, dtype=torch.long)).clamp(0, w.ck - 1)
+    sizes = torch.gather(ks.unsqueeze(2).expand(-1, -1, w.cq, -1), 3, safe)
+    kept_keys = (sizes * valid).sum(-1)                            # [1, h, cq]
+    pairs = int((kept_keys * qs).sum().item())
+    flops = 4.0 * d * pairs
+    total = sum(mean.values())
+    return {
+        "workload": f"{w.name}: 1x{h} heads, head_dim {d}, n={n} tokens, {w.cq} query / {w.ck} "
+                    f"key clusters, {w.iters} Lloyd iterations, top-p {w.top_p}",
+        "data": f"Gaussian mixture Q/K ({w.components} components, amplitude {w.amplitude}), "
+                f"normal V, seeded",
+        "density": pairs / float(h * n * n),
+        "stage_ms": mean,
+        "ms_per_layer": total,
+        "attention_tflops": flops / (mean["attention"] * 1e-3) / 1e12,
+        "layer_tflops": flops / (total * 1e-3) / 1e12,
+        "steps": steps,
+    }
 
 
 def cpu_baseline(q, k, v, w, thr, sta, budget_s):
@@ -324,6 +419,8 @@ def main():
                              attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
                              step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
         line["variants"] = var
+    if args.semantic:
+        line["semantic_variant"] = measure_semantic(cabf, max(3, args.steps // 4), 2, args.seed)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_run["thr"], sta, args.cpu_seconds)
     print(json.dumps(line), flush=True)

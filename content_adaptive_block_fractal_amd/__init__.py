@@ -27,7 +27,12 @@ CABF_BF16, CABF_F32 = 0, 1
 
 EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_unpermute", "cabf_mask_workspace_bytes",
             "cabf_build_block_mask", "cabf_build_block_mask_topk", "cabf_build_sta_mask",
-            "cabf_bsa_forward", "cabf_status_string")
+            "cabf_bsa_forward", "cabf_kmeans_workspace_bytes", "cabf_kmeans", "cabf_gather_rows",
+            "cabf_scatter_rows", "cabf_cluster_select_workspace_bytes", "cabf_cluster_select",
+            "cabf_cluster_attention_workspace_bytes", "cabf_cluster_attention",
+            "cabf_status_string")
+
+SEQ_PAD_ROWS = 64      # extra zero rows of permuted tensors for cabf_cluster_attention
 
 
 class CabfError(RuntimeError):
@@ -40,6 +45,11 @@ class _Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("P", ctypes.c_int32)]
+
+
+class _Seq(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n", ctypes.c_int32)]
 
 
 class _Sta(ctypes.Structure):
@@ -56,6 +66,7 @@ def _load():
     P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
     G = ctypes.POINTER(_Geom)
+    Q = ctypes.POINTER(_Seq)
     sig = {
         "cabf_geom_sizes": (ctypes.c_int, [G, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                            ctypes.POINTER(I32), ctypes.POINTER(I32),
@@ -70,6 +81,15 @@ def _load():
         "cabf_build_sta_mask": (ctypes.c_int, [G, ctypes.POINTER(_Sta), P, P, P]),
         "cabf_bsa_forward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, F32, P, P,
                                             ctypes.c_uint, P]),
+        "cabf_kmeans_workspace_bytes": (SZ, [Q, I32]),
+        "cabf_kmeans": (ctypes.c_int, [Q, ctypes.c_int, P, I32, P, I32, P, P, P, P, P, P, SZ, P]),
+        "cabf_gather_rows": (ctypes.c_int, [Q, ctypes.c_int, P, P, P, I32, P]),
+        "cabf_scatter_rows": (ctypes.c_int, [Q, ctypes.c_int, P, I32, P, P, P]),
+        "cabf_cluster_select_workspace_bytes": (SZ, [Q, I32, I32]),
+        "cabf_cluster_select": (ctypes.c_int, [Q, I32, I32, P, P, P, F32, F32, P, P, P, P, SZ, P]),
+        "cabf_cluster_attention_workspace_bytes": (SZ, [Q, I32, I32]),
+        "cabf_cluster_attention": (ctypes.c_int, [Q, ctypes.c_int, I32, I32, P, P, P, P, P, P, P,
+                                                  F32, P, P, P, SZ, P]),
         "cabf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -305,3 +325,146 @@ def layer(q, k, v, geom: Geom, thr: float, sta=None, scale=None):
     kv_count, kv_index = build_block_mask(qp, kp, geom, thr, sta, scale)
     op = bsa_forward(qp, kp, vp, kv_count, kv_index, geom, scale)
     return unpermute(op, geom), (kv_count, kv_index)
+
+
+# --- semantic-permutation variant ----------------------------------------------------
+
+@dataclass(frozen=True)
+class Seq:
+    """Token sequences (cabf_seq): batch x heads sequences of n tokens."""
+    batch: int
+    heads: int
+    head_dim: int
+    n: int
+
+    def c(self) -> _Seq:
+        return _Seq(self.batch, self.heads, self.head_dim, self.n)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _ws_ptr(ws: torch.Tensor):
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_cuda:
+        raise ValueError("workspace must be a 1-D uint8 device tensor")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel()
+
+
+def cabf_kmeans(seq: Seq, x, clusters: int, init, iters: int, centroids, counts, labels, perm,
+                offsets, workspace):
+    """k-means of [B, h, n, d] bf16 token features and the cluster permutation."""
+    lead = (seq.batch, seq.heads)
+    ptr, nbytes = _ws_ptr(workspace)
+    st = _lib.cabf_kmeans(
+        ctypes.byref(seq.c()), _dtype_code(x), _dev(x, lead + (seq.n, seq.head_dim), None, "x"),
+        int(clusters), _dev(init, lead + (clusters,), torch.int32, "init"), int(iters),
+        _dev(centroids, lead + (clusters, seq.head_dim), torch.float32, "centroids"),
+        _dev(counts, lead + (clusters,), torch.int32, "counts"),
+        _dev(labels, lead + (seq.n,), torch.int32, "labels"),
+        _dev(perm, lead + (seq.n,), torch.int32, "perm"),
+        _dev(offsets, lead + (clusters + 1,), torch.int32, "offsets"), ptr, nbytes, _stream(x))
+    _check("cabf_kmeans", st)
+
+
+def cabf_gather_rows(seq: Seq, x, perm, xp, rows_out: int):
+    lead = (seq.batch, seq.heads)
+    st = _lib.cabf_gather_rows(ctypes.byref(seq.c()), _dtype_code(x),
+                               _dev(x, lead + (seq.n, seq.head_dim), None, "x"),
+                               _dev(perm, lead + (seq.n,), torch.int32, "perm"),
+                               _dev(xp, lead + (rows_out, seq.head_dim), x.dtype, "xp"),
+                               int(rows_out), _stream(x))
+    _check("cabf_gather_rows", st)
+
+
+def cabf_scatter_rows(seq: Seq, xp, rows_in: int, perm, x):
+    lead = (seq.batch, seq.heads)
+    st = _lib.cabf_scatter_rows(ctypes.byref(seq.c()), _dtype_code(xp),
+                                _dev(xp, lead + (rows_in, seq.head_dim), None, "xp"), int(rows_in),
+                                _dev(perm, lead + (seq.n,), torch.int32, "perm"),
+                                _dev(x, lead + (seq.n, seq.head_dim), xp.dtype, "x"), _stream(xp))
+    _check("cabf_scatter_rows", st)
+
+
+def cabf_cluster_select(seq: Seq, cq: int, ck: int, q_centroids, k_centroids, k_counts,
+                        scale: float, top_p: float, kv_count, kv_index, probs, workspace):
+    lead = (seq.batch, seq.heads)
+    ptr, nbytes = _ws_ptr(workspace)
+    pr = None if probs is None else _dev(probs, lead + (cq, ck), torch.float32, "probs")
+    st = _lib.cabf_cluster_select(
+        ctypes.byref(seq.c()), int(cq), int(ck),
+        _dev(q_centroids, lead + (cq, seq.head_dim), torch.float32, "q_centroids"),
+        _dev(k_centroids, lead + (ck, seq.head_dim), torch.float32, "k_centroids"),
+        _dev(k_counts, lead + (ck,), torch.int32, "k_counts"), float(scale), float(top_p),
+        _dev(kv_count, lead + (cq,), torch.int32, "kv_count"),
+        _dev(kv_index, lead + (cq, ck), torch.int32, "kv_index"), pr, ptr, nbytes,
+        _stream(kv_count))
+    _check("cabf_cluster_select", st)
+
+
+def cabf_cluster_attention(seq: Seq, cq: int, ck: int, qp, kp, vp, q_offsets, k_offsets, kv_count,
+                           kv_index, scale: float, op, lse, workspace):
+    lead = (seq.batch, seq.heads)
+    rows = seq.n + SEQ_PAD_ROWS
+    ptr, nbytes = _ws_ptr(workspace)
+    shape = lead + (rows, seq.head_dim)
+    lp = None if lse is None else _dev(lse, lead + (rows,), torch.float32, "lse")
+    st = _lib.cabf_cluster_attention(
+        ctypes.byref(seq.c()), _dtype_code(qp), int(cq), int(ck), _dev(qp, shape, None, "qp"),
+        _dev(kp, shape, qp.dtype, "kp"), _dev(vp, shape, qp.dtype, "vp"),
+        _dev(q_offsets, lead + (cq + 1,), torch.int32, "q_offsets"),
+        _dev(k_offsets, lead + (ck + 1,), torch.int32, "k_offsets"),
+        _dev(kv_count, lead + (cq,), torch.int32, "kv_count"),
+        _dev(kv_index, lead + (cq, ck), torch.int32, "kv_index"), float(scale),
+        _dev(op, shape, qp.dtype, "op"), lp, ptr, nbytes, _stream(qp))
+    _check("cabf_cluster_attention", st)
+
+
+def kmeans(x, clusters: int, init, iters: int):
+    """Returns dict(centroids, counts, labels, perm, offsets) for [B, h, n, d] bf16 x."""
+    B, h, n, d = x.shape
+    seq = Seq(B, h, d, n)
+    dev = x.device
+    out = dict(centroids=torch.empty(B, h, clusters, d, dtype=torch.float32, device=dev),
+               counts=torch.empty(B, h, clusters, dtype=torch.int32, device=dev),
+               labels=torch.empty(B, h, n, dtype=torch.int32, device=dev),
+               perm=torch.empty(B, h, n, dtype=torch.int32, device=dev),
+               offsets=torch.empty(B, h, clusters + 1, dtype=torch.int32, device=dev))
+    ws = _ws(_lib.cabf_kmeans_workspace_bytes(ctypes.byref(seq.c()), int(clusters)), dev)
+    cabf_kmeans(seq, x, clusters, init, iters, out["centroids"], out["counts"], out["labels"],
+                out["perm"], out["offsets"], ws)
+    return out
+
+
+def svg_layer(q, k, v, cq: int, ck: int, init_q, init_k, iters: int, top_p: float, scale=None,
+              return_info=False):
+    """One attention layer of the semantic-permutation variant, raster order in
+    and out: k-means of Q and K, permutation, centroid top-p, cluster attention,
+    inverse permutation. q, k, v: [B, h, n, d] bf16."""
+    B, h, n, d = q.shape
+    seq = Seq(B, h, d, n)
+    dev = q.device
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    kq = kmeans(q, cq, init_q, iters)
+    kk = kmeans(k, ck, init_k, iters)
+    rows = n + SEQ_PAD_ROWS
+    qp, kp, vp, op = (torch.empty(B, h, rows, d, dtype=q.dtype, device=dev) for _ in range(4))
+    cabf_gather_rows(seq, q, kq["perm"], qp, rows)
+    cabf_gather_rows(seq, k, kk["perm"], kp, rows)
+    cabf_gather_rows(seq, v, kk["perm"], vp, rows)
+    kv_count = torch.empty(B, h, cq, dtype=torch.int32, device=dev)
+    kv_index = torch.empty(B, h, cq, ck, dtype=torch.int32, device=dev)
+    ws = _ws(_lib.cabf_cluster_select_workspace_bytes(ctypes.byref(seq.c()), int(cq), int(ck)), dev)
+    cabf_cluster_select(seq, cq, ck, kq["centroids"], kk["centroids"], kk["counts"], scale, top_p,
+                        kv_count, kv_index, None, ws)
+    ws = _ws(_lib.cabf_cluster_attention_workspace_bytes(ctypes.byref(seq.c()), int(cq), int(ck)),
+             dev)
+    lse = torch.empty(B, h, rows, dtype=torch.float32, device=dev)
+    cabf_cluster_attention(seq, cq, ck, qp, kp, vp, kq["offsets"], kk["offsets"], kv_count,
+                           kv_index, scale, op, lse, ws)
+    o = torch.empty_like(q)
+    cabf_scatter_rows(seq, op, rows, kq["perm"], o)
+    if return_info:
+        return o, dict(kq=kq, kk=kk, kv_count=kv_count, kv_index=kv_index, qp=qp, kp=kp, vp=vp,
+                       op=op, lse=lse)
+    return o

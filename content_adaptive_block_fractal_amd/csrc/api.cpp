@@ -9,6 +9,7 @@
 #include "cabf.h"
 #include "geometry.hpp"
 #include "launch.hpp"
+#include "svg.hpp"
 
 namespace {
 
@@ -90,6 +91,20 @@ int build_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void*
                                 dx, kv_count, kv_index, block_prob, workspace, stream);
   return launched();
 }
+
+// cabf_seq -> (BH, n, D); CABF_OK or the status to return
+int check_seq(const cabf_seq* s, int64_t* BH) {
+  if (s == nullptr) return CABF_EINVAL;
+  if (s->batch < 1 || s->heads < 1 || s->n < 1 || s->head_dim < 1) return CABF_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return CABF_EUNSUPPORTED;
+  if (s->n >= (1 << 24)) return CABF_EUNSUPPORTED;
+  const int64_t bh = static_cast<int64_t>(s->batch) * s->heads;
+  if (bh * s->n >= (int64_t{1} << 31)) return CABF_EUNSUPPORTED;
+  *BH = bh;
+  return CABF_OK;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; }
 
 }  // namespace
 
@@ -200,6 +215,133 @@ int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const
     return CABF_EINVAL;
   cabf::launch_bsa_forward(geo, dtype == CABF_BF16, qp, kp, vp, kv_count, kv_index, scale, op,
                            lse, (flags & CABF_BSA_DETERMINISTIC) == 0, stream);
+  return launched();
+}
+
+size_t cabf_kmeans_workspace_bytes(const cabf_seq* s, int32_t clusters) {
+  int64_t BH = 0;
+  if (check_seq(s, &BH) != CABF_OK || clusters < 1 || clusters > s->n || clusters > cabf::kMaxBlocks)
+    return 0;
+  return cabf::kmeans_workspace_layout(BH, s->n, clusters, s->head_dim).total;
+}
+
+int cabf_kmeans(const cabf_seq* s, cabf_dtype dtype, const void* x, int32_t clusters,
+                const int32_t* init, int32_t iters, float* centroids, int32_t* counts,
+                int32_t* labels, int32_t* perm, int32_t* offsets, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  int64_t BH = 0;
+  const int st = check_seq(s, &BH);
+  if (st != CABF_OK) return st;
+  if (elem_bytes(dtype) == 0) return CABF_EINVAL;
+  if (dtype != CABF_BF16) return CABF_EUNSUPPORTED;
+  if (x == nullptr || init == nullptr || centroids == nullptr || counts == nullptr ||
+      labels == nullptr || perm == nullptr || offsets == nullptr || workspace == nullptr)
+    return CABF_EINVAL;
+  if (clusters < 1 || clusters > s->n || iters < 0) return CABF_EINVAL;
+  if (clusters > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
+  if (misaligned(x, 16) || misaligned(init, 4) || misaligned(centroids, 16) ||
+      misaligned(counts, 4) || misaligned(labels, 4) || misaligned(perm, 4) ||
+      misaligned(offsets, 4) || misaligned(workspace, 256))
+    return CABF_EINVAL;
+  if (workspace_bytes < cabf::kmeans_workspace_layout(BH, s->n, clusters, s->head_dim).total)
+    return CABF_EWORKSPACE;
+  if (cabf::launch_kmeans(BH, s->n, s->head_dim, clusters, iters, x, init, centroids, counts,
+                          labels, perm, offsets, workspace, stream) != 0)
+    return CABF_EHIP;
+  return launched();
+}
+
+int cabf_gather_rows(const cabf_seq* s, cabf_dtype dtype, const void* x, const int32_t* perm,
+                     void* xp, int32_t rows_out, hipStream_t stream) {
+  int64_t BH = 0;
+  const int st = check_seq(s, &BH);
+  if (st != CABF_OK) return st;
+  const int eb = elem_bytes(dtype);
+  if (eb == 0 || x == nullptr || perm == nullptr || xp == nullptr || rows_out < s->n)
+    return CABF_EINVAL;
+  if (BH * rows_out >= (int64_t{1} << 31)) return CABF_EUNSUPPORTED;
+  if (misaligned(x, 16) || misaligned(xp, 16) || misaligned(perm, 4)) return CABF_EINVAL;
+  cabf::launch_gather_rows(BH, s->n, rows_out, s->head_dim * eb, x, perm, xp, stream);
+  return launched();
+}
+
+int cabf_scatter_rows(const cabf_seq* s, cabf_dtype dtype, const void* xp, int32_t rows_in,
+                      const int32_t* perm, void* x, hipStream_t stream) {
+  int64_t BH = 0;
+  const int st = check_seq(s, &BH);
+  if (st != CABF_OK) return st;
+  const int eb = elem_bytes(dtype);
+  if (eb == 0 || x == nullptr || perm == nullptr || xp == nullptr || rows_in < s->n)
+    return CABF_EINVAL;
+  if (BH * rows_in >= (int64_t{1} << 31)) return CABF_EUNSUPPORTED;
+  if (misaligned(x, 16) || misaligned(xp, 16) || misaligned(perm, 4)) return CABF_EINVAL;
+  cabf::launch_scatter_rows(BH, s->n, rows_in, s->head_dim * eb, xp, perm, x, stream);
+  return launched();
+}
+
+size_t cabf_cluster_select_workspace_bytes(const cabf_seq* s, int32_t cq, int32_t ck) {
+  int64_t BH = 0;
+  if (check_seq(s, &BH) != CABF_OK || cq < 1 || ck < 1 || ck > cabf::kMaxBlocks) return 0;
+  return cabf::cluster_select_workspace_layout(BH, cq, ck).total;
+}
+
+int cabf_cluster_select(const cabf_seq* s, int32_t cq, int32_t ck, const float* q_centroids,
+                        const float* k_centroids, const int32_t* k_counts, float scale,
+                        float top_p, int32_t* kv_count, int32_t* kv_index, float* probs,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int64_t BH = 0;
+  const int st = check_seq(s, &BH);
+  if (st != CABF_OK) return st;
+  if (q_centroids == nullptr || k_centroids == nullptr || k_counts == nullptr ||
+      kv_count == nullptr || kv_index == nullptr || workspace == nullptr)
+    return CABF_EINVAL;
+  if (cq < 1 || ck < 1) return CABF_EINVAL;
+  if (ck > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return CABF_EINVAL;
+  if (misaligned(q_centroids, 4) || misaligned(k_centroids, 4) || misaligned(k_counts, 4) ||
+      misaligned(kv_count, 4) || misaligned(kv_index, 4) || misaligned(probs, 4) ||
+      misaligned(workspace, 256))
+    return CABF_EINVAL;
+  if (workspace_bytes < cabf::cluster_select_workspace_layout(BH, cq, ck).total)
+    return CABF_EWORKSPACE;
+  cabf::launch_cluster_select(BH, cq, ck, s->head_dim, q_centroids, k_centroids, k_counts, scale,
+                              top_p, kv_count, kv_index, probs, workspace, stream);
+  return launched();
+}
+
+size_t cabf_cluster_attention_workspace_bytes(const cabf_seq* s, int32_t cq, int32_t ck) {
+  int64_t BH = 0;
+  if (check_seq(s, &BH) != CABF_OK || cq < 1 || ck < 1 || cq > s->n || ck > s->n) return 0;
+  return cabf::cluster_attention_workspace_layout(BH, s->n, cq, ck).total;
+}
+
+int cabf_cluster_attention(const cabf_seq* s, cabf_dtype dtype, int32_t cq, int32_t ck,
+                           const void* qp, const void* kp, const void* vp,
+                           const int32_t* q_offsets, const int32_t* k_offsets,
+                           const int32_t* kv_count, const int32_t* kv_index, float scale,
+                           void* op, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  int64_t BH = 0;
+  const int st = check_seq(s, &BH);
+  if (st != CABF_OK) return st;
+  if (elem_bytes(dtype) == 0) return CABF_EINVAL;
+  if (dtype != CABF_BF16) return CABF_EUNSUPPORTED;
+  if (qp == nullptr || kp == nullptr || vp == nullptr || q_offsets == nullptr ||
+      k_offsets == nullptr || kv_count == nullptr || kv_index == nullptr || op == nullptr ||
+      workspace == nullptr)
+    return CABF_EINVAL;
+  if (cq < 1 || ck < 1 || cq > s->n || ck > s->n) return CABF_EINVAL;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
+  if (BH * (s->n + cabf::kBlock) >= (int64_t{1} << 31)) return CABF_EUNSUPPORTED;
+  if (misaligned(qp, 16) || misaligned(kp, 16) || misaligned(vp, 16) || misaligned(op, 16) ||
+      misaligned(q_offsets, 4) || misaligned(k_offsets, 4) || misaligned(kv_count, 4) ||
+      misaligned(kv_index, 4) || misaligned(lse, 4) || misaligned(workspace, 256))
+    return CABF_EINVAL;
+  if (workspace_bytes < cabf::cluster_attention_workspace_layout(BH, s->n, cq, ck).total)
+    return CABF_EWORKSPACE;
+  cabf::launch_cluster_attention(BH, s->n, s->head_dim, cq, ck, qp, kp, vp, q_offsets, k_offsets,
+                                 kv_count, kv_index, scale, op, lse, workspace, stream);
   return launched();
 }
 

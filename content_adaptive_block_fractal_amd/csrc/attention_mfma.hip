@@ -150,8 +150,8 @@ __device__ __forceinline__ void issue_tile_load(const uint16_t* __restrict__ til
   }
 }
 
-// List entry t -> element offset of its K/V block and whether it is a real
-// block; entries outside [0, nb) load block 0 and are masked out entirely.
+// A list entry decoded: element offset of its 64 K/V rows in the head, and
+// what the layout needs to mask it (block index, or number of valid keys).
 struct TileRef {
   int64_t off;
   int jb;
@@ -170,8 +170,95 @@ __device__ inline uint32_t real_key_bits(const BlockExtent& ext, int wk, int h) 
   return bits;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t n_qblocks) {
+// What a workgroup computes: 64 consecutive rows of Q and O starting at the
+// global row qrow0 (over all batch-heads), of which the first `rows` are
+// stored, against the cnt key tiles of `list`, in head bh's K and V.
+struct WorkItem {
+  int64_t bh;
+  int64_t qrow0;
+  int rows;
+  int cnt;
+  const int32_t* list;
+};
+
+// Kept 64-token blocks of the reordered grid (NABLA path): one work item per
+// query block, list entries are key block indices, pad keys of partially
+// padded patches are masked.
+struct BlockListLayout {
+  static constexpr bool kPhased = true;   // clock-phased start (AttnArgs::sweep_ticks)
+  __device__ bool work(const AttnArgs& a, int64_t item, WorkItem& w) const {
+    w.bh = item / a.nb;
+    w.qrow0 = item * kBlock;
+    w.rows = kBlock;
+    w.cnt = min(max(a.kv_count[item], 0), a.nb);
+    w.list = a.kv_index + item * a.nb;
+    return true;
+  }
+  // entries outside [0, nb) load block 0 and are masked out entirely
+  template <int D>
+  __device__ TileRef decode(const AttnArgs& a, int32_t e) const {
+    TileRef r;
+    r.jb = e;
+    r.real = static_cast<unsigned>(e) < static_cast<unsigned>(a.nb);
+    r.off = static_cast<int64_t>(r.real ? e : 0) * kBlock * D;
+    return r;
+  }
+  // false when every key of the tile is real; else the lane's real-key bits
+  __device__ bool partial(const AttnArgs& a, const TileRef& t, int wk, int h, uint32_t& bits) const {
+    const BlockExtent ext = t.real ? block_extent(t.jb, a) : BlockExtent{0, 0};
+    if (ext.full()) return false;
+    bits = real_key_bits(ext, wk, h);
+    return true;
+  }
+};
+
+// Variable-size clusters (semantic-permutation path, Sparse VideoGen2
+// summary, Methodology C: contiguous query tokens, the key tokens of the
+// selected clusters): one work item per 64-row tile of a query cluster; list
+// entries are key chunks (first key row << 6) | (keys - 1), 1 to 64 keys.
+struct ClusterLayout {
+  static constexpr bool kPhased = false;
+  const int32_t* tiles;         // [BH, max_tiles, 2]: query cluster (or -1), first row
+  int max_tiles;
+  const int32_t* q_off;         // [BH, cq + 1]
+  int cq;
+  const int32_t* chunk_count;   // [BH, cq]
+  const int32_t* chunks;        // [BH, cq, cap]
+  int cap;
+  __device__ bool work(const AttnArgs& a, int64_t item, WorkItem& w) const {
+    const int qa = tiles[item * 2];
+    if (qa < 0) return false;
+    const int row0 = tiles[item * 2 + 1];
+    w.bh = item / max_tiles;
+    w.qrow0 = w.bh * a.N + row0;
+    w.rows = min(kBlock, q_off[w.bh * (cq + 1) + qa + 1] - row0);
+    const int64_t qc = w.bh * cq + qa;
+    w.cnt = min(max(chunk_count[qc], 0), cap);
+    w.list = chunks + qc * cap;
+    return true;
+  }
+  template <int D>
+  __device__ TileRef decode(const AttnArgs&, int32_t e) const {
+    TileRef r;
+    r.jb = (e & 63) + 1;          // keys of the chunk
+    r.real = true;
+    r.off = static_cast<int64_t>(e >> 6) * D;
+    return r;
+  }
+  __device__ bool partial(const AttnArgs&, const TileRef& t, int wk, int h, uint32_t& bits) const {
+    if (t.jb == kBlock) return false;
+    bits = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * wk + 8 * (r >> 2) + 4 * h + (r & 3);
+      bits |= key < t.jb ? (1u << r) : 0u;
+    }
+    return true;
+  }
+};
+
+template <int D, class L>
+__global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, int64_t n_items) {
   using S = Stage<D>;
   constexpr int kKS = D / 16;   // MFMA k-steps over d
   constexpr int kDT = D / 32;   // 32-row d subtiles of O^T
@@ -188,14 +275,15 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   const int wk = wave >> 1;     // key half of every tile
   const int li = lane & 31;
   const int h = lane >> 5;
-  const int64_t qblk = xcd_order(blockIdx.x, n_qblocks);
-  const int64_t bh = qblk / a.nb;
+  WorkItem w;
+  if (!lay.work(a, xcd_order(blockIdx.x, n_items), w)) return;   // uniform per workgroup
+  const int64_t bh = w.bh;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.kp) + bh * a.N * D;
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.vp) + bh * a.N * D;
 
   // Q^T fragments: lane holds query row li of this wave's half, d = 16 ks + 8 h .. +7
-  const int64_t qrow = qblk * kBlock + wq * 32 + li;
+  const int64_t qrow = w.qrow0 + wq * 32 + li;
   bf16x8 qf[kKS];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
@@ -212,8 +300,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   float l = 0.0f;        // this lane's part of the row sum
   const float c = a.scale_log2;
 
-  const int cnt = min(max(a.kv_count[qblk], 0), a.nb);
-  const int32_t* __restrict__ list = a.kv_index + qblk * a.nb;
+  const int cnt = w.cnt;
+  const int32_t* __restrict__ list = w.list;
   const int key0 = 32 * wk;     // first key of this wave's half
 
   // Where the pass over the list starts (AttnArgs::sweep_ticks): at the
@@ -227,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   __shared__ int start_shared;
   if (wave == 0) {
     int start = 0;
-    if (a.sweep_ticks != 0 && cnt > 1) {
+    if (L::kPhased && a.sweep_ticks != 0 && cnt > 1) {
       const int32_t* head_counts = a.kv_count + bh * a.nb;
       int total = min(max(head_counts[(lane * a.nb) >> 6], 1), a.nb);
 #pragma unroll
@@ -254,11 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   int batch_cur = 0, batch_nxt = 0;     // entries 64 B .. and 64 (B + 1) .. of the pass
   auto tile = [&](int t) {
     const int p = t < cnt ? t : cnt - 1;
-    TileRef r;
-    r.jb = __builtin_amdgcn_readlane(batch_cur, p & 63);
-    r.real = static_cast<unsigned>(r.jb) < static_cast<unsigned>(a.nb);
-    r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
-    return r;
+    return lay.template decode<D>(a, __builtin_amdgcn_readlane(batch_cur, p & 63));
   };
   // S^T of this wave's 32 keys from the K tile in `kb`
   auto scores = [&](const u32x4* kb) {
@@ -344,9 +428,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
 
       // ---- softmax of tile e ------------------------------------------------
       f32x16& s = s_cur;
-      const BlockExtent ext = t_cur.real ? block_extent(t_cur.jb, a) : BlockExtent{0, 0};
-      if (!ext.full()) {
-        const uint32_t bits = real_key_bits(ext, wk, h);
+      uint32_t bits = 0;
+      if (lay.partial(a, t_cur, wk, h, bits)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
       }
@@ -419,6 +502,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, int64_t 
   const float lt = l * a0 + l1 * a1;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   const float w0 = a0 * inv, w1 = a1 * inv;
+  if (wq * 32 + li >= w.rows) return;      // rows past a query cluster are not stored
   uint16_t* __restrict__ O = static_cast<uint16_t*>(a.op);
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -452,9 +536,25 @@ void launch_bsa_forward_mfma(const AttnArgs& args, int D, bool phased, hipStream
   // head_dim 128); the L2 reuse tolerates an error of a few tens of percent
   a.sweep_ticks = phased ? (D == 64 ? 90u : 150u) : 0u;
   if (D == 64)
-    hipLaunchKernelGGL((bsa_fwd_mfma<64>), dim3(grid), dim3(kThreads), 0, stream, a, n);
+    hipLaunchKernelGGL((bsa_fwd_mfma<64, BlockListLayout>), dim3(grid), dim3(kThreads), 0, stream,
+                       a, BlockListLayout{}, n);
   else
-    hipLaunchKernelGGL((bsa_fwd_mfma<128>), dim3(grid), dim3(kThreads), 0, stream, a, n);
+    hipLaunchKernelGGL((bsa_fwd_mfma<128, BlockListLayout>), dim3(grid), dim3(kThreads), 0, stream,
+                       a, BlockListLayout{}, n);
+}
+
+void launch_cluster_attention_mfma(const AttnArgs& a, int D, const int32_t* tiles, int max_tiles,
+                                   const int32_t* q_off, int cq, const int32_t* chunk_count,
+                                   const int32_t* chunks, int cap, hipStream_t stream) {
+  ClusterLayout lay{tiles, max_tiles, q_off, cq, chunk_count, chunks, cap};
+  const int64_t n = a.BH * max_tiles;
+  const unsigned grid = static_cast<unsigned>(n);
+  if (D == 64)
+    hipLaunchKernelGGL((bsa_fwd_mfma<64, ClusterLayout>), dim3(grid), dim3(kThreads), 0, stream, a,
+                       lay, n);
+  else
+    hipLaunchKernelGGL((bsa_fwd_mfma<128, ClusterLayout>), dim3(grid), dim3(kThreads), 0, stream,
+                       a, lay, n);
 }
 
 }  // namespace cabf

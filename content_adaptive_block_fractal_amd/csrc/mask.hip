@@ -28,6 +28,7 @@
 
 #include "geometry.hpp"
 #include "launch.hpp"
+#include "svg.hpp"
 
 namespace cabf {
 namespace {
@@ -423,6 +424,30 @@ MaskWorkspace mask_workspace_layout(const Geo& g) {
   w.z_off = w.kb_off + align(pooled);
   w.total = w.z_off + align(static_cast<size_t>(g.BH) * g.nb * w.ldz * sizeof(float));
   return w;
+}
+
+void launch_select_matrix(const float* z, int ldz, int64_t rows, int cols, float thr,
+                          int32_t* kv_count, int32_t* kv_index, float* probs, hipStream_t stream) {
+  SelectArgs a{};
+  a.z = z;
+  a.ldz = ldz;
+  a.nb = cols;
+  a.rows_total = rows;
+  a.thr = thr;
+  a.kv_count = kv_count;
+  a.kv_index = kv_index;
+  a.block_prob = probs;
+  a.Ty = 1;
+  a.Tx = 1;
+  const int slots = (cols + kWave - 1) / kWave;
+  if (slots <= 1) launch_select<1>(a, stream);
+  else if (slots <= 2) launch_select<2>(a, stream);
+  else if (slots <= 4) launch_select<4>(a, stream);
+  else if (slots <= 8) launch_select<8>(a, stream);
+  else if (slots <= 16) launch_select<16>(a, stream);
+  else if (slots <= 32) launch_select<32>(a, stream);
+  else if (slots <= 64) launch_select<64>(a, stream);
+  else launch_select<128>(a, stream);
 }
 
 void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_count,

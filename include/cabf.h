@@ -181,6 +181,101 @@ int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype,
                      const int32_t* kv_count, const int32_t* kv_index, float scale,
                      void* op, float* lse, unsigned flags, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Semantic-permutation variant (Sparse VideoGen2 summary, Methodology A-C):
+ * k-means clustering of Q and K, cluster-contiguous permutation, centroid
+ * scores with top-p selection, attention over the selected cluster pairs.
+ * ------------------------------------------------------------------------ */
+
+/* batch x heads sequences of n tokens: tensors [batch, heads, n, head_dim]
+ * row-major. head_dim 64 or 128; 1 <= n < 2^24 and batch*heads*n < 2^31. */
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t n;
+} cabf_seq;
+
+/* Bytes of workspace cabf_kmeans needs for `clusters` clusters (0 if the
+ * sizes are unsupported). */
+size_t cabf_kmeans_workspace_bytes(const cabf_seq* s, int32_t clusters);
+
+/* k-means of every (batch, head)'s tokens and the cluster permutation
+ * (Methodology A). Lloyd's algorithm on the rows of x with squared Euclidean
+ * distance: `iters` rounds of (assign every token to its nearest centroid,
+ * ties to the lowest index; move every centroid to the mean of its members,
+ * an empty cluster keeps its centroid), then a final assignment, so labels
+ * are the nearest final centroids. Distances use the bf16 features exactly
+ * and the centroids to about fp32 accuracy.
+ * dtype: CABF_BF16 only (else CABF_EUNSUPPORTED).
+ * x: [B, heads, n, d] bf16 (input).
+ * init: [B, heads, clusters] int32 token indices of the initial centroids
+ *   (input; the caller's random draw; values are clamped to [0, n)).
+ * centroids: [B, heads, clusters, d] fp32 (output).
+ * counts: [B, heads, clusters] int32 members per cluster (output).
+ * labels: [B, heads, n] int32 cluster of every token (output).
+ * perm: [B, heads, n] int32 (output): the tokens sorted by cluster, stable
+ *   (a cluster's tokens keep their order); perm[i] = original index.
+ * offsets: [B, heads, clusters + 1] int32 (output): cluster c occupies
+ *   sorted positions offsets[c] .. offsets[c+1]-1.
+ * 1 <= clusters <= min(n, 8192); iters >= 0. Results are deterministic. */
+int cabf_kmeans(const cabf_seq* s, cabf_dtype dtype, const void* x, int32_t clusters,
+                const int32_t* init, int32_t iters, float* centroids, int32_t* counts,
+                int32_t* labels, int32_t* perm, int32_t* offsets, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Apply a per-(batch, head) permutation to token rows: xp[i] = x[perm[i]]
+ * for i < n; rows n .. rows_out-1 of xp are set to zero (rows_out >= n).
+ * x: [B, heads, n, d]; xp: [B, heads, rows_out, d]; bf16 or fp32; perm
+ * entries are clamped to [0, n). */
+int cabf_gather_rows(const cabf_seq* s, cabf_dtype dtype, const void* x, const int32_t* perm,
+                     void* xp, int32_t rows_out, hipStream_t stream);
+
+/* Undo it: x[perm[i]] = xp[i] for i < n (xp has rows_in >= n rows per
+ * head). perm must be a permutation of 0 .. n-1 (repeated entries race). */
+int cabf_scatter_rows(const cabf_seq* s, cabf_dtype dtype, const void* xp, int32_t rows_in,
+                      const int32_t* perm, void* x, hipStream_t stream);
+
+size_t cabf_cluster_select_workspace_bytes(const cabf_seq* s, int32_t cq, int32_t ck);
+
+/* Centroid-based top-p selection (Methodology B). For query cluster a and
+ * key cluster b: p_ab = |K_b| exp(scale <cq_a, ck_b>) / sum over b' (the
+ * attention share of b's tokens when each is represented by its centroid;
+ * empty clusters get 0); then the shortest prefix of row a sorted by p
+ * (descending, ties to the lower index) whose mass reaches top_p is kept.
+ * q_centroids [B, heads, cq, d], k_centroids [B, heads, ck, d] fp32 and
+ * k_counts [B, heads, ck] int32 (inputs, e.g. from cabf_kmeans).
+ * kv_count [B, heads, cq], kv_index [B, heads, cq, ck] int32 (outputs):
+ * kept key clusters of each query cluster, ascending. probs: NULL or
+ * [B, heads, cq, ck] fp32 (output). 0 < top_p <= 1, scale > 0,
+ * 1 <= ck <= 8192. */
+int cabf_cluster_select(const cabf_seq* s, int32_t cq, int32_t ck, const float* q_centroids,
+                        const float* k_centroids, const int32_t* k_counts, float scale,
+                        float top_p, int32_t* kv_count, int32_t* kv_index, float* probs,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t cabf_cluster_attention_workspace_bytes(const cabf_seq* s, int32_t cq, int32_t ck);
+
+/* Attention over the selected cluster pairs (Methodology C): every query
+ * row i of cluster a (permuted positions q_offsets[a] .. q_offsets[a+1]-1)
+ * attends to the key rows of its kept key clusters b (positions
+ * k_offsets[b] .. k_offsets[b+1]-1 of the permuted K and V):
+ *   o_i = sum_m exp(scale q_i.k_m) v_m / sum_m exp(scale q_i.k_m),
+ *   lse_i = ln sum_m exp(scale q_i.k_m),
+ * with bf16 matrix products, fp32 softmax, o rounded to bf16.
+ * dtype: CABF_BF16 only. qp, kp, vp: [B, heads, n + 64, d] permuted rows
+ * (cabf_gather_rows with rows_out = n + 64: the 64 zero rows keep the
+ * kernel's whole-tile loads in bounds). q_offsets [B, heads, cq + 1],
+ * k_offsets [B, heads, ck + 1] (e.g. cabf_kmeans' offsets; clamped to
+ * [0, n]), kv_count / kv_index as from cabf_cluster_select.
+ * op: [B, heads, n + 64, d] bf16 (output, rows < n written); lse: NULL or
+ * [B, heads, n + 64] fp32 (output, rows < n written). Rows of a query
+ * cluster that keeps nothing get o = 0, lse = -inf. */
+int cabf_cluster_attention(const cabf_seq* s, cabf_dtype dtype, int32_t cq, int32_t ck,
+                           const void* qp, const void* kp, const void* vp,
+                           const int32_t* q_offsets, const int32_t* k_offsets,
+                           const int32_t* kv_count, const int32_t* kv_index, float scale,
+                           void* op, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* cabf_status_string(int status);
 

@@ -147,6 +147,55 @@ def test_topk_and_sta_mask_argument_checks():
 
 
 @no_gpu
+def test_semantic_permutation_argument_checks():
+    seq = ctypes.byref(cabf._Seq(1, 2, 128, 1000))
+    ws = ctypes.c_void_p(0x300000)
+    need = L.cabf_kmeans_workspace_bytes(seq, 40)
+    assert need > 0
+    assert L.cabf_kmeans_workspace_bytes(seq, 0) == 0
+    assert L.cabf_kmeans_workspace_bytes(seq, 1001) == 0
+    assert L.cabf_kmeans_workspace_bytes(ctypes.byref(cabf._Seq(1, 2, 96, 1000)), 4) == 0
+    def km(**kw):
+        a = dict(seq=seq, dt=0, x=DUMMY, C=40, init=DUMMY2, iters=3, wsb=need)
+        a.update(kw)
+        return L.cabf_kmeans(a["seq"], a["dt"], a["x"], a["C"], a["init"], a["iters"], DUMMY2,
+                             DUMMY2, DUMMY2, DUMMY2, DUMMY2, ws, a["wsb"], NULL)
+    assert km(dt=1) == cabf.CABF_EUNSUPPORTED
+    assert km(x=NULL) == cabf.CABF_EINVAL
+    assert km(C=0) == cabf.CABF_EINVAL
+    assert km(iters=-1) == cabf.CABF_EINVAL
+    assert km(wsb=need - 1) == cabf.CABF_EWORKSPACE
+    assert km(seq=ctypes.byref(cabf._Seq(1, 2, 128, 0))) == cabf.CABF_EINVAL
+    assert km(seq=ctypes.byref(cabf._Seq(1, 2, 128, 1 << 24))) == cabf.CABF_EUNSUPPORTED
+    assert L.cabf_gather_rows(seq, 0, DUMMY, DUMMY2, DUMMY2, 999, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_gather_rows(seq, 0, ctypes.c_void_p(0x100008), DUMMY2, DUMMY2, 1064, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_scatter_rows(seq, 2, DUMMY, 1064, DUMMY2, DUMMY2, NULL) == cabf.CABF_EINVAL
+    sneed = L.cabf_cluster_select_workspace_bytes(seq, 10, 40)
+    def sel(**kw):
+        a = dict(cq=10, ck=40, scale=0.1, top_p=0.9, wsb=sneed)
+        a.update(kw)
+        return L.cabf_cluster_select(seq, a["cq"], a["ck"], DUMMY, DUMMY, DUMMY2, a["scale"],
+                                     a["top_p"], DUMMY2, DUMMY2, None, ws, a["wsb"], NULL)
+    assert sel(top_p=0.0) == cabf.CABF_EINVAL
+    assert sel(top_p=1.5) == cabf.CABF_EINVAL
+    assert sel(scale=0.0) == cabf.CABF_EINVAL
+    assert sel(ck=0) == cabf.CABF_EINVAL
+    assert sel(ck=9000) == cabf.CABF_EUNSUPPORTED
+    assert sel(wsb=sneed - 1) == cabf.CABF_EWORKSPACE
+    aneed = L.cabf_cluster_attention_workspace_bytes(seq, 10, 40)
+    def att(**kw):
+        a = dict(dt=0, cq=10, ck=40, qp=DUMMY, wsb=aneed)
+        a.update(kw)
+        return L.cabf_cluster_attention(seq, a["dt"], a["cq"], a["ck"], a["qp"], DUMMY, DUMMY,
+                                        DUMMY2, DUMMY2, DUMMY2, DUMMY2, 0.1, DUMMY2, None, ws,
+                                        a["wsb"], NULL)
+    assert att(dt=1) == cabf.CABF_EUNSUPPORTED
+    assert att(qp=NULL) == cabf.CABF_EINVAL
+    assert att(cq=1001) == cabf.CABF_EINVAL
+    assert att(wsb=aneed - 1) == cabf.CABF_EWORKSPACE
+
+
+@no_gpu
 def test_mask_rejects_rows_longer_than_supported():
     g = geom(T=129, H=64, W=64)      # 129 * 64 blocks > 8192
     assert L.cabf_build_block_mask(g, 0, DUMMY, DUMMY, 0.1, 0.2, None, DUMMY2, DUMMY2, None,
