@@ -12,10 +12,11 @@
 //               on the matrix cores (x is exact in bf16), fp32 accumulation,
 //               so the dot product is close to fp32 accuracy. Ties go to the
 //               lowest index.
-//   sort        stable segmented radix sort of the labels (token index as
-//               payload): the permutation, clusters contiguous, original
-//               order inside a cluster
-//   km_offsets  offsets[c] = first sorted position with label >= c
+//   sort        stable radix sort of the keys (bh << bits) | label over all
+//               heads at once (token index as payload): the permutation of
+//               every head, clusters contiguous, original order inside a
+//               cluster
+//   km_offsets  offsets[c] = first sorted position of the head with label >= c
 //   km_update   mean of the members, summed in sorted (token) order, so the
 //               result is deterministic; an empty cluster keeps its centroid
 // After the last update a final assignment and sort make labels, counts and
@@ -33,6 +34,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -89,121 +91,189 @@ __global__ __launch_bounds__(256) void km_prep(const float* __restrict__ cent,
   if (lane == 0) norm[row] = c < C ? s : INFINITY;
 }
 
-// Nearest centroid of 32 tokens per wave (128 per workgroup).
-// S = C_chunk X^T with v_mfma_f32_32x32x16_bf16: A = 32 centroids x 16 d (one
-// term), B = 16 d x 32 tokens; lane (token li, h) holds rows 8(r/4) + 4h + r%4
-// of its token's column, increasing with r.
+// Nearest centroid of 64 tokens per wave (256 per workgroup).
+// Distances against 32 centroids at a time: S = C_chunk X^T with
+// v_mfma_f32_32x32x16_bf16, A = 32 centroids x 16 d (one bf16 term, from LDS),
+// B = 16 d x 32 tokens (registers, two groups of 32 tokens per wave); lane
+// (token li, h) holds rows 8(r/4) + 4h + r%4 of its token's column, which
+// increase with r. The three terms of a chunk of 32 centroids (24 KB at
+// d = 128) are staged in LDS by the whole workgroup, double-buffered; rows are
+// padded by 16 bytes so that the 16 lanes of a read hit distinct banks.
 template <int D>
 __global__ __launch_bounds__(256) void km_assign(const uint16_t* __restrict__ x,
                                                  const uint16_t* __restrict__ terms,
                                                  const float* __restrict__ norm,
-                                                 int32_t* __restrict__ label, int n, int Cp,
-                                                 int64_t rows_padded, int tiles_per_bh) {
+                                                 int32_t* __restrict__ label,
+                                                 uint32_t* __restrict__ sort_key, int key_bits,
+                                                 int n, int Cp, int64_t rows_padded,
+                                                 int tiles_per_bh) {
   constexpr int kKS = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int kRow = D + 8;                       // padded LDS row (bf16 elements)
+  constexpr int kChunkElems = 3 * 32 * kRow;        // three terms of 32 centroids
+  constexpr int kLoads = 3 * 32 * (D / 8) / 256;    // 16-byte loads per thread per chunk
+  static_assert(3 * 32 * (D / 8) % 256 == 0, "chunk load split");
+  __shared__ uint16_t sc[2][kChunkElems];
+  __shared__ float sn[2][32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int li = lane & 31, h = lane >> 5;
   const int64_t bh = blockIdx.x / tiles_per_bh;
   const int tile = static_cast<int>(blockIdx.x - bh * tiles_per_bh);
-  const int t = tile * 128 + wave * 32 + li;
-  const int tl = min(t, n - 1);                  // rows past n are computed, not stored
-  bf16x8 xf[kKS];
+  bf16x8 xf[2][kKS];
+  int tok[2];
 #pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    const uint4 u = *reinterpret_cast<const uint4*>(x + (bh * n + tl) * D + 16 * ks + 8 * h);
-    xf[ks] = __builtin_bit_cast(bf16x8, u);
-  }
-  const uint16_t* t0 = terms + (bh * Cp) * D;
-  const uint16_t* t1 = t0 + rows_padded * D;
-  const uint16_t* t2 = t1 + rows_padded * D;
-  const float* nb = norm + bh * Cp;
-  float best = INFINITY;
-  int best_c = 0;
-  for (int c0 = 0; c0 < Cp; c0 += 32) {
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    const int64_t crow = static_cast<int64_t>(c0 + li) * D + 8 * h;
+  for (int g = 0; g < 2; ++g) {
+    tok[g] = tile * 256 + wave * 64 + g * 32 + li;
+    const int tl = min(tok[g], n - 1);             // rows past n are computed, not stored
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t0 + crow + 16 * ks));
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t1 + crow + 16 * ks));
-      const bf16x8 a2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t2 + crow + 16 * ks));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, xf[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xf[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xf[ks], acc, 0, 0, 0);
+      const uint4 u = *reinterpret_cast<const uint4*>(x + (bh * n + tl) * D + 16 * ks + 8 * h);
+      xf[g][ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  const uint16_t* tb = terms + (bh * Cp) * D;
+  const float* nb = norm + bh * Cp;
+  // chunk c0 of the three terms: thread loads kLoads 16-byte pieces
+  u32x4 stage[kLoads];
+  float stage_n = 0.0f;
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int piece = i * 256 + tid;             // (term, row, 16-byte column)
+      const int term = piece / (32 * (D / 8));
+      const int rem = piece - term * (32 * (D / 8));
+      const int row = rem / (D / 8), col = rem - row * (D / 8);
+      stage[i] = *reinterpret_cast<const u32x4*>(tb + term * rows_padded * D +
+                                                  static_cast<int64_t>(c0 + row) * D + col * 8);
+    }
+    if (tid < 32) stage_n = nb[c0 + tid];
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int piece = i * 256 + tid;
+      const int term = piece / (32 * (D / 8));
+      const int rem = piece - term * (32 * (D / 8));
+      const int row = rem / (D / 8), col = rem - row * (D / 8);
+      *reinterpret_cast<u32x4*>(&sc[buf][(term * 32 + row) * kRow + col * 8]) = stage[i];
+    }
+    if (tid < 32) sn[buf][tid] = stage_n;
+  };
+  float best[2] = {INFINITY, INFINITY};
+  int best_c[2] = {0, 0};
+  fetch(0);
+  store(0);
+  __syncthreads();
+  const int chunks = Cp / 32;
+  for (int ci = 0; ci < chunks; ++ci) {
+    const int buf = ci & 1;
+    if (ci + 1 < chunks) fetch((ci + 1) * 32);     // next chunk in flight during the products
+    f32x16 acc[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[g][r] = 0.0f;
+    const uint16_t* base = &sc[buf][li * kRow + 8 * h];
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+      for (int term = 2; term >= 0; --term) {      // smallest term first
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(base + term * 32 * kRow + 16 * ks));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[g][ks], acc[g], 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int c = c0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      const float dist = fmaf(-2.0f, acc[r], nb[c]);
-      if (dist < best) {        // strict: the lower index wins ties
-        best = dist;
-        best_c = c;
+      const int cl = 8 * (r >> 2) + 4 * h + (r & 3);
+      const float cn = sn[buf][cl];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float dist = fmaf(-2.0f, acc[g][r], cn);
+        if (dist < best[g]) {      // strict: the lower index wins ties
+          best[g] = dist;
+          best_c[g] = ci * 32 + cl;
+        }
       }
+    }
+    if (ci + 1 < chunks) {
+      __syncthreads();             // everyone is done with buffer buf ^ 1
+      store(buf ^ 1);
+      __syncthreads();
     }
   }
   // the other 16 rows of every group of 32 sit in lane ^ 32
-  const float ob = __shfl_xor(best, 32);
-  const int oc = __shfl_xor(best_c, 32);
-  if (ob < best || (ob == best && oc < best_c)) {
-    best = ob;
-    best_c = oc;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float ob = __shfl_xor(best[g], 32);
+    const int oc = __shfl_xor(best_c[g], 32);
+    if (ob < best[g] || (ob == best[g] && oc < best_c[g])) {
+      best[g] = ob;
+      best_c[g] = oc;
+    }
+    if (h == 0 && tok[g] < n) {
+      label[bh * n + tok[g]] = best_c[g];
+      sort_key[bh * n + tok[g]] = (static_cast<uint32_t>(bh) << key_bits) | best_c[g];
+    }
   }
-  if (h == 0 && t < n) label[bh * n + t] = best_c;
 }
 
-// offsets[bh, c] = first position of the sorted labels with label >= c, c <= C
-__global__ __launch_bounds__(256) void km_offsets(const int32_t* __restrict__ sorted_label,
+// offsets[bh, c] = first position of head bh's sorted keys with label >= c,
+// c <= C (all keys of a head share its high bits); counts on request
+__global__ __launch_bounds__(256) void km_offsets(const uint32_t* __restrict__ sorted_key,
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ counts, int n, int C,
-                                                  int64_t total /* BH * (C + 1) */) {
+                                                  int key_bits, int64_t total /* BH * (C + 1) */) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= total) return;
   const int64_t bh = e / (C + 1);
   const int c = static_cast<int>(e - bh * (C + 1));
-  const int32_t* s = sorted_label + bh * n;
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (s[mid] < c) lo = mid + 1; else hi = mid;
-  }
-  offsets[e] = lo;
-  if (c > 0 && counts != nullptr) {
-    // count of cluster c - 1 = offsets[c] - offsets[c - 1]
-    int lo2 = 0, hi2 = n;
-    while (lo2 < hi2) {
-      const int mid = (lo2 + hi2) >> 1;
-      if (s[mid] < c - 1) lo2 = mid + 1; else hi2 = mid;
+  const uint32_t* s = sorted_key + bh * n;
+  const uint32_t head = static_cast<uint32_t>(bh) << key_bits;
+  auto lower = [&](uint32_t key) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s[mid] < key) lo = mid + 1; else hi = mid;
     }
-    counts[bh * C + c - 1] = lo - lo2;
-  }
+    return lo;
+  };
+  const int at = lower(head | static_cast<uint32_t>(c));
+  offsets[e] = at;
+  if (c > 0 && counts != nullptr) counts[bh * C + c - 1] = at - lower(head | static_cast<uint32_t>(c - 1));
 }
 
-// one wave per cluster: mean of the members in sorted order
+// One workgroup per cluster: wave w sums members b + w*q .. (a contiguous
+// quarter, in sorted order), the four partial sums are added in wave order,
+// so the mean is deterministic. An empty cluster keeps its centroid.
 template <int D>
 __global__ __launch_bounds__(256) void km_update(const uint16_t* __restrict__ x,
                                                  const int32_t* __restrict__ perm,
                                                  const int32_t* __restrict__ offsets,
-                                                 float* __restrict__ cent, int n, int C,
-                                                 int64_t rows /* BH * C */) {
+                                                 float* __restrict__ cent, int n, int C) {
   constexpr int kPer = D / 64;
+  __shared__ float part[4][D];
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;                // bh * C + c
   const int64_t bh = row / C;
   const int c = static_cast<int>(row - bh * C);
   const int32_t* off = offsets + bh * (C + 1);
   const int b = off[c], e = off[c + 1];
-  if (e <= b) return;                       // empty: keep the centroid
+  if (e <= b) return;                            // uniform: keep the centroid
+  const int q = (e - b + 3) / 4;
+  const int wb = min(b + wave * q, e), we = min(wb + q, e);
   float acc[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) acc[i] = 0.0f;
+  for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
   const int32_t* p = perm + bh * n;
   const uint16_t* xb = x + bh * static_cast<int64_t>(n) * D + lane * kPer;
   // four rows in flight at a time, added in member order
-  int i = b;
-  for (; i + 4 <= e; i += 4) {
+  int i = wb;
+  for (; i + 4 <= we; i += 4) {
     uint16_t v[4][kPer];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -216,14 +286,21 @@ __global__ __launch_bounds__(256) void km_update(const uint16_t* __restrict__ x,
 #pragma unroll
       for (int k = 0; k < kPer; ++k) acc[k] += bf16_bits_to_f32(v[u][k]);
   }
-  for (; i < e; ++i) {
+  for (; i < we; ++i) {
     const uint16_t* src = xb + static_cast<int64_t>(p[i]) * D;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) acc[k] += bf16_bits_to_f32(src[k]);
   }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) part[wave][lane * kPer + k] = acc[k];
+  __syncthreads();
+  if (wave != 0) return;
   const float inv = 1.0f / static_cast<float>(e - b);
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) cent[row * D + lane * kPer + k] = acc[k] * inv;
+  for (int k = 0; k < kPer; ++k) {
+    const int j = lane * kPer + k;
+    cent[row * D + j] = (((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]) * inv;
+  }
 }
 
 __global__ __launch_bounds__(256) void km_iota(int32_t* __restrict__ v, int n, int64_t total) {
@@ -231,30 +308,19 @@ __global__ __launch_bounds__(256) void km_iota(int32_t* __restrict__ v, int n, i
   if (e < total) v[e] = static_cast<int32_t>(e % n);
 }
 
-__global__ __launch_bounds__(256) void km_seg_offsets(int32_t* __restrict__ seg, int n, int BH) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e <= BH) seg[e] = e * n;
-}
-
-int key_bits(int C) {
+int bits_for(int64_t values) {
   int b = 1;
-  while ((1 << b) < C) ++b;
+  while ((int64_t{1} << b) < values) ++b;
   return b;
 }
 
-// Labels are sorted as unsigned keys (they are non-negative) over their low
-// key_bits(C) bits; radix sorting is stable, so a cluster's tokens keep their
-// original order.
+// One device-wide stable radix sort over the combined keys of all heads.
 size_t sort_temp_bytes(int64_t BH, int n, int C) {
   size_t bytes = 0;
-  const int items = static_cast<int>(BH * n);
-  const int32_t* no_offsets = nullptr;
-  const hipError_t e = hipcub::DeviceSegmentedRadixSort::SortPairs(nullptr, bytes, static_cast<const uint32_t*>(nullptr),
-                                              static_cast<uint32_t*>(nullptr),
-                                              static_cast<const int32_t*>(nullptr),
-                                              static_cast<int32_t*>(nullptr), items,
-                                              static_cast<int>(BH), no_offsets, no_offsets, 0,
-                                              key_bits(C), nullptr);
+  const hipError_t e = hipcub::DeviceRadixSort::SortPairs(
+      nullptr, bytes, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
+      static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
+      static_cast<int>(BH * n), 0, bits_for(C) + bits_for(BH), nullptr);
   return e == hipSuccess ? bytes : 0;   // 0: the sort itself reports the failure at launch
 }
 
@@ -262,15 +328,17 @@ size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
 }  // namespace
 
+bool kmeans_keys_fit(int64_t BH, int C) { return bits_for(C) + bits_for(BH) <= 32; }
+
 KmeansWorkspace kmeans_workspace_layout(int64_t BH, int n, int C, int D) {
   KmeansWorkspace w{};
   const int Cp = (C + 31) / 32 * 32;
   size_t o = 0;
   w.terms = o;   o += align256(3 * static_cast<size_t>(BH) * Cp * D * sizeof(uint16_t));
   w.norm = o;    o += align256(static_cast<size_t>(BH) * Cp * sizeof(float));
-  w.sorted = o;  o += align256(static_cast<size_t>(BH) * n * sizeof(int32_t));
+  w.keys = o;    o += align256(static_cast<size_t>(BH) * n * sizeof(uint32_t));
+  w.sorted = o;  o += align256(static_cast<size_t>(BH) * n * sizeof(uint32_t));
   w.iota = o;    o += align256(static_cast<size_t>(BH) * n * sizeof(int32_t));
-  w.seg = o;     o += align256((static_cast<size_t>(BH) + 1) * sizeof(int32_t));
   w.sort_tmp = o;
   w.sort_tmp_bytes = sort_temp_bytes(BH, n, C);
   o += align256(w.sort_tmp_bytes);
@@ -285,9 +353,9 @@ int launch_kmeans(int64_t BH, int n, int D, int C, int iters, const void* x, con
   char* ws = static_cast<char*>(workspace);
   uint16_t* terms = reinterpret_cast<uint16_t*>(ws + w.terms);
   float* norm = reinterpret_cast<float*>(ws + w.norm);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
+  uint32_t* sorted = reinterpret_cast<uint32_t*>(ws + w.sorted);
   int32_t* iota = reinterpret_cast<int32_t*>(ws + w.iota);
-  int32_t* seg = reinterpret_cast<int32_t*>(ws + w.seg);
   void* tmp = ws + w.sort_tmp;
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   const int Cp = (C + 31) / 32 * 32;
@@ -296,43 +364,41 @@ int launch_kmeans(int64_t BH, int n, int D, int C, int iters, const void* x, con
   auto blocks = [](int64_t work, int per) { return dim3(static_cast<unsigned>((work + per - 1) / per)); };
 
   hipLaunchKernelGGL(km_iota, blocks(items, 256), dim3(256), 0, stream, iota, n, items);
-  hipLaunchKernelGGL(km_seg_offsets, blocks(BH + 1, 256), dim3(256), 0, stream, seg, n,
-                     static_cast<int>(BH));
   if (D == 64)
     hipLaunchKernelGGL((km_init<64>), blocks(BH * C * 64, 256), dim3(256), 0, stream, xs, init,
                        cent, n, C, BH * C);
   else
     hipLaunchKernelGGL((km_init<128>), blocks(BH * C * 128, 256), dim3(256), 0, stream, xs, init,
                        cent, n, C, BH * C);
-  const int tiles = (n + 127) / 128;
-  const int bits = key_bits(C);
+  const int tiles = (n + 255) / 256;
+  const int bits = bits_for(C);               // label bits of a sort key
+  const int end_bit = bits + bits_for(BH);
   for (int it = 0; it <= iters; ++it) {
     if (D == 64) {
       hipLaunchKernelGGL((km_prep<64>), blocks(rows_padded, 4), dim3(256), 0, stream, cent, terms,
                          norm, C, Cp, rows_padded);
       hipLaunchKernelGGL((km_assign<64>), dim3(static_cast<unsigned>(BH * tiles)), dim3(256), 0,
-                         stream, xs, terms, norm, label, n, Cp, rows_padded, tiles);
+                         stream, xs, terms, norm, label, keys, bits, n, Cp, rows_padded, tiles);
     } else {
       hipLaunchKernelGGL((km_prep<128>), blocks(rows_padded, 4), dim3(256), 0, stream, cent, terms,
                          norm, C, Cp, rows_padded);
       hipLaunchKernelGGL((km_assign<128>), dim3(static_cast<unsigned>(BH * tiles)), dim3(256), 0,
-                         stream, xs, terms, norm, label, n, Cp, rows_padded, tiles);
+                         stream, xs, terms, norm, label, keys, bits, n, Cp, rows_padded, tiles);
     }
     size_t tmp_bytes = w.sort_tmp_bytes;
-    const hipError_t e = hipcub::DeviceSegmentedRadixSort::SortPairs(
-        tmp, tmp_bytes, reinterpret_cast<const uint32_t*>(label), reinterpret_cast<uint32_t*>(sorted),
-        iota, perm, static_cast<int>(items), static_cast<int>(BH), seg, seg + 1, 0, bits, stream);
+    const hipError_t e = hipcub::DeviceRadixSort::SortPairs(
+        tmp, tmp_bytes, keys, sorted, iota, perm, static_cast<int>(items), 0, end_bit, stream);
     if (e != hipSuccess) return -1;
     const bool last = it == iters;
     hipLaunchKernelGGL(km_offsets, blocks(BH * (C + 1), 256), dim3(256), 0, stream, sorted,
-                       offsets, last ? counts : nullptr, n, C, BH * (C + 1));
+                       offsets, last ? counts : nullptr, n, C, bits, BH * (C + 1));
     if (last) break;
     if (D == 64)
-      hipLaunchKernelGGL((km_update<64>), blocks(BH * C, 4), dim3(256), 0, stream, xs, perm,
-                         offsets, cent, n, C, BH * C);
+      hipLaunchKernelGGL((km_update<64>), dim3(static_cast<unsigned>(BH * C)), dim3(256), 0, stream,
+                         xs, perm, offsets, cent, n, C);
     else
-      hipLaunchKernelGGL((km_update<128>), blocks(BH * C, 4), dim3(256), 0, stream, xs, perm,
-                         offsets, cent, n, C, BH * C);
+      hipLaunchKernelGGL((km_update<128>), dim3(static_cast<unsigned>(BH * C)), dim3(256), 0,
+                         stream, xs, perm, offsets, cent, n, C);
   }
   return 0;
 }
