@@ -34,6 +34,7 @@ from .nabla import (  # noqa: F401
     lists_to_mask,
     exempt_rows,
     bsa_forward,
+    bsa_backward,
     dense_attention,
     masked_attention_bruteforce,
     layer,

@@ -386,6 +386,50 @@ def bsa_forward(qp, kp, vp, kv_count, kv_index, g: Grid, scale: float):
     return op, lse
 
 
+def bsa_backward(qp, kp, vp, dop, kv_count, kv_index, g: Grid, scale: float):
+    """Gradients of the block-sparse attention (NABLA summary, closing remarks:
+    the method accelerates training as well as inference, so the sparse
+    attention needs its backward pass).
+
+    With L a scalar loss of the real output rows and dop = dL/dop (pad query
+    rows, which the layer discards, do not enter the function): for a real row
+    n of block i with key set K(i) (as in ``bsa_forward``),
+      P_nm = exp(s q_n.k_m) / sum_{m' in K(i)} exp(s q_n.k_m')
+      dv_m += P_nm do_n
+      dP_nm = do_n . v_m,  D_n = sum_m P_nm dP_nm,  dS_nm = P_nm (dP_nm - D_n)
+      dq_n = s sum_m dS_nm k_m,  dk_m += s dS_nm q_n
+    Returns (dq, dk, dv) [..., N, d] float64 with zero pad rows.
+    Pinned by: central finite differences of ``bsa_forward``, and torch
+    autograd through a token-masked dense attention.
+    """
+    qp, kp, vp, dop = (np.asarray(t, dtype=np.float64) for t in (qp, kp, vp, dop))
+    valid = valid_slots(g)
+    lead = qp.shape[:-2]
+    dq, dk, dv = np.zeros_like(qp), np.zeros_like(kp), np.zeros_like(vp)
+    B = g.block
+    for pos in np.ndindex(*lead):
+        for i in range(g.nb):
+            blocks = np.asarray(kv_index[pos][i][: int(kv_count[pos][i])], dtype=np.int64)
+            keys = (blocks[:, None] * B + np.arange(B)[None, :]).reshape(-1)
+            keys = keys[valid[keys]]
+            rows = np.arange(i * B, (i + 1) * B)
+            rows = rows[valid[rows]]
+            if keys.size == 0 or rows.size == 0:
+                continue
+            q, do = qp[pos][rows], dop[pos][rows]
+            k, v = kp[pos][keys], vp[pos][keys]
+            s = scale * (q @ k.T)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)
+            dP = do @ v.T
+            D = (P * dP).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[pos][rows] += scale * (dS @ k)
+            dk[pos][keys] += scale * (dS.T @ q)
+            dv[pos][keys] += P.T @ do
+    return dq, dk, dv
+
+
 def dense_attention(q, k, v, scale: float, key_valid=None):
     """Textbook softmax(scale q k^T) v over the token axis, fp64; optional key mask."""
     q = np.asarray(q, dtype=np.float64)

@@ -369,3 +369,60 @@ def test_result_does_not_depend_on_order_inside_a_patch():
         w = np.exp(s - s.max(1, keepdims=True))
         o = (w @ vs[keys]) / w.sum(1, keepdims=True)
         assert np.allclose(o, o1[perm[i * g.block:(i + 1) * g.block]], rtol=0, atol=1e-13)
+
+
+# --- backward --------------------------------------------------------------------
+
+def _bwd_case(seed=0, thr=0.4):
+    g = oracle.Grid(2, 11, 13, 8)          # partially padded blocks
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((g.n_valid, 6)) for _ in range(4))
+    qp, kp, vp = oracle.permute(q, g), oracle.permute(k, g), oracle.permute(v, g)
+    dop = oracle.permute(do, g)              # pad rows of the gradient are zero
+    info = oracle.build_block_mask(qp, kp, g, 0.9, thr)
+    return g, qp, kp, vp, dop, info
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of L = <dop, bsa_forward(...)> over real rows."""
+    g, qp, kp, vp, dop, info = _bwd_case()
+    cnt, idx = info["kv_count"], info["kv_index"]
+    dq, dk, dv = oracle.bsa_backward(qp, kp, vp, dop, cnt, idx, g, 0.9)
+    valid = oracle.valid_slots(g)
+    def loss(q_, k_, v_):
+        o, _ = oracle.bsa_forward(q_, k_, v_, cnt, idx, g, 0.9)
+        return float((o[valid] * dop[valid]).sum())
+    h = 1e-6
+    rng = np.random.default_rng(1)
+    for name, x, grad in (("q", qp, dq), ("k", kp, dk), ("v", vp, dv)):
+        for _ in range(6):
+            r = int(rng.choice(np.nonzero(valid)[0]))
+            c = int(rng.integers(0, x.shape[1]))
+            xp_, xm_ = x.copy(), x.copy()
+            xp_[r, c] += h
+            xm_[r, c] -= h
+            args_p = {"q": (xp_, kp, vp), "k": (qp, xp_, vp), "v": (qp, kp, xp_)}[name]
+            args_m = {"q": (xm_, kp, vp), "k": (qp, xm_, vp), "v": (qp, kp, xm_)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[r, c]) < 1e-6 * max(1.0, abs(fd)), (name, r, c, fd, grad[r, c])
+    pad = ~valid
+    assert np.all(dq[pad] == 0) and np.all(dk[pad] == 0) and np.all(dv[pad] == 0)
+
+
+def test_backward_matches_autograd_of_masked_dense_attention():
+    torch = pytest.importorskip("torch")
+    g, qp, kp, vp, dop, info = _bwd_case(seed=2, thr=0.3)
+    dq, dk, dv = oracle.bsa_backward(qp, kp, vp, dop, info["kv_count"], info["kv_index"], g, 0.9)
+    valid = oracle.valid_slots(g)
+    blk = np.arange(g.N) // g.block
+    allowed = info["mask"][blk][:, blk] & valid[None, :]           # [N, N] token mask
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in
+         (("q", qp), ("k", kp), ("v", vp))}
+    s = 0.9 * t["q"] @ t["k"].T
+    s = s.masked_fill(~torch.from_numpy(allowed), float("-inf"))
+    o = torch.softmax(s, dim=-1) @ t["v"]
+    rows = torch.from_numpy(valid)
+    (o[rows] * torch.from_numpy(dop)[rows]).sum().backward()
+    assert np.allclose(dq, t["q"].grad.numpy(), atol=1e-12)
+    assert np.allclose(dk, t["k"].grad.numpy(), atol=1e-12)
+    assert np.allclose(dv, t["v"].grad.numpy(), atol=1e-12)
