@@ -44,6 +44,8 @@ def parse():
                     help="walk every block list from its first entry (bit-reproducible attention)")
     ap.add_argument("--variants", type=int, default=1,
                     help="also time the 90%% and window variants (0 to skip)")
+    ap.add_argument("--backward", type=int, default=1,
+                    help="also time the block-sparse attention backward at the main sparsity (0 to skip)")
     ap.add_argument("--semantic", type=int, default=1,
                     help="also time the semantic-permutation (k-means + top-p) variant (0 to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -143,6 +145,42 @@ def profiled_traffic(workload: str):
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def measure_backward(cabf, geom, bufs, thr, sta, steps: int):
+    """cabf_bsa_backward on the main workload's lists (after a forward that
+    keeps lse), timed with HIP events. Effective TFLOP/s counts 2.5x the
+    forward's flops (five 64x64xd products per kept tile); the kernels
+    actually run seven (S and dP are recomputed in both gradient passes)."""
+    import torch
+    q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
+    scale = cabf.default_scale(geom)
+    cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
+    cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
+    lse = torch.empty(qp.shape[:3], dtype=torch.float32, device=qp.device)
+    cabf.cabf_bsa_forward(geom, qp, kp, vp, cnt, idx, scale, op, lse)
+    dop = torch.randn(qp.shape, generator=torch.Generator(device=qp.device).manual_seed(1),
+                      device=qp.device).to(qp.dtype)
+    dq, dk, dv = (torch.empty_like(qp) for _ in range(3))
+    bws = cabf._ws(cabf._lib.cabf_bsa_backward_workspace_bytes(cabf.ctypes.byref(geom.c())),
+                   qp.device)
+    for _ in range(2):
+        cabf.cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, cnt, idx, scale, dq, dk, dv, bws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cabf.cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, cnt, idx, scale, dq, dk, dv, bws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    kept = int(cnt.sum(dtype=torch.int64).item())
+    fwd_flops = 4.0 * 64 * 64 * geom.head_dim * kept
+    ms = statistics.fmean(times)
+    return {"ms": ms, "ms_median": statistics.median(times), "kept_tiles": kept,
+            "effective_tflops": 2.5 * fwd_flops / (ms * 1e-3) / 1e12,
+            "executed_tflops": 3.5 * fwd_flops / (ms * 1e-3) / 1e12}
 
 
 def measure_semantic(cabf, steps: int, warmup: int, seed: int):
@@ -419,6 +457,9 @@ def main():
                              attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
                              step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
         line["variants"] = var
+    if args.backward:
+        line["backward"] = measure_backward(cabf, geom, bufs, main_run["thr"], sta,
+                                            max(3, args.steps // 4))
     if args.semantic:
         line["semantic_variant"] = measure_semantic(cabf, max(3, args.steps // 4), 2, args.seed)
     if args.cpu_seconds > 0:

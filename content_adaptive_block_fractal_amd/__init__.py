@@ -27,7 +27,8 @@ CABF_BF16, CABF_F32 = 0, 1
 
 EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_unpermute", "cabf_mask_workspace_bytes",
             "cabf_build_block_mask", "cabf_build_block_mask_topk", "cabf_build_sta_mask",
-            "cabf_bsa_forward", "cabf_kmeans_workspace_bytes", "cabf_kmeans", "cabf_gather_rows",
+            "cabf_bsa_forward", "cabf_bsa_backward_workspace_bytes", "cabf_bsa_backward",
+            "cabf_kmeans_workspace_bytes", "cabf_kmeans", "cabf_gather_rows",
             "cabf_scatter_rows", "cabf_cluster_select_workspace_bytes", "cabf_cluster_select",
             "cabf_cluster_attention_workspace_bytes", "cabf_cluster_attention",
             "cabf_status_string")
@@ -81,6 +82,9 @@ def _load():
         "cabf_build_sta_mask": (ctypes.c_int, [G, ctypes.POINTER(_Sta), P, P, P]),
         "cabf_bsa_forward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, F32, P, P,
                                             ctypes.c_uint, P]),
+        "cabf_bsa_backward_workspace_bytes": (SZ, [G]),
+        "cabf_bsa_backward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, P, P, P, F32, P, P, P,
+                                             P, SZ, P]),
         "cabf_kmeans_workspace_bytes": (SZ, [Q, I32]),
         "cabf_kmeans": (ctypes.c_int, [Q, ctypes.c_int, P, I32, P, I32, P, P, P, P, P, P, SZ, P]),
         "cabf_gather_rows": (ctypes.c_int, [Q, ctypes.c_int, P, P, P, I32, P]),
@@ -317,6 +321,34 @@ def bsa_forward(qp, kp, vp, kv_count, kv_index, geom: Geom, scale=None, return_l
                      default_scale(geom) if scale is None else scale, op, lse,
                      BSA_DETERMINISTIC if deterministic else 0)
     return (op, lse) if return_lse else op
+
+
+def cabf_bsa_backward(geom: Geom, qp, kp, vp, op, lse, dop, kv_count, kv_index, scale: float,
+                      dqp, dkp, dvp, workspace):
+    """Gradients of cabf_bsa_forward: dqp, dkp, dvp [B, h, N, d] (bf16)."""
+    s = geom.sizes()
+    nb = s["n_blocks"]
+    ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
+    lead = (geom.batch, geom.heads, nb)
+    ptr, nbytes = _ws_ptr(workspace)
+    st = _lib.cabf_bsa_backward(
+        ctypes.byref(geom.c()), _dtype_code(qp), _dev(qp, ps, None, "qp"),
+        _dev(kp, ps, qp.dtype, "kp"), _dev(vp, ps, qp.dtype, "vp"), _dev(op, ps, qp.dtype, "op"),
+        _dev(lse, ps[:3], torch.float32, "lse"), _dev(dop, ps, qp.dtype, "dop"),
+        _dev(kv_count, lead, torch.int32, "kv_count"),
+        _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), float(scale),
+        _dev(dqp, ps, qp.dtype, "dqp"), _dev(dkp, ps, qp.dtype, "dkp"),
+        _dev(dvp, ps, qp.dtype, "dvp"), ptr, nbytes, _stream(qp))
+    _check("cabf_bsa_backward", st)
+
+
+def bsa_backward(qp, kp, vp, op, lse, dop, kv_count, kv_index, geom: Geom, scale=None):
+    """(dqp, dkp, dvp) of the block-sparse attention over the given lists."""
+    dqp, dkp, dvp = (torch.empty_like(qp) for _ in range(3))
+    ws = _ws(_lib.cabf_bsa_backward_workspace_bytes(ctypes.byref(geom.c())), qp.device)
+    cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, kv_count, kv_index,
+                      default_scale(geom) if scale is None else scale, dqp, dkp, dvp, ws)
+    return dqp, dkp, dvp
 
 
 def layer(q, k, v, geom: Geom, thr: float, sta=None, scale=None):

@@ -218,6 +218,38 @@ int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const
   return launched();
 }
 
+size_t cabf_bsa_backward_workspace_bytes(const cabf_geom* g) {
+  Geo geo;
+  if (make_geo(g, &geo) != CABF_OK) return 0;
+  return cabf::bwd_workspace_layout(geo).total;
+}
+
+int cabf_bsa_backward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp,
+                      const void* vp, const void* op, const float* lse, const void* dop,
+                      const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
+                      void* dkp, void* dvp, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  Geo geo;
+  const int st = make_geo(g, &geo);
+  if (st != CABF_OK) return st;
+  if (elem_bytes(dtype) == 0) return CABF_EINVAL;
+  if (dtype != CABF_BF16) return CABF_EUNSUPPORTED;
+  if (qp == nullptr || kp == nullptr || vp == nullptr || op == nullptr || lse == nullptr ||
+      dop == nullptr || kv_count == nullptr || kv_index == nullptr || dqp == nullptr ||
+      dkp == nullptr || dvp == nullptr || workspace == nullptr)
+    return CABF_EINVAL;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
+  if (misaligned(qp, 16) || misaligned(kp, 16) || misaligned(vp, 16) || misaligned(op, 16) ||
+      misaligned(dop, 16) || misaligned(dqp, 16) || misaligned(dkp, 16) || misaligned(dvp, 16) ||
+      misaligned(lse, 4) || misaligned(kv_count, 4) || misaligned(kv_index, 4) ||
+      misaligned(workspace, 256))
+    return CABF_EINVAL;
+  if (workspace_bytes < cabf::bwd_workspace_layout(geo).total) return CABF_EWORKSPACE;
+  cabf::launch_bsa_backward(geo, qp, kp, vp, op, lse, dop, kv_count, kv_index, scale, dqp, dkp,
+                            dvp, workspace, stream);
+  return launched();
+}
+
 size_t cabf_kmeans_workspace_bytes(const cabf_seq* s, int32_t clusters) {
   int64_t BH = 0;
   if (check_seq(s, &BH) != CABF_OK || clusters < 1 || clusters > s->n ||

@@ -1,0 +1,565 @@
+// Block-sparse attention backward on bf16 matrix cores (gradients of the
+// forward over the same kept tiles; NABLA summary, closing remarks: the
+// sparse attention serves training as well as inference).
+//
+// For a real query row n of block i with kept key set K(i):
+//   P_nm = exp(s q_n.k_m - lse_n), dP_nm = do_n.v_m, D_n = do_n.o_n,
+//   dS_nm = P_nm (dP_nm - D_n), dq_n = s sum_m dS_nm k_m,
+//   dk_m = s sum_n dS_nm q_n, dv_m = sum_n P_nm do_n.
+// (D_n = sum_m P_nm dP_nm because o_n = sum_m P_nm v_m.)
+//
+//   bwd_rowdot     D = rowsum(dO * O), fp32
+//   bwd_dq         one workgroup per query block over its kept key blocks, as
+//                  the forward: S^T = K Q^T and dP^T = V dO^T on the matrix
+//                  cores (K, V rows from LDS; Q^T, dO^T in registers), then
+//                  dQ^T += K^T dS^T with K^T from transposing LDS reads
+//   bwd_transpose  the kept lists turned around: for every key block, the
+//                  query blocks that keep it, ascending (through a bitmap)
+//   bwd_dkdv       one workgroup per key block over those query blocks:
+//                  S = Q K^T and dP = dO V^T (Q, dO rows from LDS; K, V in
+//                  registers), then dV^T += dO^T P and dK^T += Q^T dS with
+//                  dO^T, Q^T from transposing LDS reads
+// Both gradient kernels split the 64 x 64 tile over 4 waves (two halves of
+// each side) and add the two partial sums of a row once at the end, so every
+// result is deterministic. Pad query rows do not contribute and get dq = 0;
+// pad key rows get dk = dv = 0.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "attention_common.hpp"
+#include "attention_tiles.hpp"
+#include "geometry.hpp"
+#include "launch.hpp"
+
+namespace cabf {
+namespace {
+
+using namespace tiles;
+
+__device__ inline float bf16_f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+// D[row] = sum_d dO[row, d] O[row, d]; 16 threads per row
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot(const uint16_t* __restrict__ o,
+                                                  const uint16_t* __restrict__ dout,
+                                                  float* __restrict__ delta, int64_t rows) {
+  constexpr int kPer = D / 16;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float s = 0.0f;
+  if (row < rows) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t e = row * D + sub * kPer + k;
+      s = fmaf(bf16_f(o[e]), bf16_f(dout[e]), s);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (sub == 0 && row < rows) delta[row] = s;
+}
+
+// Element offsets (within a 64-row K-swizzled tile) of the 4 * kDT transposing
+// reads that give a lane its fragments of X^T (d x rows) for rows
+// rbase + 4 (vgrp / 2) + vsl / 4 + 16 st + 8 half and columns 32 dt + vcol;
+// constant per lane.
+template <int D>
+__device__ inline void transposed_offsets(int (&off)[D / 32][2][2], int rbase, int lane) {
+  const int vgrp = lane >> 4, vsl = lane & 15;
+  const int vcol = 16 * (vgrp & 1) + 4 * (vsl & 3);
+  const int vrow = rbase + 4 * (vgrp >> 1) + (vsl >> 2);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = vrow + 16 * st + 8 * hf;
+        const int col = 32 * dt + vcol;
+        off[dt][st][hf] = k_chunk_slot<D>(row, col >> 3) * 8 + (col & 7);
+      }
+}
+
+__device__ inline bf16x8 transposed_fragment(const uint16_t* tile, int off_lo, int off_hi) {
+  const s16x4 both[2] = {read_v_transposed(tile + off_lo), read_v_transposed(tile + off_hi)};
+  bf16x8 a;
+  __builtin_memcpy(&a, both, sizeof(a));
+  return a;
+}
+
+// Bits r of the 16 accumulator rows 8 (r / 4) + 4 h + r % 4 of half `half`
+// (of a 64-row block, keys or queries) that are real tokens of a patch with
+// extent ext.
+__device__ inline uint32_t real_row_bits(const BlockExtent& ext, int half, int h) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int iy = 4 * half + (r >> 2), ix = 4 * h + (r & 3);
+    bits |= (iy < ext.vy && ix < ext.vx) ? (1u << r) : 0u;
+  }
+  return bits;
+}
+
+// Loads the D-wide rows of one 64-row tile of `a` and `b` (K/V, or Q/dO) into
+// a K-swizzled LDS slot each.
+template <int D>
+__device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, u32x4* sa, u32x4* sb,
+                                          uint32_t off, int wave) {
+  issue_tile_load<D>(a, sa, off, wave);
+  issue_tile_load<D>(b, sb, off, wave);
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per query block. Wave (wq, wk): query half wq, key half
+// wk of every tile; lane holds query row li of its half (as in the forward).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq(AttnArgs a, const uint16_t* __restrict__ dop,
+                                                      const float* __restrict__ delta,
+                                                      uint16_t* __restrict__ dqp, int64_t n_items) {
+  using S = Stage<D>;
+  constexpr int kKS = D / 16;
+  constexpr int kDT = D / 32;
+  __shared__ u32x4 k_slot0[S::kTile], k_slot1[S::kTile];
+  __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave & 1, wk = wave >> 1;
+  const int li = lane & 31, h = lane >> 5;
+  const int64_t item = xcd_order(blockIdx.x, n_items);
+  const int64_t bh = item / a.nb;
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.kp) + bh * a.N * D;
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.vp) + bh * a.N * D;
+  const int64_t qrow = item * kBlock + wq * 32 + li;
+
+  bf16x8 qf[kKS], df[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Q + qrow * D + 16 * ks + 8 * h));
+    df[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dop + qrow * D + 16 * ks + 8 * h));
+  }
+  const float lse = a.lse[qrow];
+  // a row without keys has lse = -inf: P = exp2(x - inf) = 0 everywhere
+  const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  const float dlt = delta[qrow];
+  const float c = a.scale_log2;
+  f32x16 acc[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+
+  const int cnt = min(max(a.kv_count[item], 0), a.nb);
+  const int32_t* __restrict__ list = a.kv_index + item * a.nb;
+  const int key0 = 32 * wk;
+  int toff[kDT][2][2];
+  transposed_offsets<D>(toff, key0, lane);
+  auto tile_of = [&](int t) {
+    const int jb = list[t < cnt ? t : cnt - 1];
+    const bool real = static_cast<unsigned>(jb) < static_cast<unsigned>(a.nb);
+    return real ? jb : -1;
+  };
+  // S^T or dP^T of this wave's 32 keys: rows of `tile` against fragments f
+  auto rows_times = [&](const u32x4* tile, const bf16x8 (&f)[kKS]) {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const u32x4 u = tile[k_chunk_slot<D>(key0 + li, 2 * ks + h)];
+      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), f[ks], r, 0, 0, 0);
+    }
+    return r;
+  };
+  auto step = [&](int jb, const u32x4* ks_, const u32x4* vs_) {
+    f32x16 s = rows_times(ks_, qf);
+    const f32x16 dp = rows_times(vs_, df);
+    const BlockExtent ext = jb >= 0 ? block_extent(jb, a) : BlockExtent{0, 0};
+    const uint32_t bits = ext.full() ? 0xffffu : real_row_bits(ext, wk, h);
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = ((bits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2)) : 0.0f;
+      dsb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dlt));
+    }
+    const uint16_t* kt = reinterpret_cast<const uint16_t*>(ks_);
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            transposed_fragment(kt, toff[dt][st][0], toff[dt][st][1]), dsb[st], acc[dt], 0, 0, 0);
+  };
+
+  if (cnt > 0) {
+    const uint32_t off = tile_load_offset<D, false>(wave, lane);
+    int jb_cur = tile_of(0);
+    load_pair<D>(K + static_cast<int64_t>(max(jb_cur, 0)) * kBlock * D,
+                 V + static_cast<int64_t>(max(jb_cur, 0)) * kBlock * D, k_slot0, v_slot0, off, wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto body = [&](int e, auto parity) {
+      constexpr int kOdd = decltype(parity)::value;
+      u32x4* const kc = kOdd ? k_slot1 : k_slot0;
+      u32x4* const vc = kOdd ? v_slot1 : v_slot0;
+      u32x4* const kn = kOdd ? k_slot0 : k_slot1;
+      u32x4* const vn = kOdd ? v_slot0 : v_slot1;
+      const int jb_next = tile_of(e + 1);
+      if (e + 1 < cnt)
+        load_pair<D>(K + static_cast<int64_t>(max(jb_next, 0)) * kBlock * D,
+                     V + static_cast<int64_t>(max(jb_next, 0)) * kBlock * D, kn, vn, off, wave);
+      step(jb_cur, kc, vc);
+      jb_cur = jb_next;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int e = 0; e < cnt; e += 2) {
+      body(e, std::integral_constant<int, 0>{});
+      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
+    }
+  }
+
+  // ---- add the two key halves, scale, store (pad query rows: 0) ------------
+  float* const part = reinterpret_cast<float*>(wq ? k_slot1 : k_slot0);
+  static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
+  if (wk == 1) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+  }
+  __syncthreads();
+  if (wk == 1) return;
+  const BlockExtent qext = block_extent(static_cast<int>(item % a.nb), a);
+  const int rloc = wq * 32 + li;
+  const bool real_row = qext.real(rloc);
+  const float sc = real_row ? a.scale_log2 * kLn2 : 0.0f;   // the softmax scale s
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * h;
+      float v[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * g + x;
+        v[x] = (acc[dt][r] + part[(dt * 16 + r) * 64 + lane]) * sc;
+      }
+      uint2 w;
+      w.x = static_cast<uint32_t>(f32_to_bf16_rne(v[0])) |
+            (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+      w.y = static_cast<uint32_t>(f32_to_bf16_rne(v[2])) |
+            (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+      *reinterpret_cast<uint2*>(dqp + qrow * D + d) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed lists: bit (i, j) set when query block i keeps key block j.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_fill_zero(uint32_t* __restrict__ p, int64_t words) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e < words) p[e] = 0u;
+}
+
+__global__ __launch_bounds__(256) void bwd_bitmap(const int32_t* __restrict__ kv_count,
+                                                  const int32_t* __restrict__ kv_index,
+                                                  uint32_t* __restrict__ bitmap, int nb, int words,
+                                                  int64_t total /* BH * nb * nb */) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int64_t row = e / nb;                     // bh * nb + i
+  const int t = static_cast<int>(e - row * nb);
+  if (t >= min(max(kv_count[row], 0), nb)) return;
+  const int j = kv_index[e];
+  if (static_cast<unsigned>(j) >= static_cast<unsigned>(nb)) return;
+  atomicOr(bitmap + row * words + (j >> 5), 1u << (j & 31));
+}
+
+// one wave per (bh, key block j): the query blocks i with bit (i, j), ascending
+__global__ __launch_bounds__(256) void bwd_transpose(const uint32_t* __restrict__ bitmap,
+                                                     int32_t* __restrict__ q_count,
+                                                     int32_t* __restrict__ q_index, int nb,
+                                                     int words, int64_t rows /* BH * nb */) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t bh = row / nb;
+  const int j = static_cast<int>(row - bh * nb);
+  const uint32_t* bm = bitmap + bh * nb * static_cast<int64_t>(words) + (j >> 5);
+  int32_t* out = q_index + row * nb;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int count = 0;
+  for (int base = 0; base < nb; base += 64) {
+    const int i = base + lane;
+    const bool keep = i < nb && ((bm[static_cast<int64_t>(i) * words] >> (j & 31)) & 1u);
+    const uint64_t b = __ballot(keep);
+    if (keep) out[count + __popcll(b & lt)] = i;
+    count += __popcll(b);
+  }
+  if (lane == 0) q_count[row] = count;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per key block. Wave (wk, wq): key half wk, query half
+// wq of every tile; lane holds key li of its half. S = Q K^T and dP = dO V^T
+// give each lane one key column and 16 query rows, which serve as the B
+// operand (contraction over queries) of dV^T += dO^T P and dK^T += Q^T dS.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(AttnArgs a, const uint16_t* __restrict__ dop,
+                                                        const float* __restrict__ delta,
+                                                        const int32_t* __restrict__ q_count,
+                                                        const int32_t* __restrict__ q_index,
+                                                        uint16_t* __restrict__ dkp,
+                                                        uint16_t* __restrict__ dvp, int64_t n_items) {
+  using S = Stage<D>;
+  constexpr int kKS = D / 16;
+  constexpr int kDT = D / 32;
+  __shared__ u32x4 q_slot0[S::kTile], q_slot1[S::kTile];
+  __shared__ u32x4 d_slot0[S::kTile], d_slot1[S::kTile];
+  __shared__ __align__(16) float vec_slot[2][2][kBlock];   // [slot][lse2, D][row]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave & 1, wq = wave >> 1;
+  const int li = lane & 31, h = lane >> 5;
+  const int64_t item = xcd_order(blockIdx.x, n_items);     // bh * nb + key block j
+  const int64_t bh = item / a.nb;
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp) + bh * a.N * D;
+  const uint16_t* __restrict__ dO = dop + bh * a.N * D;
+  const float* __restrict__ lse_h = a.lse + bh * a.N;
+  const float* __restrict__ dl_h = delta + bh * a.N;
+  const int64_t krow = item * kBlock + wk * 32 + li;        // global key row of this lane
+  const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(a.kp);
+  const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(a.vp);
+  bf16x8 kf[kKS], vf[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + krow * D + 16 * ks + 8 * h));
+    vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
+  }
+  const float c = a.scale_log2;
+  f32x16 dk[kDT], dv[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.0f;
+      dv[dt][r] = 0.0f;
+    }
+
+  const int cnt = min(max(q_count[item], 0), a.nb);
+  const int32_t* __restrict__ list = q_index + item * a.nb;
+  const int row0 = 32 * wq;                                 // first query row of this wave's half
+  int toff[kDT][2][2];
+  transposed_offsets<D>(toff, row0, lane);
+  auto block_of = [&](int t) { return list[t < cnt ? t : cnt - 1]; };
+  // S or dP of this wave's 32 queries x 32 keys: rows of `tile` against f
+  auto rows_times = [&](const u32x4* tile, const bf16x8 (&f)[kKS]) {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const u32x4 u = tile[k_chunk_slot<D>(row0 + li, 2 * ks + h)];
+      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), f[ks], r, 0, 0, 0);
+    }
+    return r;
+  };
+  auto step = [&](int ib, const u32x4* qs, const u32x4* ds, const float (&vec)[2][kBlock]) {
+    const f32x16 s = rows_times(qs, kf);
+    const f32x16 dp = rows_times(ds, vf);
+    const BlockExtent ext = block_extent(ib, a);
+    const uint32_t bits = ext.full() ? 0xffffu : real_row_bits(ext, wq, h);
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int m = row0 + 8 * g + 4 * h;                  // rows m .. m + 3
+      const float4 l4 = *reinterpret_cast<const float4*>(&vec[0][m]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&vec[1][m]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * g + x;
+        const float p = ((bits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x])) : 0.0f;
+        pb[r >> 3][r & 7] = static_cast<__bf16>(p);
+        dsb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dv4[x]));
+      }
+    }
+    const uint16_t* qt = reinterpret_cast<const uint16_t*>(qs);
+    const uint16_t* dt_ = reinterpret_cast<const uint16_t*>(ds);
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            transposed_fragment(dt_, toff[dt][st][0], toff[dt][st][1]), pb[st], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            transposed_fragment(qt, toff[dt][st][0], toff[dt][st][1]), dsb[st], dk[dt], 0, 0, 0);
+      }
+  };
+  // lse (base 2, +inf for rows without keys) and D of query block ib -> vec slot
+  auto load_vecs = [&](int ib, float (&vec)[2][kBlock]) {
+    if (tid < kBlock) {
+      const float l = lse_h[static_cast<int64_t>(ib) * kBlock + tid];
+      vec[0][tid] = l == -INFINITY ? INFINITY : l * kLog2e;
+      vec[1][tid] = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
+    }
+  };
+
+  if (cnt > 0) {
+    const uint32_t off = tile_load_offset<D, false>(wave, lane);
+    int ib_cur = block_of(0);
+    load_pair<D>(Q + static_cast<int64_t>(ib_cur) * kBlock * D, dO + static_cast<int64_t>(ib_cur) * kBlock * D,
+                 q_slot0, d_slot0, off, wave);
+    load_vecs(ib_cur, vec_slot[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto body = [&](int e, auto parity) {
+      constexpr int kOdd = decltype(parity)::value;
+      u32x4* const qc = kOdd ? q_slot1 : q_slot0;
+      u32x4* const dc = kOdd ? d_slot1 : d_slot0;
+      u32x4* const qn = kOdd ? q_slot0 : q_slot1;
+      u32x4* const dn = kOdd ? d_slot0 : d_slot1;
+      const int ib_next = block_of(e + 1);
+      if (e + 1 < cnt) {
+        load_pair<D>(Q + static_cast<int64_t>(ib_next) * kBlock * D,
+                     dO + static_cast<int64_t>(ib_next) * kBlock * D, qn, dn, off, wave);
+        load_vecs(ib_next, vec_slot[kOdd ^ 1]);
+      }
+      step(ib_cur, qc, dc, vec_slot[kOdd]);
+      ib_cur = ib_next;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int e = 0; e < cnt; e += 2) {
+      body(e, std::integral_constant<int, 0>{});
+      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
+    }
+  }
+
+  // ---- add the two query halves, scale dK, store (pad keys: 0) -------------
+  float* const pk = reinterpret_cast<float*>(wk ? q_slot1 : q_slot0);
+  float* const pv = reinterpret_cast<float*>(wk ? d_slot1 : d_slot0);
+  static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
+  if (wq == 1) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pk[(dt * 16 + r) * 64 + lane] = dk[dt][r];
+        pv[(dt * 16 + r) * 64 + lane] = dv[dt][r];
+      }
+  }
+  __syncthreads();
+  if (wq == 1) return;
+  const BlockExtent kext = block_extent(static_cast<int>(item % a.nb), a);
+  const bool real_key = kext.real(wk * 32 + li);
+  const float sk = real_key ? a.scale_log2 * kLn2 : 0.0f;   // dK carries the softmax scale s
+  const float sv = real_key ? 1.0f : 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * h;
+      float xk[4], xv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * g + x;
+        xk[x] = (dk[dt][r] + pk[(dt * 16 + r) * 64 + lane]) * sk;
+        xv[x] = (dv[dt][r] + pv[(dt * 16 + r) * 64 + lane]) * sv;
+      }
+      uint2 wkp, wvp;
+      wkp.x = static_cast<uint32_t>(f32_to_bf16_rne(xk[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(xk[1])) << 16);
+      wkp.y = static_cast<uint32_t>(f32_to_bf16_rne(xk[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(xk[3])) << 16);
+      wvp.x = static_cast<uint32_t>(f32_to_bf16_rne(xv[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(xv[1])) << 16);
+      wvp.y = static_cast<uint32_t>(f32_to_bf16_rne(xv[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(xv[3])) << 16);
+      *reinterpret_cast<uint2*>(dkp + krow * D + d) = wkp;
+      *reinterpret_cast<uint2*>(dvp + krow * D + d) = wvp;
+    }
+}
+
+dim3 grid_for(int64_t work, int per) { return dim3(static_cast<unsigned>((work + per - 1) / per)); }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
+
+}  // namespace
+
+BwdWorkspace bwd_workspace_layout(const Geo& g) {
+  BwdWorkspace w{};
+  w.words = (g.nb + 31) / 32;
+  size_t o = 0;
+  w.delta = o;    o += align256(static_cast<size_t>(g.BH) * g.N * sizeof(float));
+  w.bitmap = o;   o += align256(static_cast<size_t>(g.BH) * g.nb * w.words * sizeof(uint32_t));
+  w.q_count = o;  o += align256(static_cast<size_t>(g.BH) * g.nb * sizeof(int32_t));
+  w.q_index = o;  o += align256(static_cast<size_t>(g.BH) * g.nb * g.nb * sizeof(int32_t));
+  w.total = o;
+  return w;
+}
+
+void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const void* vp,
+                         const void* op, const float* lse, const void* dop,
+                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
+                         void* dkp, void* dvp, void* workspace, hipStream_t stream) {
+  const BwdWorkspace w = bwd_workspace_layout(g);
+  char* ws = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws + w.delta);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + w.bitmap);
+  int32_t* q_count = reinterpret_cast<int32_t*>(ws + w.q_count);
+  int32_t* q_index = reinterpret_cast<int32_t*>(ws + w.q_index);
+  const int64_t rows = g.BH * g.N;
+  const uint16_t* o16 = static_cast<const uint16_t*>(op);
+  const uint16_t* do16 = static_cast<const uint16_t*>(dop);
+  if (g.D == 64)
+    hipLaunchKernelGGL((bwd_rowdot<64>), grid_for(rows, 16), dim3(256), 0, stream, o16, do16, delta, rows);
+  else
+    hipLaunchKernelGGL((bwd_rowdot<128>), grid_for(rows, 16), dim3(256), 0, stream, o16, do16, delta, rows);
+  const int64_t words = g.BH * g.nb * w.words;
+  hipLaunchKernelGGL(bwd_fill_zero, grid_for(words, 256), dim3(256), 0, stream, bitmap, words);
+  const int64_t entries = g.BH * g.nb * g.nb;
+  hipLaunchKernelGGL(bwd_bitmap, grid_for(entries, 256), dim3(256), 0, stream, kv_count, kv_index,
+                     bitmap, g.nb, w.words, entries);
+  hipLaunchKernelGGL(bwd_transpose, grid_for(g.BH * g.nb, 4), dim3(256), 0, stream, bitmap, q_count,
+                     q_index, g.nb, w.words, g.BH * g.nb);
+
+  AttnArgs a{};
+  a.qp = qp;
+  a.kp = kp;
+  a.vp = vp;
+  a.kv_count = kv_count;
+  a.kv_index = kv_index;
+  a.lse = const_cast<float*>(lse);
+  a.scale_log2 = scale * kLog2e;
+  a.nb = g.nb;
+  a.Ty = g.Ty;
+  a.Tx = g.Tx;
+  a.H = g.H;
+  a.W = g.W;
+  a.N = g.N;
+  a.BH = g.BH;
+  const int64_t items = g.BH * g.nb;
+  const unsigned grid = static_cast<unsigned>(items);
+  uint16_t* dq16 = static_cast<uint16_t*>(dqp);
+  uint16_t* dk16 = static_cast<uint16_t*>(dkp);
+  uint16_t* dv16 = static_cast<uint16_t*>(dvp);
+  if (g.D == 64) {
+    hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, dq16, items);
+    hipLaunchKernelGGL((bwd_dkdv<64>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, q_count,
+                       q_index, dk16, dv16, items);
+  } else {
+    hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, dq16, items);
+    hipLaunchKernelGGL((bwd_dkdv<128>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, q_count,
+                       q_index, dk16, dv16, items);
+  }
+}
+
+}  // namespace cabf

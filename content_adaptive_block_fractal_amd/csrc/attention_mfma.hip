@@ -45,110 +45,15 @@
 #include <type_traits>
 
 #include "attention_common.hpp"
+#include "attention_tiles.hpp"
 #include "geometry.hpp"
 #include "launch.hpp"
 
 namespace cabf {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kXcds = 8;
+using namespace tiles;
 constexpr float kRescaleSlack = 8.0f;   // base-2 headroom before the running max is raised
-
-// Workgroup id -> query block: XCD x (which receives ids x, x+8, ...) gets
-// the contiguous range [start_x, start_x + count_x).
-__device__ inline int64_t xcd_order(int64_t wg, int64_t total) {
-#if defined(CABF_WG_ORDER) && CABF_WG_ORDER == 1
-  return wg;   // plain dispatch order: all XCDs sweep the same head together
-#endif
-  const int64_t xcd = wg % kXcds, local = wg / kXcds;
-  const int64_t per = total / kXcds, rem = total % kXcds;
-  return xcd * per + (xcd < rem ? xcd : rem) + local;
-}
-
-// K tile: 64 rows x D bf16 = 64 x (D/8) chunks of 16 bytes.
-template <int D>
-__device__ inline int k_chunk_slot(int key, int chunk) {
-  constexpr int kChunks = D / 8;
-  // D = 128: a row spans all 64 banks, rotate chunks by key % 16;
-  // D = 64: two rows per bank sweep, rotate by (key / 2) % 8.
-  const int swz = (D == 128) ? (key & 15) : ((key >> 1) & 7);
-  return key * kChunks + (chunk ^ swz);
-}
-
-// V tile: 64 rows x D bf16, row-major like K. A transposing read fetches,
-// per 16-lane group, 4 consecutive rows x 32 bytes; the two groups of a
-// 32-lane half read the same rows at neighbouring 32-byte columns. XOR-ing
-// the 16-byte chunk index with 4 * (row % 4) (D = 64: 4 * ((row / 2) % 2))
-// keeps every 32-byte pair intact and gives the 8 (row, pair) reads of a
-// half distinct banks.
-template <int D>
-__device__ inline int v_chunk_slot(int key, int chunk) {
-  constexpr int kChunks = D / 8;
-  const int swz = (D == 128) ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-  return key * kChunks + (chunk ^ swz);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// max of v over lanes l and l ^ 32 (v_permlane32_swap exchanges the upper
-// half of its first operand with the lower half of its second: with both set
-// to v, the two results hold v of lane l and of lane l ^ 32 in every lane)
-__device__ inline float pair_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// 4 consecutive keys of one head-dim column of the V tile (see above).
-__device__ inline s16x4 read_v_transposed(const uint16_t* sv_row_chunk) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_row_chunk));
-}
-
-template <int D>
-struct Stage {
-  static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
-  static constexpr int kIters = kBlock * kChunks / kThreads;   // chunks per thread per tensor
-  static constexpr int kTile = kBlock * kChunks;               // 16-byte chunks per K (or V) tile
-  static constexpr int kRowsPerIter = kThreads / kChunks;      // rows one pass of the workgroup fills
-};
-
-// Direct-to-LDS copy of one K or V tile into a ring slot: each wave
-// instruction fills 64 consecutive 16-byte LDS chunks (lane l -> chunk base +
-// l); the lane fetches the global chunk that the swizzle places there. Pass i
-// covers the rows of pass 0 moved down by i * kRowsPerIter, a multiple of the
-// swizzle's period in the row, so a lane's source offset in pass i is its
-// offset in pass 0 plus a constant (added to the scalar base). The offsets are
-// the same for every tile.
-template <int D, bool IS_V>
-__device__ inline uint32_t tile_load_offset(int wave, int lane) {
-  using S = Stage<D>;
-  static_assert(S::kRowsPerIter % 16 == 0, "swizzle period");
-  const int phys = wave * 64 + lane;
-  const int row = phys / S::kChunks;
-  const int pc = phys % S::kChunks;
-  // the swizzle is an XOR with a function of the row: its own inverse
-  const int chunk = IS_V ? (v_chunk_slot<D>(row, pc) - row * S::kChunks)
-                         : (k_chunk_slot<D>(row, pc) - row * S::kChunks);
-  return static_cast<uint32_t>((row * D + chunk * 8) * 2);
-}
-
-template <int D>
-__device__ __forceinline__ void issue_tile_load(const uint16_t* __restrict__ tile_src, u32x4* slot,
-                                                uint32_t off, int wave) {
-  using S = Stage<D>;
-#pragma unroll
-  for (int i = 0; i < S::kIters; ++i) {
-    const char* base = reinterpret_cast<const char*>(tile_src + i * S::kRowsPerIter * D);
-    __builtin_amdgcn_global_load_lds(base + off, slot + (i * kWaves + wave) * 64, 16, 0, 0);
-  }
-}
 
 // A list entry decoded: element offset of its 64 K/V rows in the head, and
 // what the layout needs to mask it (block index, or number of valid keys).

@@ -30,6 +30,18 @@ void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void
 void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_count,
                            int32_t* kv_index, hipStream_t stream);
 
+// Backward workspace: D = rowsum(dO * O), the kept-list bitmap and the
+// transposed lists (query blocks of every key block).
+struct BwdWorkspace {
+  int words;
+  size_t delta, bitmap, q_count, q_index, total;
+};
+BwdWorkspace bwd_workspace_layout(const Geo& g);
+void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const void* vp,
+                         const void* op, const float* lse, const void* dop,
+                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
+                         void* dkp, void* dvp, void* workspace, hipStream_t stream);
+
 void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
                         float* lse, bool phased, hipStream_t stream);

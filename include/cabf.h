@@ -181,6 +181,31 @@ int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype,
                      const int32_t* kv_count, const int32_t* kv_index, float scale,
                      void* op, float* lse, unsigned flags, hipStream_t stream);
 
+/* Bytes of workspace cabf_bsa_backward needs (0 if the geometry is
+ * unsupported): fp32 D per row, a kept-list bitmap and the transposed lists
+ * (about B*heads*nb*nb*4 bytes). */
+size_t cabf_bsa_backward_workspace_bytes(const cabf_geom* g);
+
+/* Gradients of cabf_bsa_forward (NABLA summary, closing remarks: the sparse
+ * attention serves training as well as inference). With a scalar loss of the
+ * real output rows and dop = its gradient with respect to op: for a real
+ * query row n of block i and the real keys m of i's kept blocks,
+ *   P_nm = exp(scale q_n.k_m - lse_n), D_n = do_n . o_n,
+ *   dS_nm = P_nm (do_n . v_m - D_n),
+ *   dq_n = scale sum_m dS_nm k_m, dk_m = scale sum_n dS_nm q_n,
+ *   dv_m = sum_n P_nm do_n.
+ * Pad query rows do not contribute; pad rows of dq, dk, dv are zero.
+ * dtype: CABF_BF16 only (else CABF_EUNSUPPORTED). qp, kp, vp, op (the
+ * forward's output) and dop: [B, heads, N, head_dim] bf16; lse: the
+ * forward's [B, heads, N] fp32; kv_count / kv_index: the forward's lists
+ * (inputs). dqp, dkp, dvp: [B, heads, N, head_dim] bf16 (outputs).
+ * bf16 matrix products with fp32 accumulation; results are deterministic. */
+int cabf_bsa_backward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp,
+                      const void* vp, const void* op, const float* lse, const void* dop,
+                      const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
+                      void* dkp, void* dvp, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Semantic-permutation variant (Sparse VideoGen2 summary, Methodology A-C):
  * k-means clustering of Q and K, cluster-contiguous permutation, centroid

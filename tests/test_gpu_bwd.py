@@ -1,0 +1,129 @@
+"""GPU parity of the block-sparse attention backward (cabf_bsa_backward)
+against the oracle's gradients, through the C ABI.
+
+Tolerance: the gradients run through bf16 products (P, dS and the inputs
+rounded to bf16, fp32 accumulation), so their errors scale with the
+gradient's own magnitude: max |err| <= 2e-2 * max |ref| and mean |err| <=
+1e-2 * mean |ref| over the compared rows, per tensor.
+"""
+import numpy as np
+import pytest
+import torch
+
+import content_adaptive_block_fractal_amd as cabf
+import oracle
+from synth import WORKLOADS, fourier_video_qkv
+from tests.parity import say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+REL_MAX, REL_MEAN = 2e-2, 1e-2
+
+
+def compare_grad(got, ref, rows, label):
+    g = to_np(got)[rows]
+    r = np.asarray(ref)[rows]
+    err = np.abs(g - r)
+    scale_max, scale_mean = float(np.abs(r).max()), float(np.abs(r).mean())
+    say(f"{label}: max_err {err.max():.3e} (ref max {scale_max:.3e}), mean_err {err.mean():.3e} "
+        f"(ref mean {scale_mean:.3e})")
+    assert err.max() <= REL_MAX * scale_max + 1e-6
+    assert err.mean() <= REL_MEAN * scale_mean + 1e-7
+
+
+def setup(T, H, W, heads, d, thr, sta, seed=0, amp=0.7):
+    g = cabf.Geom(1, heads, d, T, H, W, 8)
+    og = oracle.Grid(T, H, W, 8)
+    q, k, v = fourier_video_qkv(T, H, W, heads, d, amp, seed=seed, dtype="bf16")
+    qp, kp, vp = cabf.permute(q.to(DEV), k.to(DEV), v.to(DEV), g)
+    s = cabf.default_scale(g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, thr, sta, s)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=True)
+    gen = torch.Generator(device=DEV).manual_seed(seed + 5)
+    dop = torch.randn(qp.shape, generator=gen, device=DEV).to(torch.bfloat16)   # pad rows too
+    return g, og, s, qp, kp, vp, cnt, idx, op, lse, dop
+
+
+CASES = [
+    ("ragged-d128", (3, 21, 35, 2, 128), 0.4, None),
+    ("ragged-d128-window", (3, 21, 35, 2, 128), 0.7, (1, 1, 1)),
+    ("ragged-d64", (5, 9, 17, 2, 64), 0.5, None),
+    ("wide-d128", (3, 24, 88, 2, 128), 0.8, None),
+    ("dense-d128", (2, 16, 16, 1, 128), 0.0, None),
+]
+
+
+@pytest.mark.parametrize("name,shape,thr,sta", CASES)
+def test_backward_matches_oracle(name, shape, thr, sta):
+    say(f"backward {name} thr={thr} sta={sta}")
+    g, og, s, qp, kp, vp, cnt, idx, op, lse, dop = setup(*shape, thr, sta)
+    dq, dk, dv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
+    dq2, dk2, dv2 = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))      # deterministic
+    valid = oracle.valid_slots(og)
+    for hd in range(g.heads):
+        ref = oracle.bsa_backward(to_np(qp[0, hd]), to_np(kp[0, hd]), to_np(vp[0, hd]),
+                                  to_np(dop[0, hd]), cnt[0, hd].cpu().numpy(),
+                                  idx[0, hd].cpu().numpy(), og, s)
+        for nm, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+            compare_grad(got[0, hd], r, valid, f"{name} head {hd} {nm}")
+            assert torch.all(got[0, hd][torch.from_numpy(~valid).to(DEV)] == 0)
+
+
+def test_backward_rows_without_blocks_and_unused_keys():
+    g, og, s, qp, kp, vp, cnt, idx, op, lse, dop = setup(3, 21, 35, 2, 128, 0.5, None, seed=3)
+    nb = og.nb
+    rng = np.random.default_rng(4)
+    mask = rng.random((1, g.heads, nb, nb)) < 0.25
+    mask[0, 0, 5] = False                  # a query block that keeps nothing
+    mask[0, 1, :, 7] = False               # a key block nobody keeps
+    cnt_np, idx_np = oracle.mask_to_lists(mask)
+    cnt, idx = torch.from_numpy(cnt_np).to(DEV), torch.from_numpy(idx_np).to(DEV)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=True)
+    dq, dk, dv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
+    torch.cuda.synchronize()
+    assert torch.all(dq[0, 0, 5 * 64:6 * 64] == 0)
+    assert torch.all(dk[0, 1, 7 * 64:8 * 64] == 0) and torch.all(dv[0, 1, 7 * 64:8 * 64] == 0)
+    valid = oracle.valid_slots(og)
+    for hd in range(g.heads):
+        ref = oracle.bsa_backward(to_np(qp[0, hd]), to_np(kp[0, hd]), to_np(vp[0, hd]),
+                                  to_np(dop[0, hd]), cnt_np[0, hd], idx_np[0, hd], og, s)
+        for nm, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+            compare_grad(got[0, hd], r, valid, f"arbitrary lists head {hd} {nm}")
+
+
+def test_backward_full_size_sampled():
+    """Wan-14B 720p at 80% sparsity: the gradients of two key blocks (every
+    query block that keeps them is included, so those rows are exact) and the
+    dq of those query blocks, head 0."""
+    w = WORKLOADS["wan14b-720p"]
+    g = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
+    og = oracle.Grid(w.T, w.H, w.W, w.P)
+    q, k, v = fourier_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, w.amplitude, seed=8,
+                                dtype=w.dtype, device=DEV)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    s = cabf.default_scale(g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, 0.7935, None, s)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True)
+    dop = torch.randn(qp.shape, generator=torch.Generator(device=DEV).manual_seed(9),
+                      device=DEV).to(torch.bfloat16)
+    dq, dk, dv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
+    torch.cuda.synchronize()
+    hd = 0
+    c0, i0 = cnt[0, hd].cpu().numpy(), idx[0, hd].cpu().numpy()
+    key_blocks = [0, og.nb - 1]
+    keeps = np.array([np.isin(key_blocks, i0[i][: c0[i]]).any() for i in range(og.nb)])
+    sub = np.where(keeps, c0, 0)
+    say(f"full-size backward: {int(keeps.sum())} query blocks keep key blocks {key_blocks}")
+    ref = oracle.bsa_backward(to_np(qp[0, hd]), to_np(kp[0, hd]), to_np(vp[0, hd]),
+                              to_np(dop[0, hd]), sub, i0, og, s)
+    valid = oracle.valid_slots(og)
+    krows = np.concatenate([np.arange(b * 64, (b + 1) * 64) for b in key_blocks])
+    krows = krows[valid[krows]]
+    qrows = np.concatenate([np.arange(b * 64, (b + 1) * 64) for b in np.nonzero(keeps)[0][:40]])
+    qrows = qrows[valid[qrows]]
+    compare_grad(dk[0, hd], ref[1], krows, "full-size dk")
+    compare_grad(dv[0, hd], ref[2], krows, "full-size dv")
+    compare_grad(dq[0, hd], ref[0], qrows, "full-size dq")
