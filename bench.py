@@ -81,8 +81,10 @@ def calibrate_thr(cabf, qp, kp, geom, target, sta, ws, kv_count, kv_index, iters
     return best[0]
 
 
-def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0, select="cdf", topk=0):
-    """n steps of the whole path; returns per-stage event times (ms) if timed."""
+def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0, select="cdf", topk=0, fused=False):
+    """n steps of the whole path; returns per-stage event times (ms) if timed.
+    fused: the reorder also pools the blocks (cabf_permute_pool) and the mask is
+    built from those means (cabf_build_block_mask_pooled)."""
     import torch
     q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
     scale = cabf.default_scale(geom)
@@ -91,10 +93,17 @@ def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0, select="cdf", topk=
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
         if timed:
             ev[0].record()
-        cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
+        if fused:
+            cabf.cabf_permute_pool(geom, q, k, v, qp, kp, vp, ws)
+        else:
+            cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
         if timed:
             ev[1].record()
-        if select == "cdf":
+        if fused:
+            cabf.cabf_build_block_mask_pooled(geom, scale, 0.0 if select == "topk" else thr,
+                                              topk if select == "topk" else 0, sta, cnt, idx,
+                                              None, ws)
+        elif select == "cdf":
             cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
         elif select == "topk":
             cabf.cabf_build_block_mask(geom, qp, kp, scale, 0.0, sta, cnt, idx, None, ws, topk=topk)
@@ -145,6 +154,36 @@ def profiled_traffic(workload: str):
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def measure_subset(cabf, geom, bufs, thr, sta, flags, steps: int, frac: float = 0.25):
+    """cabf_bsa_forward_subset over a seeded random quarter of the query blocks
+    (the active set), on the lists of the main run: time and tile rate."""
+    import numpy as np
+    import torch
+    q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
+    scale = cabf.default_scale(geom)
+    cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
+    cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
+    total = cnt.numel()
+    rng = np.random.default_rng(11)
+    ids = np.nonzero(rng.random(total) < frac)[0].astype(np.int32)
+    qb = torch.from_numpy(ids).to(qp.device)
+    kept = int(cnt.view(-1)[qb.long()].sum(dtype=torch.int64).item())
+    flops = 4.0 * 64 * 64 * geom.head_dim * kept
+    for _ in range(2):
+        cabf.cabf_bsa_forward_subset(geom, qp, kp, vp, cnt, idx, qb, scale, op, None, flags)
+    times = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cabf.cabf_bsa_forward_subset(geom, qp, kp, vp, cnt, idx, qb, scale, op, None, flags)
+        e1.record()
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = statistics.fmean(a.elapsed_time(b) for a, b in times)
+    return dict(active_blocks=int(ids.size), of_blocks=total, kept_tiles=kept, attention_ms=ms,
+                attention_tflops=flops / (ms * 1e-3) / 1e12)
 
 
 def measure_backward(cabf, geom, bufs, thr, sta, steps: int):
@@ -350,11 +389,11 @@ def main():
     ws = cabf.mask_workspace(geom, dev)
     bufs = (q, k, v, qp, kp, vp, op, o, cnt, idx, ws)
 
-    def measure(sparsity, sta, steps, warmup, flags, select="cdf", topk=0):
+    def measure(sparsity, sta, steps, warmup, flags, select="cdf", topk=0, fused=False):
         cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
         thr = (calibrate_thr(cabf, qp, kp, geom, sparsity, sta, ws, cnt, idx) if select == "cdf"
                else None)
-        kw = dict(flags=flags, select=select, topk=topk)
+        kw = dict(flags=flags, select=select, topk=topk, fused=fused)
         run_steps(cabf, geom, bufs, thr, sta, warmup, timed=False, **kw)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -456,7 +495,19 @@ def main():
                              attention_ms=a, mask_ms=r["stage_ms_mean"]["mask"],
                              attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
                              step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
+        # the fused reorder + pooling, then the mask from the pooled means
+        r = measure(args.sparsity, sta, max(3, args.steps // 4), 2, flags, fused=True)
+        a = r["stage_ms_mean"]["attention"]
+        var["fused permute+pool"] = dict(
+            thr=r["thr"], sparsity=r["sparsity"], ms_per_step=r["wall_ms"],
+            permute_pool_ms=r["stage_ms_mean"]["permute"], mask_ms=r["stage_ms_mean"]["mask"],
+            attention_ms=a, step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12,
+            unfused_permute_plus_mask_ms=main_run["stage_ms_mean"]["permute"]
+            + main_run["stage_ms_mean"]["mask"],
+            fused_permute_plus_mask_ms=r["stage_ms_mean"]["permute"] + r["stage_ms_mean"]["mask"])
         line["variants"] = var
+        line["active_query_subset"] = measure_subset(cabf, geom, bufs, main_run["thr"], sta,
+                                                     flags, max(3, args.steps // 4))
     if args.backward:
         line["backward"] = measure_backward(cabf, geom, bufs, main_run["thr"], sta,
                                             max(3, args.steps // 4))

@@ -25,9 +25,10 @@ LIB_PATH = os.environ.get("CABF_LIB") or os.path.join(_HERE, "libcabf.so")
 CABF_OK, CABF_EINVAL, CABF_EUNSUPPORTED, CABF_EWORKSPACE, CABF_EHIP = 0, -1, -2, -3, -4
 CABF_BF16, CABF_F32 = 0, 1
 
-EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_unpermute", "cabf_mask_workspace_bytes",
-            "cabf_build_block_mask", "cabf_build_block_mask_topk", "cabf_build_sta_mask",
-            "cabf_bsa_forward", "cabf_bsa_backward_workspace_bytes", "cabf_bsa_backward",
+EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_permute_pool", "cabf_unpermute",
+            "cabf_mask_workspace_bytes", "cabf_build_block_mask", "cabf_build_block_mask_topk",
+            "cabf_build_block_mask_pooled", "cabf_build_sta_mask", "cabf_bsa_forward",
+            "cabf_bsa_forward_subset", "cabf_bsa_backward_workspace_bytes", "cabf_bsa_backward",
             "cabf_kmeans_workspace_bytes", "cabf_kmeans", "cabf_gather_rows",
             "cabf_scatter_rows", "cabf_cluster_select_workspace_bytes", "cabf_cluster_select",
             "cabf_cluster_attention_workspace_bytes", "cabf_cluster_attention",
@@ -73,15 +74,20 @@ def _load():
                                            ctypes.POINTER(I32), ctypes.POINTER(I32),
                                            ctypes.POINTER(I32)]),
         "cabf_permute": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, P, P]),
+        "cabf_permute_pool": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, P, P, SZ, P]),
         "cabf_unpermute": (ctypes.c_int, [G, ctypes.c_int, P, P, P]),
         "cabf_mask_workspace_bytes": (SZ, [G]),
         "cabf_build_block_mask": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, F32,
                                                  ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
         "cabf_build_block_mask_topk": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, I32,
                                                       ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
+        "cabf_build_block_mask_pooled": (ctypes.c_int, [G, F32, F32, I32, ctypes.POINTER(_Sta),
+                                                        P, P, P, P, SZ, P]),
         "cabf_build_sta_mask": (ctypes.c_int, [G, ctypes.POINTER(_Sta), P, P, P]),
         "cabf_bsa_forward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, F32, P, P,
                                             ctypes.c_uint, P]),
+        "cabf_bsa_forward_subset": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, P, I64, F32, P,
+                                                   P, ctypes.c_uint, P]),
         "cabf_bsa_backward_workspace_bytes": (SZ, [G]),
         "cabf_bsa_backward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, P, P, P, F32, P, P, P,
                                              P, SZ, P]),
@@ -184,6 +190,21 @@ def cabf_permute(geom: Geom, q, k, v, qp, kp, vp):
     _check("cabf_permute", st)
 
 
+def cabf_permute_pool(geom: Geom, q, k, v, qp, kp, vp, workspace):
+    """cabf_permute that also leaves the fp32 block means of q and k in ``workspace``
+    (a mask workspace) for cabf_build_block_mask_pooled. v / vp may be None."""
+    s = geom.sizes()
+    rs = (geom.batch, geom.heads, s["tokens_raster"], geom.head_dim)
+    ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
+    dt = q.dtype
+    vv = (None, None) if v is None and vp is None else (_dev(v, rs, dt, "v"), _dev(vp, ps, dt, "vp"))
+    ptr, nbytes = _ws_ptr(workspace)
+    st = _lib.cabf_permute_pool(ctypes.byref(geom.c()), _dtype_code(q), _dev(q, rs, None, "q"),
+                                _dev(k, rs, dt, "k"), vv[0], _dev(qp, ps, dt, "qp"),
+                                _dev(kp, ps, dt, "kp"), vv[1], ptr, nbytes, _stream(q))
+    _check("cabf_permute_pool", st)
+
+
 def cabf_unpermute(geom: Geom, op, o):
     """Restore raster order: op [B, h, N, d] -> o [B, h, T*H*W, d]."""
     s = geom.sizes()
@@ -225,6 +246,26 @@ def cabf_build_block_mask(geom: Geom, qp, kp, scale: float, thr: float, sta, kv_
     _check("cabf_build_block_mask" if topk is None else "cabf_build_block_mask_topk", st)
 
 
+def cabf_build_block_mask_pooled(geom: Geom, scale: float, thr: float, k: int, sta, kv_count,
+                                 kv_index, block_prob, workspace):
+    """Block mask from the means cabf_permute_pool left in ``workspace``: the CDF cut at
+    thr (k = 0) or the top-k blocks per row (k >= 1)."""
+    nb = geom.sizes()["n_blocks"]
+    lead = (geom.batch, geom.heads, nb)
+    sta_c = None
+    if sta is not None:
+        sta_c = ctypes.byref(_Sta(1, int(sta[0]), int(sta[1]), int(sta[2])))
+    bp = None if block_prob is None else _dev(block_prob, lead + (nb,), torch.float32,
+                                              "block_prob")
+    ptr, nbytes = _ws_ptr(workspace)
+    st = _lib.cabf_build_block_mask_pooled(
+        ctypes.byref(geom.c()), float(scale), float(thr), int(k), sta_c,
+        _dev(kv_count, lead, torch.int32, "kv_count"),
+        _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), bp, ptr, nbytes,
+        _stream(kv_count))
+    _check("cabf_build_block_mask_pooled", st)
+
+
 def cabf_build_sta_mask(geom: Geom, sta, kv_count, kv_index):
     """Sliding-tile window lists alone into kv_count / kv_index (int32)."""
     nb = geom.sizes()["n_blocks"]
@@ -255,6 +296,28 @@ def cabf_bsa_forward(geom: Geom, qp, kp, vp, kv_count, kv_index, scale: float, o
         _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), float(scale),
         _dev(op, ps, qp.dtype, "op"), lp, int(flags), _stream(qp))
     _check("cabf_bsa_forward", st)
+
+
+def cabf_bsa_forward_subset(geom: Geom, qp, kp, vp, kv_count, kv_index, q_blocks, scale: float,
+                            op, lse=None, flags: int = 0):
+    """cabf_bsa_forward over the global query blocks in ``q_blocks`` (int32 device
+    tensor of (b*heads + h)*nb + i); other rows of op / lse are left untouched."""
+    s = geom.sizes()
+    nb = s["n_blocks"]
+    ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
+    lead = (geom.batch, geom.heads, nb)
+    lp = None if lse is None else _dev(lse, ps[:3], torch.float32, "lse")
+    if q_blocks.dtype != torch.int32 or q_blocks.dim() != 1:
+        raise ValueError("q_blocks must be a 1-D int32 tensor")
+    n = q_blocks.numel()
+    qb = _dev(q_blocks, (n,), torch.int32, "q_blocks") if n > 0 else None
+    st = _lib.cabf_bsa_forward_subset(
+        ctypes.byref(geom.c()), _dtype_code(qp), _dev(qp, ps, None, "qp"),
+        _dev(kp, ps, qp.dtype, "kp"), _dev(vp, ps, qp.dtype, "vp"),
+        _dev(kv_count, lead, torch.int32, "kv_count"),
+        _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), qb, n, float(scale),
+        _dev(op, ps, qp.dtype, "op"), lp, int(flags), _stream(qp))
+    _check("cabf_bsa_forward_subset", st)
 
 
 # --- allocating helpers -----------------------------------------------------------
@@ -298,6 +361,35 @@ def build_block_mask(qp, kp, geom: Geom, thr: float, sta=None, scale=None, retur
     return kv_count, kv_index
 
 
+def permute_pool(q, k, v, geom: Geom, workspace=None):
+    """(qp, kp, vp, workspace): the reordered tensors and a mask workspace holding the
+    block means, ready for build_block_mask_pooled."""
+    n = geom.sizes()["tokens_padded"]
+    shape = (geom.batch, geom.heads, n, geom.head_dim)
+    qp, kp = (torch.empty(shape, dtype=q.dtype, device=q.device) for _ in range(2))
+    vp = None if v is None else torch.empty(shape, dtype=q.dtype, device=q.device)
+    ws = mask_workspace(geom, q.device) if workspace is None else workspace
+    cabf_permute_pool(geom, q, k, v, qp, kp, vp, ws)
+    return qp, kp, vp, ws
+
+
+def build_block_mask_pooled(workspace, geom: Geom, thr: float, sta=None, scale=None,
+                            return_probs=False, topk=None, device=None):
+    """build_block_mask from the block means left by permute_pool."""
+    nb = geom.sizes()["n_blocks"]
+    lead = (geom.batch, geom.heads, nb)
+    dev = workspace.device if device is None else device
+    kv_count = torch.empty(lead, dtype=torch.int32, device=dev)
+    kv_index = torch.empty(lead + (nb,), dtype=torch.int32, device=dev)
+    probs = torch.empty(lead + (nb,), dtype=torch.float32, device=dev) if return_probs else None
+    cabf_build_block_mask_pooled(geom, default_scale(geom) if scale is None else scale,
+                                 0.0 if topk else thr, int(topk or 0), sta, kv_count, kv_index,
+                                 probs, workspace)
+    if return_probs:
+        return kv_count, kv_index, probs
+    return kv_count, kv_index
+
+
 def topk_for_ratio(geom: Geom, ratio: float) -> int:
     """Blocks kept per row for a static keep ratio: ceil(ratio * nb), at least 1."""
     nb = geom.sizes()["n_blocks"]
@@ -321,6 +413,15 @@ def bsa_forward(qp, kp, vp, kv_count, kv_index, geom: Geom, scale=None, return_l
                      default_scale(geom) if scale is None else scale, op, lse,
                      BSA_DETERMINISTIC if deterministic else 0)
     return (op, lse) if return_lse else op
+
+
+def bsa_forward_subset(qp, kp, vp, kv_count, kv_index, q_blocks, geom: Geom, op, lse=None,
+                       scale=None, deterministic=False):
+    """Fill the rows of the listed query blocks of op (and lse) in place."""
+    cabf_bsa_forward_subset(geom, qp, kp, vp, kv_count, kv_index, q_blocks,
+                            default_scale(geom) if scale is None else scale, op, lse,
+                            BSA_DETERMINISTIC if deterministic else 0)
+    return op
 
 
 def cabf_bsa_backward(geom: Geom, qp, kp, vp, op, lse, dop, kv_count, kv_index, scale: float,

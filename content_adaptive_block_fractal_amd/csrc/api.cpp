@@ -60,16 +60,17 @@ int launched() {
 }
 
 // Shared by the CDF (topk = 0) and the top-k entry points.
-int build_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp, float scale,
-               float thr, int topk, const cabf_sta* sta, int32_t* kv_count, int32_t* kv_index,
-               float* block_prob, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// pooled: the block means are already in the workspace (cabf_permute_pool),
+// qp, kp and dtype are unused
+int build_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp, bool pooled,
+               float scale, float thr, int topk, const cabf_sta* sta, int32_t* kv_count,
+               int32_t* kv_index, float* block_prob, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
   Geo geo;
   const int st = make_geo(g, &geo);
   if (st != CABF_OK) return st;
-  if (elem_bytes(dtype) == 0) return CABF_EINVAL;
-  if (qp == nullptr || kp == nullptr || kv_count == nullptr || kv_index == nullptr ||
-      workspace == nullptr)
-    return CABF_EINVAL;
+  if (!pooled && (elem_bytes(dtype) == 0 || qp == nullptr || kp == nullptr)) return CABF_EINVAL;
+  if (kv_count == nullptr || kv_index == nullptr || workspace == nullptr) return CABF_EINVAL;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
   if (!(thr >= 0.0f && thr <= 1.0f)) return CABF_EINVAL;
   if (reinterpret_cast<uintptr_t>(qp) % 16 || reinterpret_cast<uintptr_t>(kp) % 16 ||
@@ -87,9 +88,27 @@ int build_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void*
   }
   if (geo.nb > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
   if (workspace_bytes < cabf::mask_workspace_layout(geo).total) return CABF_EWORKSPACE;
-  cabf::launch_build_block_mask(geo, dtype == CABF_BF16, qp, kp, scale, thr, topk, sta_on, dt, dy,
-                                dx, kv_count, kv_index, block_prob, workspace, stream);
+  if (pooled)
+    cabf::launch_mask_from_pooled(geo, scale, thr, topk, sta_on, dt, dy, dx, kv_count, kv_index,
+                                  block_prob, workspace, stream);
+  else
+    cabf::launch_build_block_mask(geo, dtype == CABF_BF16, qp, kp, scale, thr, topk, sta_on, dt,
+                                  dy, dx, kv_count, kv_index, block_prob, workspace, stream);
   return launched();
+}
+
+// q, k, v, qp, kp, vp for the permute entries: CABF_OK or the status
+int check_pairs(const void* const src[3], void* const dst[3], int* pairs) {
+  *pairs = 0;
+  for (int i = 0; i < 3; ++i) {
+    if ((src[i] == nullptr) != (dst[i] == nullptr)) return CABF_EINVAL;
+    if (src[i] != nullptr) {
+      ++*pairs;
+      if (reinterpret_cast<uintptr_t>(src[i]) % 16 || reinterpret_cast<uintptr_t>(dst[i]) % 16)
+        return CABF_EINVAL;
+    }
+  }
+  return CABF_OK;
 }
 
 // cabf_seq -> (BH, n, D); CABF_OK or the status to return
@@ -133,16 +152,31 @@ int cabf_permute(const cabf_geom* g, cabf_dtype dtype, const void* q, const void
   const void* src[3] = {q, k, v};
   void* dst[3] = {qp, kp, vp};
   int pairs = 0;
-  for (int i = 0; i < 3; ++i) {
-    if ((src[i] == nullptr) != (dst[i] == nullptr)) return CABF_EINVAL;
-    if (src[i] != nullptr) {
-      ++pairs;
-      if (reinterpret_cast<uintptr_t>(src[i]) % 16 || reinterpret_cast<uintptr_t>(dst[i]) % 16)
-        return CABF_EINVAL;
-    }
-  }
+  if (check_pairs(src, dst, &pairs) != CABF_OK) return CABF_EINVAL;
   if (pairs == 0) return CABF_OK;
   cabf::launch_permute(geo, eb, src, dst, stream);
+  return launched();
+}
+
+int cabf_permute_pool(const cabf_geom* g, cabf_dtype dtype, const void* q, const void* k,
+                      const void* v, void* qp, void* kp, void* vp, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  Geo geo;
+  const int st = make_geo(g, &geo);
+  if (st != CABF_OK) return st;
+  const int eb = elem_bytes(dtype);
+  if (eb == 0 || q == nullptr || k == nullptr || workspace == nullptr) return CABF_EINVAL;
+  const void* src[3] = {q, k, v};
+  void* dst[3] = {qp, kp, vp};
+  int pairs = 0;
+  if (check_pairs(src, dst, &pairs) != CABF_OK) return CABF_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return CABF_EINVAL;
+  if (geo.nb > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
+  const cabf::MaskWorkspace lay = cabf::mask_workspace_layout(geo);
+  if (workspace_bytes < lay.total) return CABF_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  cabf::launch_permute_pool(geo, eb, src, dst, reinterpret_cast<float*>(ws + lay.qb_off),
+                            reinterpret_cast<float*>(ws + lay.kb_off), stream);
   return launched();
 }
 
@@ -169,7 +203,7 @@ int cabf_build_block_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, 
                           float scale, float thr, const cabf_sta* sta, int32_t* kv_count,
                           int32_t* kv_index, float* block_prob, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  return build_mask(g, dtype, qp, kp, scale, thr, 0, sta, kv_count, kv_index, block_prob,
+  return build_mask(g, dtype, qp, kp, false, scale, thr, 0, sta, kv_count, kv_index, block_prob,
                     workspace, workspace_bytes, stream);
 }
 
@@ -178,8 +212,17 @@ int cabf_build_block_mask_topk(const cabf_geom* g, cabf_dtype dtype, const void*
                                int32_t* kv_count, int32_t* kv_index, float* block_prob,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (k < 1) return CABF_EINVAL;
-  return build_mask(g, dtype, qp, kp, scale, 0.0f, k, sta, kv_count, kv_index, block_prob,
+  return build_mask(g, dtype, qp, kp, false, scale, 0.0f, k, sta, kv_count, kv_index, block_prob,
                     workspace, workspace_bytes, stream);
+}
+
+int cabf_build_block_mask_pooled(const cabf_geom* g, float scale, float thr, int32_t k,
+                                 const cabf_sta* sta, int32_t* kv_count, int32_t* kv_index,
+                                 float* block_prob, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (k < 0) return CABF_EINVAL;
+  return build_mask(g, CABF_BF16, nullptr, nullptr, true, scale, k > 0 ? 0.0f : thr, k, sta,
+                    kv_count, kv_index, block_prob, workspace, workspace_bytes, stream);
 }
 
 int cabf_build_sta_mask(const cabf_geom* g, const cabf_sta* sta, int32_t* kv_count,
@@ -215,6 +258,32 @@ int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const
     return CABF_EINVAL;
   cabf::launch_bsa_forward(geo, dtype == CABF_BF16, qp, kp, vp, kv_count, kv_index, scale, op,
                            lse, (flags & CABF_BSA_DETERMINISTIC) == 0, stream);
+  return launched();
+}
+
+int cabf_bsa_forward_subset(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp,
+                            const void* vp, const int32_t* kv_count, const int32_t* kv_index,
+                            const int32_t* q_blocks, int64_t n_blocks, float scale, void* op,
+                            float* lse, unsigned flags, hipStream_t stream) {
+  Geo geo;
+  const int st = make_geo(g, &geo);
+  if (st != CABF_OK) return st;
+  if (dtype != CABF_BF16) return elem_bytes(dtype) == 0 ? CABF_EINVAL : CABF_EUNSUPPORTED;
+  if (geo.BH * geo.nb > 0x7fffffff) return CABF_EUNSUPPORTED;   // int32 block ids
+  if (n_blocks < 0 || n_blocks > 0x7fffffff) return CABF_EINVAL;
+  if (qp == nullptr || kp == nullptr || vp == nullptr || kv_count == nullptr ||
+      kv_index == nullptr || op == nullptr || (q_blocks == nullptr && n_blocks > 0))
+    return CABF_EINVAL;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
+  if ((flags & ~static_cast<unsigned>(CABF_BSA_DETERMINISTIC)) != 0) return CABF_EINVAL;
+  if (reinterpret_cast<uintptr_t>(qp) % 16 || reinterpret_cast<uintptr_t>(kp) % 16 ||
+      reinterpret_cast<uintptr_t>(vp) % 16 || reinterpret_cast<uintptr_t>(op) % 16 ||
+      reinterpret_cast<uintptr_t>(kv_count) % 4 || reinterpret_cast<uintptr_t>(kv_index) % 4 ||
+      reinterpret_cast<uintptr_t>(lse) % 4 || reinterpret_cast<uintptr_t>(q_blocks) % 4)
+    return CABF_EINVAL;
+  if (n_blocks == 0) return CABF_OK;
+  cabf::launch_bsa_forward_subset(geo, qp, kp, vp, kv_count, kv_index, q_blocks, n_blocks, scale,
+                                  op, lse, (flags & CABF_BSA_DETERMINISTIC) == 0, stream);
   return launched();
 }
 

@@ -7,9 +7,10 @@
 
 namespace cabf {
 
-void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
-                        const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
-                        float* lse, bool phased, hipStream_t stream) {
+namespace {
+AttnArgs make_args(const Geo& g, const void* qp, const void* kp, const void* vp,
+                   const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
+                   float* lse) {
   AttnArgs a{};
   a.qp = qp;
   a.kp = kp;
@@ -26,10 +27,26 @@ void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp,
   a.W = g.W;
   a.N = g.N;
   a.BH = g.BH;
+  return a;
+}
+}  // namespace
+
+void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
+                        const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
+                        float* lse, bool phased, hipStream_t stream) {
+  const AttnArgs a = make_args(g, qp, kp, vp, kv_count, kv_index, scale, op, lse);
   if (bf16)
     launch_bsa_forward_mfma(a, g.D, phased, stream);   // bf16 matrix cores
   else
     launch_bsa_forward_simple(a, false, g.D, stream);  // always walks lists in order
+}
+
+void launch_bsa_forward_subset(const Geo& g, const void* qp, const void* kp, const void* vp,
+                               const int32_t* kv_count, const int32_t* kv_index,
+                               const int32_t* q_blocks, int64_t n_blocks, float scale, void* op,
+                               float* lse, bool phased, hipStream_t stream) {
+  const AttnArgs a = make_args(g, qp, kp, vp, kv_count, kv_index, scale, op, lse);
+  launch_bsa_forward_subset_mfma(a, g.D, phased, q_blocks, n_blocks, stream);
 }
 
 }  // namespace cabf

@@ -69,6 +69,9 @@ __device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16_rne(v
 
 void launch_bsa_forward_simple(const AttnArgs& a, bool bf16, int D, hipStream_t stream);
 void launch_bsa_forward_mfma(const AttnArgs& a, int D, bool phased, hipStream_t stream);
+// The bf16 forward over a list of n global query block ids only.
+void launch_bsa_forward_subset_mfma(const AttnArgs& a, int D, bool phased,
+                                    const int32_t* q_blocks, int64_t n, hipStream_t stream);
 // Variable-size cluster attention on the same kernel: a.N = rows per head of
 // the permuted (and padded) tensors; work items from the query-tile table.
 void launch_cluster_attention_mfma(const AttnArgs& a, int D, const int32_t* tiles, int max_tiles,

@@ -117,6 +117,20 @@ struct BlockListLayout {
   }
 };
 
+// A caller-given subset of query blocks (active queries: HSA summary, KV-cache
+// synchronisation, only the active tokens' queries attend, over the full K
+// and V): work item = entry of a list of global query block ids; entries
+// outside [0, B*h*nb) are skipped.
+struct SubsetLayout : BlockListLayout {
+  const int32_t* items;
+  int64_t total;
+  __device__ bool work(const AttnArgs& a, int64_t idx, WorkItem& w) const {
+    const int32_t it = items[idx];
+    if (it < 0 || it >= total) return false;
+    return BlockListLayout::work(a, it, w);
+  }
+};
+
 // Variable-size clusters (semantic-permutation path, Sparse VideoGen2
 // summary, Methodology C: contiguous query tokens, the key tokens of the
 // selected clusters): one work item per 64-row tile of a query cluster; list
@@ -446,6 +460,22 @@ void launch_bsa_forward_mfma(const AttnArgs& args, int D, bool phased, hipStream
   else
     hipLaunchKernelGGL((bsa_fwd_mfma<128, BlockListLayout>), dim3(grid), dim3(kThreads), 0, stream,
                        a, BlockListLayout{}, n);
+}
+
+void launch_bsa_forward_subset_mfma(const AttnArgs& args, int D, bool phased,
+                                    const int32_t* q_blocks, int64_t n, hipStream_t stream) {
+  AttnArgs a = args;
+  a.sweep_ticks = phased ? (D == 64 ? 90u : 150u) : 0u;
+  SubsetLayout lay{};
+  lay.items = q_blocks;
+  lay.total = a.BH * a.nb;
+  const unsigned grid = static_cast<unsigned>(n);
+  if (D == 64)
+    hipLaunchKernelGGL((bsa_fwd_mfma<64, SubsetLayout>), dim3(grid), dim3(kThreads), 0, stream, a,
+                       lay, n);
+  else
+    hipLaunchKernelGGL((bsa_fwd_mfma<128, SubsetLayout>), dim3(grid), dim3(kThreads), 0, stream, a,
+                       lay, n);
 }
 
 void launch_cluster_attention_mfma(const AttnArgs& a, int D, const int32_t* tiles, int max_tiles,

@@ -13,6 +13,9 @@ void launch_permute(const Geo& g, int elem_bytes, const void* const src[3], void
                     hipStream_t stream);
 // Inverse reorder of one tensor.
 void launch_unpermute(const Geo& g, int elem_bytes, const void* src, void* dst, hipStream_t stream);
+// permute that also writes the pooled means of src[0] (Q) and src[1] (K)
+void launch_permute_pool(const Geo& g, int elem_bytes, const void* const src[3],
+                         void* const dst[3], float* qb, float* kb, hipStream_t stream);
 
 // Mask workspace layout (bytes from the workspace base).
 struct MaskWorkspace {
@@ -26,6 +29,11 @@ void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void
                              float thr, int topk, bool sta_on, int dt, int dy, int dx,
                              int32_t* kv_count, int32_t* kv_index, float* block_prob,
                              void* workspace, hipStream_t stream);
+
+// logits, selection and compaction from pooled means already in the workspace
+void launch_mask_from_pooled(const Geo& g, float scale, float thr, int topk, bool sta_on, int dt,
+                             int dy, int dx, int32_t* kv_count, int32_t* kv_index,
+                             float* block_prob, void* workspace, hipStream_t stream);
 
 void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_count,
                            int32_t* kv_index, hipStream_t stream);
@@ -45,5 +53,11 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
 void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,
                         float* lse, bool phased, hipStream_t stream);
+// bf16 forward over the listed global query blocks (b*heads*nb + h*nb + block)
+// only; entries outside that range are skipped
+void launch_bsa_forward_subset(const Geo& g, const void* qp, const void* kp, const void* vp,
+                               const int32_t* kv_count, const int32_t* kv_index,
+                               const int32_t* q_blocks, int64_t n_blocks, float scale, void* op,
+                               float* lse, bool phased, hipStream_t stream);
 
 }  // namespace cabf

@@ -465,7 +465,6 @@ void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void
   char* ws = static_cast<char*>(workspace);
   float* qb = reinterpret_cast<float*>(ws + w.qb_off);
   float* kb = reinterpret_cast<float*>(ws + w.kb_off);
-  float* z = reinterpret_cast<float*>(ws + w.z_off);
   const int64_t blocks_total = g.BH * g.nb;
 
   const dim3 pool_grid(static_cast<unsigned>((blocks_total + 3) / 4), 2);
@@ -479,7 +478,19 @@ void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void
     if (g.D == 64) CABF_POOL(float, 64); else CABF_POOL(float, 128);
   }
 #undef CABF_POOL
+  launch_mask_from_pooled(g, scale, thr, topk, sta_on, dt, dy, dx, kv_count, kv_index, block_prob,
+                          workspace, stream);
+}
 
+void launch_mask_from_pooled(const Geo& g, float scale, float thr, int topk, bool sta_on, int dt,
+                             int dy, int dx, int32_t* kv_count, int32_t* kv_index,
+                             float* block_prob, void* workspace, hipStream_t stream) {
+  const MaskWorkspace w = mask_workspace_layout(g);
+  char* ws = static_cast<char*>(workspace);
+  const float* qb = reinterpret_cast<const float*>(ws + w.qb_off);
+  const float* kb = reinterpret_cast<const float*>(ws + w.kb_off);
+  float* z = reinterpret_cast<float*>(ws + w.z_off);
+  const int64_t blocks_total = g.BH * g.nb;
   const int tps = (g.nb + kTile - 1) / kTile;
   const unsigned lg_grid = static_cast<unsigned>(g.BH * tps * tps);
   if (g.D == 64)

@@ -97,6 +97,22 @@ int cabf_permute(const cabf_geom* g, cabf_dtype dtype,
                  const void* q, const void* k, const void* v,
                  void* qp, void* kp, void* vp, hipStream_t stream);
 
+/* cabf_permute fused with step 1 of cabf_build_block_mask (NABLA summary,
+ * Methodology items 1-2: the reordered Q and K are pooled per 64-token block;
+ * doing both in one pass reads Q and K once instead of twice). Writes qp,
+ * kp, vp exactly as cabf_permute does and, into `workspace`, the fp32 means
+ * Qb, Kb of the real tokens of every block, for cabf_build_block_mask_pooled.
+ * q, k, qp, kp are required; v and vp may both be NULL. workspace: at least
+ * cabf_mask_workspace_bytes(g) bytes, 256-byte aligned, the same buffer then
+ * handed to cabf_build_block_mask_pooled on the same stream, untouched in
+ * between. Supports nb <= 8192 (else CABF_EUNSUPPORTED). The means are summed
+ * in a fixed order, so they are bit-identical from run to run but may differ
+ * in the last bits from the ones cabf_build_block_mask computes. */
+int cabf_permute_pool(const cabf_geom* g, cabf_dtype dtype,
+                      const void* q, const void* k, const void* v,
+                      void* qp, void* kp, void* vp, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* Inverse of cabf_permute for the attention output (Sparse VideoGen2
  * summary, section 2A: undoing the token permutation restores the original
  * order). op: reordered [B, heads, N, head_dim] (input); o: raster
@@ -146,6 +162,15 @@ int cabf_build_block_mask_topk(const cabf_geom* g, cabf_dtype dtype,
                                float* block_prob, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Steps 2-5 of cabf_build_block_mask (k = 0: the CDF cut at thr) or of
+ * cabf_build_block_mask_topk (k >= 1), from the block means that
+ * cabf_permute_pool left in `workspace` (the same buffer, same geometry).
+ * k < 0 is CABF_EINVAL. Outputs and limits as for cabf_build_block_mask. */
+int cabf_build_block_mask_pooled(const cabf_geom* g, float scale, float thr, int32_t k,
+                                 const cabf_sta* sta, int32_t* kv_count, int32_t* kv_index,
+                                 float* block_prob, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* Pure sliding-tile block lists (NABLA summary, comparison with static
  * methods: the STA-only configuration), with no content scores: row i keeps
  * exactly the window of cabf_build_block_mask step 4, ascending.
@@ -180,6 +205,24 @@ int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype,
                      const void* qp, const void* kp, const void* vp,
                      const int32_t* kv_count, const int32_t* kv_index, float scale,
                      void* op, float* lse, unsigned flags, hipStream_t stream);
+
+/* cabf_bsa_forward restricted to a set of query blocks (HSA summary,
+ * section 2.2, KV-cache synchronisation: only the active tokens' queries are
+ * computed, each attending over all of K and V; here the active set is given
+ * at block granularity, and each active block attends over its kept list).
+ * q_blocks: [n_blocks] int32 global block ids g = (b*heads + h)*nb + i
+ * (device); the rows of those blocks of op (and lse) are written exactly as
+ * cabf_bsa_forward writes them, with the same flags; every other row is left
+ * untouched. Ids outside [0, B*heads*nb) are skipped; a repeated id writes
+ * the same rows twice (identical values under CABF_BSA_DETERMINISTIC).
+ * n_blocks = 0 is a no-op. dtype: CABF_BF16 only (else CABF_EUNSUPPORTED);
+ * B*heads*nb must fit in int32 (else CABF_EUNSUPPORTED). Other arguments as
+ * for cabf_bsa_forward. */
+int cabf_bsa_forward_subset(const cabf_geom* g, cabf_dtype dtype,
+                            const void* qp, const void* kp, const void* vp,
+                            const int32_t* kv_count, const int32_t* kv_index,
+                            const int32_t* q_blocks, int64_t n_blocks, float scale,
+                            void* op, float* lse, unsigned flags, hipStream_t stream);
 
 /* Bytes of workspace cabf_bsa_backward needs (0 if the geometry is
  * unsupported): fp32 D per row, a kept-list bitmap and the transposed lists

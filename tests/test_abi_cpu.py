@@ -219,3 +219,48 @@ def test_attention_argument_checks():
     assert call(dt=2) == cabf.CABF_EINVAL
     assert call(flags=2) == cabf.CABF_EINVAL
     assert call(flags=cabf.BSA_DETERMINISTIC | 4) == cabf.CABF_EINVAL
+
+
+@no_gpu
+def test_fused_entry_argument_checks():
+    g = geom()
+    need = L.cabf_mask_workspace_bytes(g)
+    ws = ctypes.c_void_p(0x300000)
+    def pp(**kw):
+        a = dict(dt=0, q=DUMMY, k=DUMMY, v=NULL, qp=DUMMY2, kp=DUMMY2, vp=NULL, ws=ws, wsb=need)
+        a.update(kw)
+        return L.cabf_permute_pool(g, a["dt"], a["q"], a["k"], a["v"], a["qp"], a["kp"], a["vp"],
+                                   a["ws"], a["wsb"], NULL)
+    assert pp(q=NULL, qp=NULL) == cabf.CABF_EINVAL          # q and k are required
+    assert pp(k=NULL, kp=NULL) == cabf.CABF_EINVAL
+    assert pp(v=DUMMY) == cabf.CABF_EINVAL                  # v without vp
+    assert pp(ws=NULL) == cabf.CABF_EINVAL
+    assert pp(ws=ctypes.c_void_p(0x300040)) == cabf.CABF_EINVAL
+    assert pp(wsb=need - 1) == cabf.CABF_EWORKSPACE
+    assert pp(dt=4) == cabf.CABF_EINVAL
+    assert L.cabf_permute_pool(geom(T=129, H=64, W=64), 0, DUMMY, DUMMY, NULL, DUMMY2, DUMMY2, NULL,
+                               ws, 1 << 40, NULL) == cabf.CABF_EUNSUPPORTED
+    def mp(**kw):
+        a = dict(scale=0.125, thr=0.2, k=0, cnt=DUMMY2, ws=ws, wsb=need)
+        a.update(kw)
+        return L.cabf_build_block_mask_pooled(g, a["scale"], a["thr"], a["k"], None, a["cnt"],
+                                              DUMMY2, None, a["ws"], a["wsb"], NULL)
+    assert mp(k=-1) == cabf.CABF_EINVAL
+    assert mp(thr=1.2) == cabf.CABF_EINVAL
+    assert mp(scale=0.0) == cabf.CABF_EINVAL
+    assert mp(cnt=NULL) == cabf.CABF_EINVAL
+    assert mp(wsb=need - 1) == cabf.CABF_EWORKSPACE
+    def sub(**kw):
+        a = dict(dt=0, qb=DUMMY2, n=4, scale=0.125, flags=0, op=DUMMY2)
+        a.update(kw)
+        return L.cabf_bsa_forward_subset(g, a["dt"], DUMMY, DUMMY, DUMMY, DUMMY2, DUMMY2, a["qb"],
+                                         a["n"], a["scale"], a["op"], None, a["flags"], NULL)
+    assert sub(dt=1) == cabf.CABF_EUNSUPPORTED
+    assert sub(dt=3) == cabf.CABF_EINVAL
+    assert sub(n=-1) == cabf.CABF_EINVAL
+    assert sub(qb=NULL) == cabf.CABF_EINVAL
+    assert sub(qb=NULL, n=0) == cabf.CABF_OK                # nothing to do
+    assert sub(qb=ctypes.c_void_p(0x200002)) == cabf.CABF_EINVAL
+    assert sub(op=NULL) == cabf.CABF_EINVAL
+    assert sub(flags=8) == cabf.CABF_EINVAL
+    assert sub(scale=float("nan")) == cabf.CABF_EINVAL
