@@ -130,7 +130,7 @@ def kernel_source_digest() -> str:
     """sha256 of the attention kernel's sources (ties a counter profile to a kernel version)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("attention_mfma.hip", "attention_common.hpp", "geometry.hpp"):
+    for f in ("attention_mfma.hip", "attention_common.hpp", "attention_tiles.hpp", "geometry.hpp"):
         with open(os.path.join(ROOT, "content_adaptive_block_fractal_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

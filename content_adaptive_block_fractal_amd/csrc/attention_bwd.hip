@@ -21,7 +21,8 @@
 //                  dO^T, Q^T from transposing LDS reads
 // Both gradient kernels split the 64 x 64 tile over 4 waves (two halves of
 // each side) and add the two partial sums of a row once at the end, so every
-// result is deterministic. Pad query rows do not contribute and get dq = 0;
+// result is deterministic. bwd_dq fits two workgroups per CU (<= 256 VGPRs);
+// bwd_dkdv holds K, V and two accumulators per lane and runs one. Pad query rows do not contribute and get dq = 0;
 // pad key rows get dk = dv = 0.
 #include <hip/hip_runtime.h>
 
@@ -117,7 +118,7 @@ __device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, 
 // wk of every tile; lane holds query row li of its half (as in the forward).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq(AttnArgs a, const uint16_t* __restrict__ dop,
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t* __restrict__ dop,
                                                       const float* __restrict__ delta,
                                                       uint16_t* __restrict__ dqp, int64_t n_items) {
   using S = Stage<D>;

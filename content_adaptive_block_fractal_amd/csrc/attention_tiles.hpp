@@ -101,10 +101,17 @@ template <int D>
 __device__ __forceinline__ void issue_tile_load(const uint16_t* __restrict__ tile_src, u32x4* slot,
                                                 uint32_t off, int wave) {
   using S = Stage<D>;
+  // An empty asm makes each load's scalar base (tile and pass) and lane
+  // offset opaque, so the compiler cannot fold (base + lane offset) once and
+  // rebuild every other address with 64-bit vector adds: the base stays in
+  // SGPRs and the 32-bit offset in a VGPR (the saddr + voffset form).
+  uint32_t o = off;
+  asm volatile("" : "+v"(o));
 #pragma unroll
   for (int i = 0; i < S::kIters; ++i) {
     const char* base = reinterpret_cast<const char*>(tile_src + i * S::kRowsPerIter * D);
-    __builtin_amdgcn_global_load_lds(base + off, slot + (i * kWaves + wave) * 64, 16, 0, 0);
+    asm volatile("" : "+s"(base));
+    __builtin_amdgcn_global_load_lds(base + o, slot + (i * kWaves + wave) * 64, 16, 0, 0);
   }
 }
 
