@@ -15,14 +15,17 @@
 //                  dQ^T += K^T dS^T with K^T from transposing LDS reads
 //   bwd_transpose  the kept lists turned around: for every key block, the
 //                  query blocks that keep it, ascending (through a bitmap)
-//   bwd_dkdv       one workgroup per key block over those query blocks:
-//                  S = Q K^T and dP = dO V^T (Q, dO rows from LDS; K, V in
-//                  registers), then dV^T += dO^T P and dK^T += Q^T dS with
-//                  dO^T, Q^T from transposing LDS reads
-// Both gradient kernels split the 64 x 64 tile over 4 waves (two halves of
-// each side) and add the two partial sums of a row once at the end, so every
-// result is deterministic. bwd_dq fits two workgroups per CU (<= 256 VGPRs);
-// bwd_dkdv holds K, V and two accumulators per lane and runs one. Pad query rows do not contribute and get dq = 0;
+//   bwd_dkdv<DK>   one workgroup per key block over those query blocks, in
+//                  two passes: DK = false: S = Q K^T, then dV^T += dO^T P;
+//                  DK = true: S = Q K^T and dP = dO V^T, then dK^T += Q^T dS
+//                  (Q, dO rows from LDS; K, V in registers; dO^T, Q^T from
+//                  transposing LDS reads). One pass computing both would hold
+//                  K, V and both accumulators per lane (over 256 registers,
+//                  one workgroup per CU); split, each pass runs two per CU,
+//                  which outweighs recomputing S in the second.
+// Every gradient kernel splits the 64 x 64 tile over 4 waves (two halves of
+// each side) and adds the two partial sums of a row once at the end, so every
+// result is deterministic. Pad query rows do not contribute and get dq = 0;
 // pad key rows get dk = dv = 0.
 #include <hip/hip_runtime.h>
 
@@ -308,18 +311,18 @@ __global__ __launch_bounds__(256) void bwd_transpose(const uint32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per key block. Wave (wk, wq): key half wk, query half
-// wq of every tile; lane holds key li of its half. S = Q K^T and dP = dO V^T
-// give each lane one key column and 16 query rows, which serve as the B
-// operand (contraction over queries) of dV^T += dO^T P and dK^T += Q^T dS.
+// dV (DK = false) or dK (DK = true): one workgroup per key block. Wave
+// (wk, wq): key half wk, query half wq of every tile; lane holds key li of
+// its half. S = Q K^T (and dP = dO V^T) give each lane one key column and 16
+// query rows, which serve as the B operand (contraction over queries) of
+// dV^T += dO^T P, or dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(AttnArgs a, const uint16_t* __restrict__ dop,
+template <int D, bool DK>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16_t* __restrict__ dop,
                                                         const float* __restrict__ delta,
                                                         const int32_t* __restrict__ q_count,
                                                         const int32_t* __restrict__ q_index,
-                                                        uint16_t* __restrict__ dkp,
-                                                        uint16_t* __restrict__ dvp, int64_t n_items) {
+                                                        uint16_t* __restrict__ grad, int64_t n_items) {
   using S = Stage<D>;
   constexpr int kKS = D / 16;
   constexpr int kDT = D / 32;
@@ -341,21 +344,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(AttnArgs a, const uint16
   const int64_t krow = item * kBlock + wk * 32 + li;        // global key row of this lane
   const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(a.kp);
   const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(a.vp);
-  bf16x8 kf[kKS], vf[kKS];
+  bf16x8 kf[kKS], vf[DK ? kKS : 1];
 #pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
+  for (int ks = 0; ks < kKS; ++ks)
     kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + krow * D + 16 * ks + 8 * h));
-    vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
+  if constexpr (DK) {
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
   }
   const float c = a.scale_log2;
-  f32x16 dk[kDT], dv[kDT];
+  f32x16 acc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[dt][r] = 0.0f;
-      dv[dt][r] = 0.0f;
-    }
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
 
   const int cnt = min(max(q_count[item], 0), a.nb);
   const int32_t* __restrict__ list = q_index + item * a.nb;
@@ -377,43 +380,49 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(AttnArgs a, const uint16
   };
   auto step = [&](int ib, const u32x4* qs, const u32x4* ds, const float (&vec)[2][kBlock]) {
     const f32x16 s = rows_times(qs, kf);
-    const f32x16 dp = rows_times(ds, vf);
+    f32x16 dp;
+    if constexpr (DK) dp = rows_times(ds, vf);
     const BlockExtent ext = block_extent(ib, a);
     const uint32_t bits = ext.full() ? 0xffffu : real_row_bits(ext, wq, h);
-    bf16x8 pb[2], dsb[2];
+    bf16x8 wb[2];      // P (dV pass) or dS (dK pass), bf16
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int m = row0 + 8 * g + 4 * h;                  // rows m .. m + 3
       const float4 l4 = *reinterpret_cast<const float4*>(&vec[0][m]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&vec[1][m]);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      float dv4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (DK) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&vec[1][m]);
+        dv4[0] = d4.x;
+        dv4[1] = d4.y;
+        dv4[2] = d4.z;
+        dv4[3] = d4.w;
+      }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * g + x;
         const float p = ((bits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x])) : 0.0f;
-        pb[r >> 3][r & 7] = static_cast<__bf16>(p);
-        dsb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dv4[x]));
+        if constexpr (DK)
+          wb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dv4[x]));
+        else
+          wb[r >> 3][r & 7] = static_cast<__bf16>(p);
       }
     }
-    const uint16_t* qt = reinterpret_cast<const uint16_t*>(qs);
-    const uint16_t* dt_ = reinterpret_cast<const uint16_t*>(ds);
+    // dV^T += dO^T P, or dK^T += Q^T dS
+    const uint16_t* xt = reinterpret_cast<const uint16_t*>(DK ? qs : ds);
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            transposed_fragment(dt_, toff[dt][st][0], toff[dt][st][1]), pb[st], dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            transposed_fragment(qt, toff[dt][st][0], toff[dt][st][1]), dsb[st], dk[dt], 0, 0, 0);
-      }
+      for (int st = 0; st < 2; ++st)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            transposed_fragment(xt, toff[dt][st][0], toff[dt][st][1]), wb[st], acc[dt], 0, 0, 0);
   };
   // lse (base 2, +inf for rows without keys) and D of query block ib -> vec slot
   auto load_vecs = [&](int ib, float (&vec)[2][kBlock]) {
     if (tid < kBlock) {
       const float l = lse_h[static_cast<int64_t>(ib) * kBlock + tid];
       vec[0][tid] = l == -INFINITY ? INFINITY : l * kLog2e;
-      vec[1][tid] = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
+      if constexpr (DK) vec[1][tid] = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
     }
   };
 
@@ -449,43 +458,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(AttnArgs a, const uint16
   }
 
   // ---- add the two query halves, scale dK, store (pad keys: 0) -------------
-  float* const pk = reinterpret_cast<float*>(wk ? q_slot1 : q_slot0);
-  float* const pv = reinterpret_cast<float*>(wk ? d_slot1 : d_slot0);
+  float* const part = reinterpret_cast<float*>(wk ? q_slot1 : q_slot0);
   static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
   if (wq == 1) {
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pk[(dt * 16 + r) * 64 + lane] = dk[dt][r];
-        pv[(dt * 16 + r) * 64 + lane] = dv[dt][r];
-      }
+      for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * 64 + lane] = acc[dt][r];
   }
   __syncthreads();
   if (wq == 1) return;
   const BlockExtent kext = block_extent(static_cast<int>(item % a.nb), a);
   const bool real_key = kext.real(wk * 32 + li);
-  const float sk = real_key ? a.scale_log2 * kLn2 : 0.0f;   // dK carries the softmax scale s
-  const float sv = real_key ? 1.0f : 0.0f;
+  // dK carries the softmax scale s; pad keys get 0
+  const float sc = real_key ? (DK ? a.scale_log2 * kLn2 : 1.0f) : 0.0f;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * dt + 8 * g + 4 * h;
-      float xk[4], xv[4];
+      float x[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 4 * g + x;
-        xk[x] = (dk[dt][r] + pk[(dt * 16 + r) * 64 + lane]) * sk;
-        xv[x] = (dv[dt][r] + pv[(dt * 16 + r) * 64 + lane]) * sv;
+      for (int xx = 0; xx < 4; ++xx) {
+        const int r = 4 * g + xx;
+        x[xx] = (acc[dt][r] + part[(dt * 16 + r) * 64 + lane]) * sc;
       }
-      uint2 wkp, wvp;
-      wkp.x = static_cast<uint32_t>(f32_to_bf16_rne(xk[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(xk[1])) << 16);
-      wkp.y = static_cast<uint32_t>(f32_to_bf16_rne(xk[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(xk[3])) << 16);
-      wvp.x = static_cast<uint32_t>(f32_to_bf16_rne(xv[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(xv[1])) << 16);
-      wvp.y = static_cast<uint32_t>(f32_to_bf16_rne(xv[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(xv[3])) << 16);
-      *reinterpret_cast<uint2*>(dkp + krow * D + d) = wkp;
-      *reinterpret_cast<uint2*>(dvp + krow * D + d) = wvp;
+      uint2 w;
+      w.x = static_cast<uint32_t>(f32_to_bf16_rne(x[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[1])) << 16);
+      w.y = static_cast<uint32_t>(f32_to_bf16_rne(x[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16);
+      *reinterpret_cast<uint2*>(grad + krow * D + d) = w;
     }
 }
 
@@ -554,12 +555,16 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   uint16_t* dv16 = static_cast<uint16_t*>(dvp);
   if (g.D == 64) {
     hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, dq16, items);
-    hipLaunchKernelGGL((bwd_dkdv<64>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, q_count,
-                       q_index, dk16, dv16, items);
+    hipLaunchKernelGGL((bwd_dkdv<64, false>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
+                       q_count, q_index, dv16, items);
+    hipLaunchKernelGGL((bwd_dkdv<64, true>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
+                       q_count, q_index, dk16, items);
   } else {
     hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, dq16, items);
-    hipLaunchKernelGGL((bwd_dkdv<128>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, q_count,
-                       q_index, dk16, dv16, items);
+    hipLaunchKernelGGL((bwd_dkdv<128, false>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
+                       q_count, q_index, dv16, items);
+    hipLaunchKernelGGL((bwd_dkdv<128, true>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
+                       q_count, q_index, dk16, items);
   }
 }
 
