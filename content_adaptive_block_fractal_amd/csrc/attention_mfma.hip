@@ -53,7 +53,17 @@ namespace cabf {
 namespace {
 
 using namespace tiles;
-constexpr float kRescaleSlack = 8.0f;   // base-2 headroom before the running max is raised
+constexpr float kRescaleSlack = 8.0f;
+
+// s_waitcnt immediate: vmcnt = the loads of one tile copy (Stage::kIters),
+// expcnt and lgkmcnt not waited on (gfx9 encoding: vmcnt[3:0] and [15:14],
+// expcnt[6:4], lgkmcnt[11:8])
+template <int D>
+constexpr int kWaitAllButOneTile() {
+  constexpr int n = Stage<D>::kIters;
+  static_assert(n < 64, "vmcnt range");
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}   // base-2 headroom before the running max is raised
 
 // A list entry decoded: element offset of its 64 K/V rows in the head, and
 // what the layout needs to mask it (block index, or number of valid keys).
@@ -183,9 +193,14 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   constexpr int kDT = D / 32;   // 32-row d subtiles of O^T
   // Ring slots are separate LDS objects so that the compiler can tell the
   // tile being read from the tiles still streaming in (no wait on them).
+  // K has two slots, V three: V of tile e+2 may still be in flight when tile
+  // e+1 starts. Five 16 KB slots (d = 128) leave room for two workgroups per
+  // CU; the start position and the merge scalars borrow the third V slot
+  // when no tile is in it.
   __shared__ u32x4 k_slot0[S::kTile], k_slot1[S::kTile];
-  __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile];
-  __shared__ float merge_ml[2 * 2 * 64];
+  __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile], v_slot2[S::kTile];
+  float* const merge_ml = reinterpret_cast<float*>(v_slot0);   // [2 * 2 * 64]
+  int* const start_shared = reinterpret_cast<int*>(v_slot2);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -231,7 +246,6 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   // P = sweep_ticks * the mean list length of 64 rows spread evenly over the
   // head, which all of them sample alike. Wave 0 computes the start and
   // shares it through LDS, so that all waves agree on it.
-  __shared__ int start_shared;
   if (wave == 0) {
     int start = 0;
     if (L::kPhased && a.sweep_ticks != 0 && cnt > 1) {
@@ -244,10 +258,10 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
       const uint32_t now = static_cast<uint32_t>(__builtin_amdgcn_s_memrealtime());
       start = static_cast<int>(static_cast<uint64_t>(now % period) * cnt / period);
     }
-    if (lane == 0) start_shared = start;
+    if (lane == 0) *start_shared = start;
   }
   __syncthreads();
-  const int start = __builtin_amdgcn_readfirstlane(start_shared);
+  const int start = __builtin_amdgcn_readfirstlane(*start_shared);
   // Entries of the pass are fetched 64 at a time, one per lane, a batch ahead
   // of use, and read out with readlane: no list load is waited on per tile.
   // Entry t of the pass is list entry start + t (wrapped); t is clamped to the
@@ -297,9 +311,11 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
     const TileRef t0 = tile(0);
+    const TileRef t1 = tile(1);
     issue_tile_load<D>(K + t0.off, k_slot0, koff, wave);
     issue_tile_load<D>(V + t0.off, v_slot0, voff, wave);
-    issue_tile_load<D>(K + tile(1).off, k_slot1, koff, wave);
+    issue_tile_load<D>(K + t1.off, k_slot1, koff, wave);
+    issue_tile_load<D>(V + t1.off, v_slot1, voff, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur = scores(k_slot0);
@@ -307,21 +323,21 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     TileRef t_next = tile(1);
     __syncthreads();            // tile 0's K slot is refilled next
 
-    // tile e: K of e+1 is in k_slot[(e+1)%2], V of e in v_slot[e%2]; K of e+2
-    // streams into k_slot[e%2] and V of e+1 into v_slot[(e+1)%2]
-    auto body = [&](int e, auto parity) {
+    // tile e: K of e+1 is in k_slot[(e+1)%2], V of e in v_slot[e%3], V of e+1
+    // in v_slot[(e+1)%3] or still arriving; K and V of e+2 stream into
+    // k_slot[e%2] and v_slot[(e+2)%3]
+    auto body = [&](int e, auto parity, auto phase) {
       constexpr int kOdd = decltype(parity)::value;
+      constexpr int kPh = decltype(phase)::value;
       u32x4* const k_here = kOdd ? k_slot1 : k_slot0;    // slot e % 2
       u32x4* const k_next = kOdd ? k_slot0 : k_slot1;    // slot (e + 1) % 2
-      u32x4* const v_here = kOdd ? v_slot1 : v_slot0;
-      u32x4* const v_next = kOdd ? v_slot0 : v_slot1;
+      u32x4* const v_here = kPh == 0 ? v_slot0 : (kPh == 1 ? v_slot1 : v_slot2);   // e % 3
+      u32x4* const v_fill = kPh == 0 ? v_slot2 : (kPh == 1 ? v_slot0 : v_slot1);   // (e + 2) % 3
       if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
         batch_cur = batch_nxt;
         batch_nxt = load_batch(((e + 2) >> 6) + 1);
       }
       const TileRef t2 = tile(e + 2);
-      issue_tile_load<D>(K + t2.off, k_here, koff, wave);
-      issue_tile_load<D>(V + t_next.off, v_next, voff, wave);
 
       // V^T fragments of tile e (16 transposing reads)
       bf16x8 vf[kDT][2];
@@ -343,6 +359,12 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
       // latency hides behind the matrix work and the softmax.
       const f32x16 s_nxt = scores(k_next);
       read_v();
+      __builtin_amdgcn_sched_barrier(0);
+      // The copies of tile e+2 are issued after this tile's LDS reads: the
+      // compiler tracks only a few LDS copies in flight, and reads issued
+      // behind more of them would wait for all of them.
+      issue_tile_load<D>(K + t2.off, k_here, koff, wave);
+      issue_tile_load<D>(V + t2.off, v_fill, voff, wave);
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax of tile e ------------------------------------------------
@@ -389,14 +411,28 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
       s_cur = s_nxt;
       t_cur = t_next;
       t_next = t2;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      // Every load but the newest tile copy (V of e+2) has landed: K of e+2
+      // and V of e+1 are in LDS for every wave after the barrier. The empty
+      // asm statements keep the compiler from moving LDS accesses across it.
+      __builtin_amdgcn_s_waitcnt(kWaitAllButOneTile<D>());
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     };
-    for (int e = 0; e < cnt; e += 2) {
-      body(e, std::integral_constant<int, 0>{});
-      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int e = 0; e < cnt; e += 6) {
+      body(e, I0{}, I0{});
+      if (e + 1 < cnt) body(e + 1, I1{}, I1{});
+      if (e + 2 < cnt) body(e + 2, I0{}, I2{});
+      if (e + 3 < cnt) body(e + 3, I1{}, I0{});
+      if (e + 4 < cnt) body(e + 4, I0{}, I1{});
+      if (e + 5 < cnt) body(e + 5, I1{}, I2{});
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);    // the last tile copies land before the slots are reused
+  __syncthreads();
 
   // ---- merge the two key halves of every query row -----------------------
   l += __shfl_xor(l, 32);       // both lanes of a row hold the same m

@@ -98,7 +98,7 @@ __device__ inline uint32_t tile_load_offset(int wave, int lane) {
 }
 
 template <int D>
-__device__ __forceinline__ void issue_tile_load(const uint16_t* __restrict__ tile_src, u32x4* slot,
+__device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4* slot,
                                                 uint32_t off, int wave) {
   using S = Stage<D>;
   // An empty asm makes each load's scalar base (tile and pass) and lane
