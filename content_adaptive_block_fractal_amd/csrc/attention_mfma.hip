@@ -360,9 +360,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
       const f32x16 s_nxt = scores(k_next);
       read_v();
       __builtin_amdgcn_sched_barrier(0);
-      // The copies of tile e+2 are issued after this tile's LDS reads: the
-      // compiler tracks only a few LDS copies in flight, and reads issued
-      // behind more of them would wait for all of them.
+      // The copies of tile e+2 are issued after this tile's LDS reads, so
+      // that no read of this tile has to be ordered behind them.
       issue_tile_load<D>(K + t2.off, k_here, koff, wave);
       issue_tile_load<D>(V + t2.off, v_fill, voff, wave);
       __builtin_amdgcn_sched_barrier(0);
