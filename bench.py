@@ -188,9 +188,10 @@ def measure_subset(cabf, geom, bufs, thr, sta, flags, steps: int, frac: float = 
 
 def measure_backward(cabf, geom, bufs, thr, sta, steps: int):
     """cabf_bsa_backward on the main workload's lists (after a forward that
-    keeps lse), timed with HIP events. Effective TFLOP/s counts 2.5x the
-    forward's flops (five 64x64xd products per kept tile); the kernels
-    actually run seven (S and dP are recomputed in both gradient passes)."""
+    keeps lse), timed with HIP events, in the default clock-phased order and
+    in deterministic order. Effective TFLOP/s counts 2.5x the forward's flops
+    (five 64x64xd products per kept tile); the kernels actually run eight
+    (S in all three passes, dP in two)."""
     import torch
     q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
     scale = cabf.default_scale(geom)
@@ -203,23 +204,28 @@ def measure_backward(cabf, geom, bufs, thr, sta, steps: int):
     dq, dk, dv = (torch.empty_like(qp) for _ in range(3))
     bws = cabf._ws(cabf._lib.cabf_bsa_backward_workspace_bytes(cabf.ctypes.byref(geom.c())),
                    qp.device)
-    for _ in range(2):
-        cabf.cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, cnt, idx, scale, dq, dk, dv, bws)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        cabf.cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, cnt, idx, scale, dq, dk, dv, bws)
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
     kept = int(cnt.sum(dtype=torch.int64).item())
     fwd_flops = 4.0 * 64 * 64 * geom.head_dim * kept
-    ms = statistics.fmean(times)
-    return {"ms": ms, "ms_median": statistics.median(times), "kept_tiles": kept,
-            "effective_tflops": 2.5 * fwd_flops / (ms * 1e-3) / 1e12,
-            "executed_tflops": 3.5 * fwd_flops / (ms * 1e-3) / 1e12}
+    out = {"kept_tiles": kept}
+    for label, flags in (("", 0), ("deterministic_", cabf.BSA_DETERMINISTIC)):
+        for _ in range(2):
+            cabf.cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, cnt, idx, scale, dq, dk, dv, bws,
+                                   flags)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            cabf.cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, cnt, idx, scale, dq, dk, dv, bws,
+                                   flags)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = statistics.fmean(times)
+        out.update({label + "ms": ms, label + "ms_median": statistics.median(times),
+                    label + "effective_tflops": 2.5 * fwd_flops / (ms * 1e-3) / 1e12})
+    out["executed_tflops"] = 4.0 * fwd_flops / (out["ms"] * 1e-3) / 1e12
+    return out
 
 
 def measure_semantic(cabf, steps: int, warmup: int, seed: int):

@@ -90,7 +90,7 @@ def _load():
                                                    P, ctypes.c_uint, P]),
         "cabf_bsa_backward_workspace_bytes": (SZ, [G]),
         "cabf_bsa_backward": (ctypes.c_int, [G, ctypes.c_int, P, P, P, P, P, P, P, P, F32, P, P, P,
-                                             P, SZ, P]),
+                                             P, SZ, ctypes.c_uint, P]),
         "cabf_kmeans_workspace_bytes": (SZ, [Q, I32]),
         "cabf_kmeans": (ctypes.c_int, [Q, ctypes.c_int, P, I32, P, I32, P, P, P, P, P, P, SZ, P]),
         "cabf_gather_rows": (ctypes.c_int, [Q, ctypes.c_int, P, P, P, I32, P]),
@@ -425,7 +425,7 @@ def bsa_forward_subset(qp, kp, vp, kv_count, kv_index, q_blocks, geom: Geom, op,
 
 
 def cabf_bsa_backward(geom: Geom, qp, kp, vp, op, lse, dop, kv_count, kv_index, scale: float,
-                      dqp, dkp, dvp, workspace):
+                      dqp, dkp, dvp, workspace, flags: int = 0):
     """Gradients of cabf_bsa_forward: dqp, dkp, dvp [B, h, N, d] (bf16)."""
     s = geom.sizes()
     nb = s["n_blocks"]
@@ -439,16 +439,18 @@ def cabf_bsa_backward(geom: Geom, qp, kp, vp, op, lse, dop, kv_count, kv_index, 
         _dev(kv_count, lead, torch.int32, "kv_count"),
         _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), float(scale),
         _dev(dqp, ps, qp.dtype, "dqp"), _dev(dkp, ps, qp.dtype, "dkp"),
-        _dev(dvp, ps, qp.dtype, "dvp"), ptr, nbytes, _stream(qp))
+        _dev(dvp, ps, qp.dtype, "dvp"), ptr, nbytes, int(flags), _stream(qp))
     _check("cabf_bsa_backward", st)
 
 
-def bsa_backward(qp, kp, vp, op, lse, dop, kv_count, kv_index, geom: Geom, scale=None):
+def bsa_backward(qp, kp, vp, op, lse, dop, kv_count, kv_index, geom: Geom, scale=None,
+                 deterministic=False):
     """(dqp, dkp, dvp) of the block-sparse attention over the given lists."""
     dqp, dkp, dvp = (torch.empty_like(qp) for _ in range(3))
     ws = _ws(_lib.cabf_bsa_backward_workspace_bytes(ctypes.byref(geom.c())), qp.device)
     cabf_bsa_backward(geom, qp, kp, vp, op, lse, dop, kv_count, kv_index,
-                      default_scale(geom) if scale is None else scale, dqp, dkp, dvp, ws)
+                      default_scale(geom) if scale is None else scale, dqp, dkp, dvp, ws,
+                      BSA_DETERMINISTIC if deterministic else 0)
     return dqp, dkp, dvp
 
 

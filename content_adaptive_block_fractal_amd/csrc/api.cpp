@@ -297,12 +297,13 @@ int cabf_bsa_backward(const cabf_geom* g, cabf_dtype dtype, const void* qp, cons
                       const void* vp, const void* op, const float* lse, const void* dop,
                       const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
                       void* dkp, void* dvp, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+                      unsigned flags, hipStream_t stream) {
   Geo geo;
   const int st = make_geo(g, &geo);
   if (st != CABF_OK) return st;
   if (elem_bytes(dtype) == 0) return CABF_EINVAL;
   if (dtype != CABF_BF16) return CABF_EUNSUPPORTED;
+  if ((flags & ~static_cast<unsigned>(CABF_BSA_DETERMINISTIC)) != 0) return CABF_EINVAL;
   if (qp == nullptr || kp == nullptr || vp == nullptr || op == nullptr || lse == nullptr ||
       dop == nullptr || kv_count == nullptr || kv_index == nullptr || dqp == nullptr ||
       dkp == nullptr || dvp == nullptr || workspace == nullptr)
@@ -315,7 +316,7 @@ int cabf_bsa_backward(const cabf_geom* g, cabf_dtype dtype, const void* qp, cons
     return CABF_EINVAL;
   if (workspace_bytes < cabf::bwd_workspace_layout(geo).total) return CABF_EWORKSPACE;
   cabf::launch_bsa_backward(geo, qp, kp, vp, op, lse, dop, kv_count, kv_index, scale, dqp, dkp,
-                            dvp, workspace, stream);
+                            dvp, workspace, (flags & CABF_BSA_DETERMINISTIC) == 0, stream);
   return launched();
 }
 

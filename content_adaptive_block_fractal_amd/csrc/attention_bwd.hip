@@ -164,8 +164,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   const int key0 = 32 * wk;
   int toff[kDT][2][2];
   transposed_offsets<D>(toff, key0, lane);
+  // first list entry of the pass (0, or clock-phased: see clock_phased_start)
+  __shared__ int start_sh;
+  if (wave == 0) {
+    const int st = clock_phased_start(a.kv_count + bh * a.nb, a.nb, cnt, a.sweep_ticks, lane);
+    if (lane == 0) start_sh = st;
+  }
+  __syncthreads();
+  const int start = __builtin_amdgcn_readfirstlane(start_sh);
   auto tile_of = [&](int t) {
-    const int jb = list[t < cnt ? t : cnt - 1];
+    int p = (t < cnt ? t : cnt - 1) + start;
+    p -= p >= cnt ? cnt : 0;
+    const int jb = list[p];
     const bool real = static_cast<unsigned>(jb) < static_cast<unsigned>(a.nb);
     return real ? jb : -1;
   };
@@ -365,7 +375,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
   const int row0 = 32 * wq;                                 // first query row of this wave's half
   int toff[kDT][2][2];
   transposed_offsets<D>(toff, row0, lane);
-  auto block_of = [&](int t) { return list[t < cnt ? t : cnt - 1]; };
+  // first list entry of the pass (0, or clock-phased: see clock_phased_start)
+  __shared__ int start_sh;
+  if (wave == 0) {
+    const int st = clock_phased_start(q_count + bh * a.nb, a.nb, cnt, a.sweep_ticks, lane);
+    if (lane == 0) start_sh = st;
+  }
+  __syncthreads();
+  const int start = __builtin_amdgcn_readfirstlane(start_sh);
+  auto block_of = [&](int t) {
+    int p = (t < cnt ? t : cnt - 1) + start;
+    p -= p >= cnt ? cnt : 0;
+    return list[p];
+  };
   // S or dP of this wave's 32 queries x 32 keys: rows of `tile` against f
   auto rows_times = [&](const u32x4* tile, const bf16x8 (&f)[kKS]) {
     f32x16 r;
@@ -378,25 +400,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
     }
     return r;
   };
-  auto step = [&](int ib, const u32x4* qs, const u32x4* ds, const float (&vec)[2][kBlock]) {
-    const f32x16 s = rows_times(qs, kf);
-    f32x16 dp;
-    if constexpr (DK) dp = rows_times(ds, vf);
+  // P (dV pass) or dS (dK pass) of query block ib in bf16, from S (and dP)
+  auto weights = [&](int ib, const f32x16& s, const f32x16& dp, const float (&vec)[2][kBlock],
+                     bf16x8 (&wb)[2]) {
     const BlockExtent ext = block_extent(ib, a);
     const uint32_t bits = ext.full() ? 0xffffu : real_row_bits(ext, wq, h);
-    bf16x8 wb[2];      // P (dV pass) or dS (dK pass), bf16
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int m = row0 + 8 * g + 4 * h;                  // rows m .. m + 3
-      const float4 l4 = *reinterpret_cast<const float4*>(&vec[0][m]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      // element reads (the compiler then sees that they do not touch the
+      // tiles being copied, and does not wait for the copies; vector-cast
+      // reads made it wait)
+      const float lv[4] = {vec[0][m], vec[0][m + 1], vec[0][m + 2], vec[0][m + 3]};
       float dv4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (DK) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&vec[1][m]);
-        dv4[0] = d4.x;
-        dv4[1] = d4.y;
-        dv4[2] = d4.z;
-        dv4[3] = d4.w;
+        dv4[0] = vec[1][m];
+        dv4[1] = vec[1][m + 1];
+        dv4[2] = vec[1][m + 2];
+        dv4[3] = vec[1][m + 3];
       }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -408,8 +429,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
           wb[r >> 3][r & 7] = static_cast<__bf16>(p);
       }
     }
-    // dV^T += dO^T P, or dK^T += Q^T dS
-    const uint16_t* xt = reinterpret_cast<const uint16_t*>(DK ? qs : ds);
+  };
+  // dV^T += dO^T P (xs: the dO tile), or dK^T += Q^T dS (xs: the Q tile)
+  auto accumulate = [&](const u32x4* xs, const bf16x8 (&wb)[2]) {
+    const uint16_t* xt = reinterpret_cast<const uint16_t*>(xs);
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -417,21 +440,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             transposed_fragment(xt, toff[dt][st][0], toff[dt][st][1]), wb[st], acc[dt], 0, 0, 0);
   };
-  // lse (base 2, +inf for rows without keys) and D of query block ib -> vec slot
-  auto load_vecs = [&](int ib, float (&vec)[2][kBlock]) {
+  // lse (base 2, +inf for rows without keys) and D of a query block -> vec
+  // slot, in two steps: the loads are issued before the tile copies (waiting
+  // for them later does not wait for the copies) and stored at the end of
+  // the tile
+  float l_raw = 0.0f, d_raw = 0.0f;
+  auto fetch_vecs = [&](int ib) {
     if (tid < kBlock) {
-      const float l = lse_h[static_cast<int64_t>(ib) * kBlock + tid];
-      vec[0][tid] = l == -INFINITY ? INFINITY : l * kLog2e;
-      if constexpr (DK) vec[1][tid] = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
+      l_raw = lse_h[static_cast<int64_t>(ib) * kBlock + tid];
+      if constexpr (DK) d_raw = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
+    }
+  };
+  auto store_vecs = [&](float (&vec)[2][kBlock]) {
+    if (tid < kBlock) {
+      vec[0][tid] = l_raw == -INFINITY ? INFINITY : l_raw * kLog2e;
+      if constexpr (DK) vec[1][tid] = d_raw;
     }
   };
 
-  if (cnt > 0) {
-    const uint32_t off = tile_load_offset<D, false>(wave, lane);
+  const uint32_t off = tile_load_offset<D, false>(wave, lane);
+  auto q_tile = [&](int ib) { return Q + static_cast<int64_t>(ib) * kBlock * D; };
+  auto d_tile = [&](int ib) { return dO + static_cast<int64_t>(ib) * kBlock * D; };
+  if constexpr (DK) {
+   if (cnt > 0) {
+    // dK pass: Q and dO of tile e+1 stream in while tile e is computed
     int ib_cur = block_of(0);
-    load_pair<D>(Q + static_cast<int64_t>(ib_cur) * kBlock * D, dO + static_cast<int64_t>(ib_cur) * kBlock * D,
-                 q_slot0, d_slot0, off, wave);
-    load_vecs(ib_cur, vec_slot[0]);
+    fetch_vecs(ib_cur);
+    load_pair<D>(q_tile(ib_cur), d_tile(ib_cur), q_slot0, d_slot0, off, wave);
+    store_vecs(vec_slot[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     auto body = [&](int e, auto parity) {
@@ -442,11 +478,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
       u32x4* const dn = kOdd ? d_slot0 : d_slot1;
       const int ib_next = block_of(e + 1);
       if (e + 1 < cnt) {
-        load_pair<D>(Q + static_cast<int64_t>(ib_next) * kBlock * D,
-                     dO + static_cast<int64_t>(ib_next) * kBlock * D, qn, dn, off, wave);
-        load_vecs(ib_next, vec_slot[kOdd ^ 1]);
+        fetch_vecs(ib_next);
+        __builtin_amdgcn_sched_barrier(0);      // the vector loads stay ahead of the copies
+        load_pair<D>(q_tile(ib_next), d_tile(ib_next), qn, dn, off, wave);
       }
-      step(ib_cur, qc, dc, vec_slot[kOdd]);
+      const f32x16 sv = rows_times(qc, kf);
+      const f32x16 dp = rows_times(dc, vf);
+      bf16x8 wb[2];
+      weights(ib_cur, sv, dp, vec_slot[kOdd], wb);
+      accumulate(qc, wb);
+      if (e + 1 < cnt) store_vecs(vec_slot[kOdd ^ 1]);
       ib_cur = ib_next;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -455,6 +496,51 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
       body(e, std::integral_constant<int, 0>{});
       if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
     }
+   }
+  } else {
+   if (cnt > 0) {
+    // dV pass, software-pipelined as the forward: Q runs one tile ahead of
+    // dO, and S of tile e+1 is issued to the matrix cores before P of tile e
+    // is formed. Tile e: Q of e+1 in q_slot[(e+1)%2], dO of e in d_slot[e%2];
+    // Q of e+2 streams into q_slot[e%2], dO of e+1 into d_slot[(e+1)%2].
+    int ib_cur = block_of(0), ib_nxt = block_of(1);
+    fetch_vecs(ib_cur);
+    issue_tile_load<D>(q_tile(ib_cur), q_slot0, off, wave);
+    issue_tile_load<D>(d_tile(ib_cur), d_slot0, off, wave);
+    issue_tile_load<D>(q_tile(ib_nxt), q_slot1, off, wave);
+    store_vecs(vec_slot[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 s_cur = rows_times(q_slot0, kf);
+    __syncthreads();            // tile 0's Q slot is refilled next
+    const f32x16 no_dp = {};
+    auto body = [&](int e, auto parity) {
+      constexpr int kOdd = decltype(parity)::value;
+      u32x4* const q_here = kOdd ? q_slot1 : q_slot0;    // slot e % 2
+      u32x4* const q_next = kOdd ? q_slot0 : q_slot1;
+      u32x4* const d_here = kOdd ? d_slot1 : d_slot0;
+      u32x4* const d_next = kOdd ? d_slot0 : d_slot1;
+      const int ib2 = block_of(e + 2);                     // clamped: redundant but in bounds
+      fetch_vecs(ib_nxt);
+      __builtin_amdgcn_sched_barrier(0);        // the vector loads stay ahead of the copies
+      issue_tile_load<D>(q_tile(ib2), q_here, off, wave);
+      issue_tile_load<D>(d_tile(ib_nxt), d_next, off, wave);
+      const f32x16 s_nxt = rows_times(q_next, kf);
+      bf16x8 wb[2];
+      weights(ib_cur, s_cur, no_dp, vec_slot[kOdd], wb);
+      accumulate(d_here, wb);
+      store_vecs(vec_slot[kOdd ^ 1]);
+      s_cur = s_nxt;
+      ib_cur = ib_nxt;
+      ib_nxt = ib2;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int e = 0; e < cnt; e += 2) {
+      body(e, std::integral_constant<int, 0>{});
+      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
+    }
+   }
   }
 
   // ---- add the two query halves, scale dK, store (pad keys: 0) -------------
@@ -511,7 +597,7 @@ BwdWorkspace bwd_workspace_layout(const Geo& g) {
 void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const void* vp,
                          const void* op, const float* lse, const void* dop,
                          const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
-                         void* dkp, void* dvp, void* workspace, hipStream_t stream) {
+                         void* dkp, void* dvp, void* workspace, bool phased, hipStream_t stream) {
   const BwdWorkspace w = bwd_workspace_layout(g);
   char* ws = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws + w.delta);
@@ -553,18 +639,29 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   uint16_t* dq16 = static_cast<uint16_t*>(dqp);
   uint16_t* dk16 = static_cast<uint16_t*>(dkp);
   uint16_t* dv16 = static_cast<uint16_t*>(dvp);
+  // clock-phased periods: ticks of the 100 MHz clock per tile of each pass
+  // (d = 128 at 720p; d = 64 tiles take about half as long)
+  const uint32_t t_dq = phased ? (g.D == 64 ? 95u : 185u) : 0u;
+  const uint32_t t_dv = phased ? (g.D == 64 ? 95u : 185u) : 0u;
+  const uint32_t t_dk = phased ? (g.D == 64 ? 110u : 220u) : 0u;
+  AttnArgs a_dq = a, a_dv = a, a_dk = a;
+  a_dq.sweep_ticks = t_dq;
+  a_dv.sweep_ticks = t_dv;
+  a_dk.sweep_ticks = t_dk;
   if (g.D == 64) {
-    hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, dq16, items);
-    hipLaunchKernelGGL((bwd_dkdv<64, false>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
-                       q_count, q_index, dv16, items);
-    hipLaunchKernelGGL((bwd_dkdv<64, true>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
-                       q_count, q_index, dk16, items);
+    hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta, dq16,
+                       items);
+    hipLaunchKernelGGL((bwd_dkdv<64, false>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16,
+                       delta, q_count, q_index, dv16, items);
+    hipLaunchKernelGGL((bwd_dkdv<64, true>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
+                       delta, q_count, q_index, dk16, items);
   } else {
-    hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta, dq16, items);
-    hipLaunchKernelGGL((bwd_dkdv<128, false>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
-                       q_count, q_index, dv16, items);
-    hipLaunchKernelGGL((bwd_dkdv<128, true>), dim3(grid), dim3(kThreads), 0, stream, a, do16, delta,
-                       q_count, q_index, dk16, items);
+    hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta, dq16,
+                       items);
+    hipLaunchKernelGGL((bwd_dkdv<128, false>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16,
+                       delta, q_count, q_index, dv16, items);
+    hipLaunchKernelGGL((bwd_dkdv<128, true>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
+                       delta, q_count, q_index, dk16, items);
   }
 }
 

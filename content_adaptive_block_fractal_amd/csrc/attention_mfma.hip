@@ -238,26 +238,13 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   const int32_t* __restrict__ list = w.list;
   const int key0 = 32 * wk;     // first key of this wave's half
 
-  // Where the pass over the list starts (AttnArgs::sweep_ticks): at the
-  // fraction (clock mod P) / P of the list. Lists of a head spread their
-  // entries over the key range alike (or are shifted copies of each other),
-  // so equal fractions mean nearby key blocks. The period P must be the same
-  // for every workgroup of a head, or clock mod P would not be coherent:
-  // P = sweep_ticks * the mean list length of 64 rows spread evenly over the
-  // head, which all of them sample alike. Wave 0 computes the start and
-  // shares it through LDS, so that all waves agree on it.
+  // Where the pass over the list starts (AttnArgs::sweep_ticks; see
+  // clock_phased_start). Wave 0 computes it and shares it through LDS, so
+  // that all waves agree on it.
   if (wave == 0) {
-    int start = 0;
-    if (L::kPhased && a.sweep_ticks != 0 && cnt > 1) {
-      const int32_t* head_counts = a.kv_count + bh * a.nb;
-      int total = min(max(head_counts[(lane * a.nb) >> 6], 1), a.nb);
-#pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) total += __shfl_xor(total, sh);
-      // 32 clock bits wrap every 43 s: one incoherent moment, harmless
-      const uint32_t period = static_cast<uint32_t>(max(total >> 6, 1)) * a.sweep_ticks;
-      const uint32_t now = static_cast<uint32_t>(__builtin_amdgcn_s_memrealtime());
-      start = static_cast<int>(static_cast<uint64_t>(now % period) * cnt / period);
-    }
+    const int start = L::kPhased ? clock_phased_start(a.kv_count + bh * a.nb, a.nb, cnt,
+                                                      a.sweep_ticks, lane)
+                                 : 0;
     if (lane == 0) *start_shared = start;
   }
   __syncthreads();

@@ -48,7 +48,8 @@ BwdWorkspace bwd_workspace_layout(const Geo& g);
 void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const void* vp,
                          const void* op, const float* lse, const void* dop,
                          const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
-                         void* dkp, void* dvp, void* workspace, hipStream_t stream);
+                         void* dkp, void* dvp, void* workspace, bool phased,
+                         hipStream_t stream);
 
 void launch_bsa_forward(const Geo& g, bool bf16, const void* qp, const void* kp, const void* vp,
                         const int32_t* kv_count, const int32_t* kv_index, float scale, void* op,

@@ -242,12 +242,17 @@ size_t cabf_bsa_backward_workspace_bytes(const cabf_geom* g);
  * forward's output) and dop: [B, heads, N, head_dim] bf16; lse: the
  * forward's [B, heads, N] fp32; kv_count / kv_index: the forward's lists
  * (inputs). dqp, dkp, dvp: [B, heads, N, head_dim] bf16 (outputs).
- * bf16 matrix products with fp32 accumulation; results are deterministic. */
+ * bf16 matrix products with fp32 accumulation.
+ * flags: 0 or CABF_BSA_DETERMINISTIC (other bits give CABF_EINVAL), as for
+ *   cabf_bsa_forward: with 0 each pass over a list starts at a clock-derived
+ *   entry (the same sums in another order, so results may differ from run to
+ *   run in the last bits); CABF_BSA_DETERMINISTIC walks the lists in order
+ *   and gives bit-identical results on every run. */
 int cabf_bsa_backward(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp,
                       const void* vp, const void* op, const float* lse, const void* dop,
                       const int32_t* kv_count, const int32_t* kv_index, float scale, void* dqp,
                       void* dkp, void* dvp, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream);
+                      unsigned flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Semantic-permutation variant (Sparse VideoGen2 summary, Methodology A-C):

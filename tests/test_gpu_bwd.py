@@ -57,8 +57,9 @@ CASES = [
 def test_backward_matches_oracle(name, shape, thr, sta):
     say(f"backward {name} thr={thr} sta={sta}")
     g, og, s, qp, kp, vp, cnt, idx, op, lse, dop = setup(*shape, thr, sta)
-    dq, dk, dv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
-    dq2, dk2, dv2 = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
+    dq, dk, dv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s, deterministic=True)
+    dq2, dk2, dv2 = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s, deterministic=True)
+    pq, pk, pv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)     # clock-phased
     torch.cuda.synchronize()
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))      # deterministic
@@ -69,6 +70,9 @@ def test_backward_matches_oracle(name, shape, thr, sta):
                                   idx[0, hd].cpu().numpy(), og, s)
         for nm, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
             compare_grad(got[0, hd], r, valid, f"{name} head {hd} {nm}")
+            assert torch.all(got[0, hd][torch.from_numpy(~valid).to(DEV)] == 0)
+        for nm, got, r in (("dq", pq, ref[0]), ("dk", pk, ref[1]), ("dv", pv, ref[2])):
+            compare_grad(got[0, hd], r, valid, f"{name} head {hd} {nm} (clock-phased)")
             assert torch.all(got[0, hd][torch.from_numpy(~valid).to(DEV)] == 0)
 
 
