@@ -172,10 +172,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   }
   __syncthreads();
   const int start = __builtin_amdgcn_readfirstlane(start_sh);
+  // List entries are fetched 64 at a time, one per lane, a batch ahead of
+  // use, and read out with readlane (as in the forward): no list load is
+  // waited on per tile. Entry t of the pass is list entry start + t
+  // (wrapped); t is clamped to the last one.
+  auto load_batch = [&](int b) {
+    int pos = min(b * 64 + lane, cnt - 1) + start;
+    pos -= pos >= cnt ? cnt : 0;
+    return list[pos];
+  };
+  int batch_cur = 0, batch_nxt = 0;     // entries 64 B .. and 64 (B + 1) .. of the pass
   auto tile_of = [&](int t) {
-    int p = (t < cnt ? t : cnt - 1) + start;
-    p -= p >= cnt ? cnt : 0;
-    const int jb = list[p];
+    const int p = t < cnt ? t : cnt - 1;
+    const int jb = __builtin_amdgcn_readlane(batch_cur, p & 63);
     const bool real = static_cast<unsigned>(jb) < static_cast<unsigned>(a.nb);
     return real ? jb : -1;
   };
@@ -213,6 +222,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
 
   if (cnt > 0) {
     const uint32_t off = tile_load_offset<D, false>(wave, lane);
+    batch_cur = load_batch(0);
+    batch_nxt = load_batch(1);
     int jb_cur = tile_of(0);
     load_pair<D>(K + static_cast<int64_t>(max(jb_cur, 0)) * kBlock * D,
                  V + static_cast<int64_t>(max(jb_cur, 0)) * kBlock * D, k_slot0, v_slot0, off, wave);
@@ -224,6 +235,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
       u32x4* const vc = kOdd ? v_slot1 : v_slot0;
       u32x4* const kn = kOdd ? k_slot0 : k_slot1;
       u32x4* const vn = kOdd ? v_slot0 : v_slot1;
+      if (((e + 1) & 63) == 0 && e + 1 < cnt) {   // entry e + 1 opens the next batch
+        batch_cur = batch_nxt;
+        batch_nxt = load_batch(((e + 1) >> 6) + 1);
+      }
       const int jb_next = tile_of(e + 1);
       if (e + 1 < cnt)
         load_pair<D>(K + static_cast<int64_t>(max(jb_next, 0)) * kBlock * D,
