@@ -186,6 +186,57 @@ def measure_subset(cabf, geom, bufs, thr, sta, flags, steps: int, frac: float = 
                 attention_tflops=flops / (ms * 1e-3) / 1e12)
 
 
+def measured_peaks(cabf, dev):
+    """What this GPU sustains: a dense bf16 matrix-core loop (cabf_mfma_peak_probe)
+    and a plain 2 GiB device copy, timed with HIP events."""
+    import torch
+    wgs, iters = 2048, 20000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    cabf.cabf_mfma_peak_probe(wgs, 200, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cabf.cabf_mfma_peak_probe(wgs, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    flops = wgs * 4 * iters * 8 * 2.0 * 32 * 32 * 16
+    mfma_tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = (2 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del src, dst
+    copy_gbs = 2.0 * n * 4 / (min(times) * 1e-3) / 1e9
+    return {"mfma_bf16_tflops": mfma_tflops, "hbm_copy_gbs": copy_gbs,
+            "mfma_probe": f"{wgs} workgroups x 4 waves x {iters} x 8 v_mfma_f32_32x32x16_bf16",
+            "copy_probe": "2 GiB fp32 device-to-device copy (read + write counted), best of 5"}
+
+
+def hbm_fractions(geom, sizes, stages, kept, elem_bytes):
+    """Algorithmic bytes of the memory-bound stages over their measured time, against
+    the HBM peak: permute moves Q, K, V raster -> padded; the mask reads Qp, Kp, writes
+    and reads the fp32 block means and writes the lists; unpermute moves O back."""
+    row = geom.batch * geom.heads * geom.head_dim * elem_bytes
+    raster, padded = sizes["tokens_raster"] * row, sizes["tokens_padded"] * row
+    nb = sizes["n_blocks"]
+    pooled = 2 * geom.batch * geom.heads * nb * geom.head_dim * 4
+    lists = 4 * kept + 4 * geom.batch * geom.heads * nb
+    work = {"permute": 3 * (raster + padded), "mask": 2 * padded + 2 * pooled + lists,
+            "unpermute": raster + padded}
+    out = {}
+    for k, b in work.items():
+        gbs = b / (stages[k] * 1e-3) / 1e9
+        out[k] = {"bytes": b, "gbs": gbs, "frac": gbs / PEAK_HBM_GBS}
+    return out
+
+
 def measure_backward(cabf, geom, bufs, thr, sta, steps: int):
     """cabf_bsa_backward on the main workload's lists (after a forward that
     keeps lse), timed with HIP events, in the default clock-phased order and
@@ -472,7 +523,12 @@ def main():
         "ms_per_layer": mask_ms + attn_ms,
         "mask_share": mask_ms / (mask_ms + attn_ms),
         "kept_tiles": main_run["kept_tiles"],
+        "hbm_fractions": hbm_fractions(geom, sizes, main_run["stage_ms_mean"], main_run["kept_tiles"],
+                                       2 if w.dtype == "bf16" else 4),
     }
+    peaks = measured_peaks(cabf, dev)
+    line["measured_peaks"] = peaks
+    line["roofline"]["frac_of_measured_peak"] = attn_tflops / peaks["mfma_bf16_tflops"]
     if args.variants:
         var = {}
         cases = [(0.90, None, flags), (0.80, (1, 1, 1), flags), (0.90, (1, 1, 1), flags),

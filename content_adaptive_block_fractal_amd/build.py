@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcabf.so")
 
 SOURCES = ["api.cpp", "permute.hip", "mask.hip", "attention.hip", "attention_simple.hip",
-           "attention_mfma.hip", "attention_bwd.hip", "kmeans.hip", "svg.hip"]
+           "attention_mfma.hip", "attention_bwd.hip", "kmeans.hip", "svg.hip", "probe.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -61,4 +61,8 @@ void launch_bsa_forward_subset(const Geo& g, const void* qp, const void* kp, con
                                const int32_t* q_blocks, int64_t n_blocks, float scale, void* op,
                                float* lse, bool phased, hipStream_t stream);
 
+// Dense bf16 matrix-core loop (measurement aid): workgroups of 256 threads,
+// each wave iters x 8 products of 32x32x16; out holds workgroups * 256 floats.
+void launch_mfma_peak(int workgroups, int iters, float* out, hipStream_t stream);
+
 }  // namespace cabf

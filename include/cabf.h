@@ -349,6 +349,14 @@ int cabf_cluster_attention(const cabf_seq* s, cabf_dtype dtype, int32_t cq, int3
                            void* op, float* lse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Measurement aid, not part of the method: a dense bf16 matrix-core loop
+ * (each wave runs iters x 8 independent 32x32x16 products, 262144 * iters
+ * flops per wave) whose time gives the matrix-core rate the chip sustains
+ * under load, to set beside the published peak. workgroups of 256 threads
+ * (4 waves); out: workgroups * 256 floats (device, output, values without
+ * meaning). workgroups, iters >= 1, else CABF_EINVAL. */
+int cabf_mfma_peak_probe(int32_t workgroups, int32_t iters, float* out, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* cabf_status_string(int status);
 
