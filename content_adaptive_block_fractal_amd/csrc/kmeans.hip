@@ -248,7 +248,9 @@ __global__ __launch_bounds__(256) void km_offsets(const uint32_t* __restrict__ s
 
 // One workgroup per cluster: wave w sums members b + w*q .. (a contiguous
 // quarter, in sorted order), the four partial sums are added in wave order,
-// so the mean is deterministic. An empty cluster keeps its centroid.
+// so the mean is deterministic. An empty cluster keeps its centroid. Rows are
+// gathered through the permutation (256 bytes each at d = 128), so the loop
+// keeps many of them in flight.
 template <int D>
 __global__ __launch_bounds__(256) void km_update(const uint16_t* __restrict__ x,
                                                  const int32_t* __restrict__ perm,
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256) void km_update(const uint16_t* __restrict__ x,
   constexpr int kPer = D / 64;
   __shared__ float part[4][D];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int64_t row = blockIdx.x;                // bh * C + c
   const int64_t bh = row / C;
   const int c = static_cast<int>(row - bh * C);
@@ -270,26 +272,30 @@ __global__ __launch_bounds__(256) void km_update(const uint16_t* __restrict__ x,
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
   const int32_t* p = perm + bh * n;
+  // lane's kPer consecutive bf16 of a row, fetched as one load
+  typedef uint16_t lane_vec __attribute__((ext_vector_type(kPer)));
   const uint16_t* xb = x + bh * static_cast<int64_t>(n) * D + lane * kPer;
-  // four rows in flight at a time, added in member order
-  int i = wb;
-  for (; i + 4 <= we; i += 4) {
-    uint16_t v[4][kPer];
+  // kRows rows in flight at a time (the loop is latency-bound), added in
+  // member order. The batch's member indices come in with one load (lane u
+  // holds member i + u, clamped to the last one) and are read out with
+  // readlane, so every row address is scalar and the row loads issue back
+  // to back; rows past the end of the quarter are loaded (in bounds) but
+  // contribute nothing.
+  constexpr int kRows = 16;
+  for (int i = wb; i < we; i += kRows) {
+    const int mine = p[min(i + (lane & (kRows - 1)), we - 1)];
+    lane_vec v[kRows];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint16_t* src = xb + static_cast<int64_t>(p[i + u]) * D;
+    for (int u = 0; u < kRows; ++u)
+      v[u] = *reinterpret_cast<const lane_vec*>(
+          xb + static_cast<int64_t>(__builtin_amdgcn_readlane(mine, u)) * D);
+    // rows past the end add -0 (x + -0 = x exactly), so every load is used
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) v[u][k] = src[k];
+    for (int u = 0; u < kRows; ++u) {
+      const bool in = i + u < we;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) acc[k] += in ? bf16_bits_to_f32(v[u][k]) : -0.0f;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) acc[k] += bf16_bits_to_f32(v[u][k]);
-  }
-  for (; i < we; ++i) {
-    const uint16_t* src = xb + static_cast<int64_t>(p[i]) * D;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) acc[k] += bf16_bits_to_f32(src[k]);
   }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) part[wave][lane * kPer + k] = acc[k];
