@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--sparsity", type=float, default=0.80)
     ap.add_argument("--sta", action="store_true", help="union the +-1 sliding-tile window")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="reorder and pool in separate passes (default: cabf_permute_pool)")
     ap.add_argument("--deterministic", action="store_true",
                     help="walk every block list from its first entry (bit-reproducible attention)")
     ap.add_argument("--variants", type=int, default=1,
@@ -93,22 +95,22 @@ def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0, select="cdf", topk=
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
         if timed:
             ev[0].record()
-        if fused:
+        if fused and select != "sta":
             cabf.cabf_permute_pool(geom, q, k, v, qp, kp, vp, ws)
         else:
             cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
         if timed:
             ev[1].record()
-        if fused:
+        if select == "sta":
+            cabf.cabf_build_sta_mask(geom, sta, cnt, idx)
+        elif fused:
             cabf.cabf_build_block_mask_pooled(geom, scale, 0.0 if select == "topk" else thr,
                                               topk if select == "topk" else 0, sta, cnt, idx,
                                               None, ws)
         elif select == "cdf":
             cabf.cabf_build_block_mask(geom, qp, kp, scale, thr, sta, cnt, idx, None, ws)
-        elif select == "topk":
-            cabf.cabf_build_block_mask(geom, qp, kp, scale, 0.0, sta, cnt, idx, None, ws, topk=topk)
         else:
-            cabf.cabf_build_sta_mask(geom, sta, cnt, idx)
+            cabf.cabf_build_block_mask(geom, qp, kp, scale, 0.0, sta, cnt, idx, None, ws, topk=topk)
         if timed:
             ev[2].record()
         cabf.cabf_bsa_forward(geom, qp, kp, vp, cnt, idx, scale, op, None, flags)
@@ -219,17 +221,22 @@ def measured_peaks(cabf, dev):
             "copy_probe": "2 GiB fp32 device-to-device copy (read + write counted), best of 5"}
 
 
-def hbm_fractions(geom, sizes, stages, kept, elem_bytes):
+def hbm_fractions(geom, sizes, stages, kept, elem_bytes, fused):
     """Algorithmic bytes of the memory-bound stages over their measured time, against
-    the HBM peak: permute moves Q, K, V raster -> padded; the mask reads Qp, Kp, writes
-    and reads the fp32 block means and writes the lists; unpermute moves O back."""
+    the HBM peak: permute moves Q, K, V raster -> padded (fused: and writes the fp32
+    block means); the mask reads Qp, Kp (unfused only), writes and reads the block
+    means (unfused) or reads them (fused), and writes the lists; unpermute moves O
+    back."""
     row = geom.batch * geom.heads * geom.head_dim * elem_bytes
     raster, padded = sizes["tokens_raster"] * row, sizes["tokens_padded"] * row
     nb = sizes["n_blocks"]
     pooled = 2 * geom.batch * geom.heads * nb * geom.head_dim * 4
     lists = 4 * kept + 4 * geom.batch * geom.heads * nb
-    work = {"permute": 3 * (raster + padded), "mask": 2 * padded + 2 * pooled + lists,
-            "unpermute": raster + padded}
+    if fused:
+        work = {"permute": 3 * (raster + padded) + pooled, "mask": pooled + lists}
+    else:
+        work = {"permute": 3 * (raster + padded), "mask": 2 * padded + 2 * pooled + lists}
+    work["unpermute"] = raster + padded
     out = {}
     for k, b in work.items():
         gbs = b / (stages[k] * 1e-3) / 1e9
@@ -446,7 +453,8 @@ def main():
     ws = cabf.mask_workspace(geom, dev)
     bufs = (q, k, v, qp, kp, vp, op, o, cnt, idx, ws)
 
-    def measure(sparsity, sta, steps, warmup, flags, select="cdf", topk=0, fused=False):
+    def measure(sparsity, sta, steps, warmup, flags, select="cdf", topk=0, fused=None):
+        fused = (not args.unfused) if fused is None else fused
         cabf.cabf_permute(geom, q, k, v, qp, kp, vp)
         thr = (calibrate_thr(cabf, qp, kp, geom, sparsity, sta, ws, cnt, idx) if select == "cdf"
                else None)
@@ -476,7 +484,7 @@ def main():
         del src, dst
     sta = (1, 1, 1) if args.sta else None
     flags = cabf.BSA_DETERMINISTIC if args.deterministic else 0
-    main_run = measure(args.sparsity, sta, args.steps, args.warmup, flags)
+    main_run = measure(args.sparsity, sta, args.steps, args.warmup, flags, fused=not args.unfused)
     ms = main_run["wall_ms"]
     attn_ms = main_run["stage_ms_mean"]["attention"]
     mask_ms = main_run["stage_ms_mean"]["mask"]
@@ -505,6 +513,9 @@ def main():
             "parallelism": "single GPU",
             "attention_order": "list order (deterministic)" if args.deterministic
                                else "clock-phased start (default)",
+            "reorder": "separate reorder and block pooling" if args.unfused
+                       else "reorder fused with block pooling (cabf_permute_pool, "
+                            "cabf_build_block_mask_pooled)",
         },
         "roofline": {
             "bound": "mfma",
@@ -524,7 +535,7 @@ def main():
         "mask_share": mask_ms / (mask_ms + attn_ms),
         "kept_tiles": main_run["kept_tiles"],
         "hbm_fractions": hbm_fractions(geom, sizes, main_run["stage_ms_mean"], main_run["kept_tiles"],
-                                       2 if w.dtype == "bf16" else 4),
+                                       2 if w.dtype == "bf16" else 4, not args.unfused),
     }
     peaks = measured_peaks(cabf, dev)
     line["measured_peaks"] = peaks
@@ -557,16 +568,16 @@ def main():
                              attention_ms=a, mask_ms=r["stage_ms_mean"]["mask"],
                              attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
                              step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
-        # the fused reorder + pooling, then the mask from the pooled means
-        r = measure(args.sparsity, sta, max(3, args.steps // 4), 2, flags, fused=True)
+        # the other reorder: separate passes if the main run fused them, or fused
+        r = measure(args.sparsity, sta, max(3, args.steps // 4), 2, flags, fused=args.unfused)
         a = r["stage_ms_mean"]["attention"]
-        var["fused permute+pool"] = dict(
+        pm = lambda x: x["stage_ms_mean"]["permute"] + x["stage_ms_mean"]["mask"]
+        fused_r, unfused_r = (r, main_run) if args.unfused else (main_run, r)
+        var["fused permute+pool" if args.unfused else "unfused permute, mask"] = dict(
             thr=r["thr"], sparsity=r["sparsity"], ms_per_step=r["wall_ms"],
-            permute_pool_ms=r["stage_ms_mean"]["permute"], mask_ms=r["stage_ms_mean"]["mask"],
+            permute_ms=r["stage_ms_mean"]["permute"], mask_ms=r["stage_ms_mean"]["mask"],
             attention_ms=a, step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12,
-            unfused_permute_plus_mask_ms=main_run["stage_ms_mean"]["permute"]
-            + main_run["stage_ms_mean"]["mask"],
-            fused_permute_plus_mask_ms=r["stage_ms_mean"]["permute"] + r["stage_ms_mean"]["mask"])
+            unfused_permute_plus_mask_ms=pm(unfused_r), fused_permute_plus_mask_ms=pm(fused_r))
         line["variants"] = var
         line["active_query_subset"] = measure_subset(cabf, geom, bufs, main_run["thr"], sta,
                                                      flags, max(3, args.steps // 4))

@@ -456,9 +456,10 @@ def bsa_backward(qp, kp, vp, op, lse, dop, kv_count, kv_index, geom: Geom, scale
 
 
 def layer(q, k, v, geom: Geom, thr: float, sta=None, scale=None):
-    """One attention layer: reorder, mask, block-sparse attention, restore order."""
-    qp, kp, vp = permute(q, k, v, geom)
-    kv_count, kv_index = build_block_mask(qp, kp, geom, thr, sta, scale)
+    """One attention layer: reorder (pooling the blocks on the way), mask,
+    block-sparse attention, restore order."""
+    qp, kp, vp, ws = permute_pool(q, k, v, geom)
+    kv_count, kv_index = build_block_mask_pooled(ws, geom, thr, sta, scale)
     op = bsa_forward(qp, kp, vp, kv_count, kv_index, geom, scale)
     return unpermute(op, geom), (kv_count, kv_index)
 

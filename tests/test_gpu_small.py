@@ -257,8 +257,9 @@ def test_attention_rows_with_no_blocks_and_arbitrary_lists():
 @pytest.mark.parametrize("name,thr,sta", [("tiny-f32-d64", 0.2, (1, 1, 1)),
                                           ("ragged-bf16-d128", 0.5, (1, 1, 1))])
 def test_layer_end_to_end(name, thr, sta):
-    """permute -> build_block_mask -> bsa_forward -> unpermute on the GPU against
-    the oracle's layer; query blocks whose lists differ (exempt rows) are excluded."""
+    """permute_pool -> build_block_mask_pooled -> bsa_forward -> unpermute (the
+    layer helper) on the GPU against the oracle's layer; query blocks whose
+    lists differ (exempt rows) are excluded."""
     say(f"layer {name}")
     g, og, q, k, v = make(name)
     s = cabf.default_scale(g)
