@@ -33,11 +33,12 @@
 // lanes the same way in both operands; V^T is read with the key order the
 // S^T accumulator layout gives P.
 //
-// Pipeline: K and V tiles stream straight from global memory into a
-// two-slot LDS ring (global_load_lds_dwordx4), one LDS object per slot so
-// that reads of the current tile never wait for the tiles in flight. K runs
-// one tile ahead of V: S^T of tile e+1 is issued on the matrix cores before
-// the softmax of tile e runs on the vector ALUs. One barrier per tile.
+// Pipeline: K and V tiles stream straight from global memory into LDS rings
+// (global_load_lds_dwordx4; two K slots, three V slots), one LDS object per
+// slot so that reads of the current tile never wait for the tiles in
+// flight. K runs one tile ahead of V: S^T of tile e+1 is issued on the
+// matrix cores before the softmax of tile e runs on the vector ALUs. One
+// barrier per tile, which waits for every copy but the newest V tile.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
