@@ -264,3 +264,11 @@ def test_fused_entry_argument_checks():
     assert sub(op=NULL) == cabf.CABF_EINVAL
     assert sub(flags=8) == cabf.CABF_EINVAL
     assert sub(scale=float("nan")) == cabf.CABF_EINVAL
+
+
+@no_gpu
+def test_probe_argument_checks():
+    assert L.cabf_mfma_peak_probe(0, 10, DUMMY2, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_mfma_peak_probe(4, 0, DUMMY2, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_mfma_peak_probe(4, 10, NULL, NULL) == cabf.CABF_EINVAL
+    assert L.cabf_mfma_peak_probe(4, 10, ctypes.c_void_p(0x200002), NULL) == cabf.CABF_EINVAL

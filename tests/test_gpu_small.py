@@ -278,3 +278,12 @@ def test_layer_end_to_end(name, thr, sta):
         assert err.max() <= 2e-2 and err.mean() <= 2e-3
     else:
         assert err.max() <= 1e-4
+
+
+def test_mfma_peak_probe_runs():
+    """The measurement aid: every lane writes the sum of its accumulators,
+    finite and positive (the products of positive inputs)."""
+    out = torch.full((8 * 256,), -1.0, device=DEV)
+    cabf.cabf_mfma_peak_probe(8, 3, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and (out > 0).all()

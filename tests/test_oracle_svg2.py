@@ -57,6 +57,26 @@ def test_objective_never_increases_and_labels_are_nearest():
     assert np.all(d2[np.arange(300), out["assign"]] <= d2.min(axis=1) + 1e-12)
 
 
+def test_kmeans_matches_library_lloyd():
+    """Lloyd's algorithm as a library implements it (scikit-learn, lloyd, one
+    run from the same initial centroids, the same number of rounds, final
+    labels re-assigned to the final centroids): same labels, same centroids,
+    on data where no cluster empties (the library relocates empty clusters,
+    the oracle keeps their centroid)."""
+    sk = pytest.importorskip("sklearn.cluster")
+    q, _ = gaussian_mixture_qk(600, 1, 16, components=6, spread=0.6, amplitude=3.0, seed=2,
+                               dtype="f32")
+    x = q[0, 0].numpy().astype(np.float64)
+    init = kmeans_init_indices(600, 9, 1, seed=3)[0]
+    for iters in (1, 4, 9):
+        out = svg2.kmeans(x, init, iters)
+        assert out["counts"].min() > 0
+        km = sk.KMeans(n_clusters=9, init=x[init], n_init=1, max_iter=iters, tol=0.0,
+                       algorithm="lloyd").fit(x)
+        assert np.array_equal(km.labels_, out["assign"]), iters
+        assert np.allclose(km.cluster_centers_, out["cent"], rtol=0, atol=1e-9), iters
+
+
 # --- permutation -----------------------------------------------------------------
 
 def test_stable_permutation_hand_example():
