@@ -324,14 +324,32 @@ def measure_semantic(cabf, steps: int, warmup: int, seed: int):
     ws_att = cabf._ws(cabf._lib.cabf_cluster_attention_workspace_bytes(
         cabf.ctypes.byref(seq.c()), w.cq, w.ck), dev)
     names = ("kmeans_q", "kmeans_k", "gather", "select", "attention", "scatter")
+    side = torch.cuda.Stream(device=dev)          # default priority
 
-    def step(ev):
+    def run_kmeans(name, x, C, init):
+        m = km[name]
+        cabf.cabf_kmeans(seq, x, C, init, w.iters, m["centroids"], m["counts"], m["labels"],
+                         m["perm"], m["offsets"], m["ws"])
+
+    def step(ev, overlap):
         ev[0].record()
-        for i, (name, x, C, init) in enumerate((("q", q, w.cq, init_q), ("k", k, w.ck, init_k))):
-            m = km[name]
-            cabf.cabf_kmeans(seq, x, C, init, w.iters, m["centroids"], m["counts"], m["labels"],
-                             m["perm"], m["offsets"], m["ws"])
-            ev[1 + i].record()
+        if overlap:
+            # the two clusterings are independent: K's runs on a second stream
+            # while Q's runs on this one; stage "kmeans_q" then covers both
+            side.wait_event(ev[0])
+            with torch.cuda.stream(side):
+                run_kmeans("k", k, w.ck, init_k)
+                done_k = torch.cuda.Event()
+                done_k.record()
+            run_kmeans("q", q, w.cq, init_q)
+            torch.cuda.current_stream().wait_event(done_k)
+            ev[1].record()
+            ev[2].record()
+        else:
+            run_kmeans("q", q, w.cq, init_q)
+            ev[1].record()
+            run_kmeans("k", k, w.ck, init_k)
+            ev[2].record()
         cabf.cabf_gather_rows(seq, q, km["q"]["perm"], qp, rows)
         cabf.cabf_gather_rows(seq, k, km["k"]["perm"], kp, rows)
         cabf.cabf_gather_rows(seq, v, km["k"]["perm"], vp, rows)
@@ -345,15 +363,19 @@ def measure_semantic(cabf, steps: int, warmup: int, seed: int):
         cabf.cabf_scatter_rows(seq, op, rows, km["q"]["perm"], o)
         ev[6].record()
 
-    times = {nm: [] for nm in names}
-    for it in range(warmup + steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-        step(ev)
-        torch.cuda.synchronize()
-        if it >= warmup:
-            for i, nm in enumerate(names):
-                times[nm].append(ev[i].elapsed_time(ev[i + 1]))
-    mean = {nm: statistics.fmean(t) for nm, t in times.items()}
+    def timed(overlap):
+        times = {nm: [] for nm in names}
+        for it in range(warmup + steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+            step(ev, overlap)
+            torch.cuda.synchronize()
+            if it >= warmup:
+                for i, nm in enumerate(names):
+                    times[nm].append(ev[i].elapsed_time(ev[i + 1]))
+        return {nm: statistics.fmean(t) for nm, t in times.items()}
+
+    serial = timed(False)
+    mean = timed(True)
     # kept (query, key) token pairs of the selection, from the cluster sizes
     qs = torch.diff(km["q"]["offsets"].long(), dim=-1)            # [1, h, cq]
     ks = torch.diff(km["k"]["offsets"].long(), dim=-1)            # [1, h, ck]
@@ -372,7 +394,10 @@ def measure_semantic(cabf, steps: int, warmup: int, seed: int):
                 f"normal V, seeded",
         "density": pairs / float(h * n * n),
         "stage_ms": mean,
+        "kmeans_streams": "Q and K clustered concurrently on two streams (kmeans_q covers both)",
         "ms_per_layer": total,
+        "ms_per_layer_serial_kmeans": sum(serial.values()),
+        "kmeans_serial_ms": {"q": serial["kmeans_q"], "k": serial["kmeans_k"]},
         "attention_tflops": flops / (mean["attention"] * 1e-3) / 1e12,
         "layer_tflops": flops / (total * 1e-3) / 1e12,
         "steps": steps,

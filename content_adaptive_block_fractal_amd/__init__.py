@@ -590,8 +590,16 @@ def svg_layer(q, k, v, cq: int, ck: int, init_q, init_k, iters: int, top_p: floa
     seq = Seq(B, h, d, n)
     dev = q.device
     scale = 1.0 / math.sqrt(d) if scale is None else scale
+    # the two clusterings are independent: K's runs on a second stream
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        kk = kmeans(k, ck, init_k, iters)
     kq = kmeans(q, cq, init_q, iters)
-    kk = kmeans(k, ck, init_k, iters)
+    main.wait_stream(side)
+    for t in kk.values():
+        t.record_stream(main)
     rows = n + SEQ_PAD_ROWS
     qp, kp, vp, op = (torch.empty(B, h, rows, d, dtype=q.dtype, device=dev) for _ in range(4))
     cabf_gather_rows(seq, q, kq["perm"], qp, rows)
