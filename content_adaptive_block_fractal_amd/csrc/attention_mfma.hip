@@ -54,7 +54,7 @@ namespace cabf {
 namespace {
 
 using namespace tiles;
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleSlack = 8.0f;   // base-2 headroom before the running max is raised
 
 // s_waitcnt immediate: vmcnt = the loads of one tile copy (Stage::kIters),
 // expcnt and lgkmcnt not waited on (gfx9 encoding: vmcnt[3:0] and [15:14],
@@ -64,13 +64,14 @@ constexpr int kWaitAllButOneTile() {
   constexpr int n = Stage<D>::kIters;
   static_assert(n < 64, "vmcnt range");
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}   // base-2 headroom before the running max is raised
+}
 
 // A list entry decoded: element offset of its 64 K/V rows in the head, and
 // what the layout needs to mask it (block index, or number of valid keys).
 struct TileRef {
   int64_t off;
   int jb;
+  int code;     // block list: the extent code of the entry (see BlockListLayout::prep)
   bool real;
 };
 
@@ -110,18 +111,28 @@ struct BlockListLayout {
     w.list = a.kv_index + item * a.nb;
     return true;
   }
+  // A list entry as the batch holds it: the block index in bits 0..23 and
+  // its real extent in bits 24..31 (vy << 4 | vx; 0 for an entry outside
+  // [0, nb)). Computed once per batch of 64 entries, one per lane, so the
+  // tile loop needs no division to find a block's extent.
+  __device__ uint32_t prep(const AttnArgs& a, int32_t e) const {
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(a.nb)) return 0u;
+    const BlockExtent ext = block_extent(e, a);
+    return static_cast<uint32_t>(e) | (static_cast<uint32_t>((ext.vy << 4) | ext.vx) << 24);
+  }
   // entries outside [0, nb) load block 0 and are masked out entirely
   template <int D>
-  __device__ TileRef decode(const AttnArgs& a, int32_t e) const {
+  __device__ TileRef decode(const AttnArgs&, uint32_t p) const {
     TileRef r;
-    r.jb = e;
-    r.real = static_cast<unsigned>(e) < static_cast<unsigned>(a.nb);
-    r.off = static_cast<int64_t>(r.real ? e : 0) * kBlock * D;
+    r.code = static_cast<int>(p >> 24);
+    r.real = r.code != 0;
+    r.jb = static_cast<int>(p & 0xffffffu);
+    r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
     return r;
   }
   // false when every key of the tile is real; else the lane's real-key bits
-  __device__ bool partial(const AttnArgs& a, const TileRef& t, int wk, int h, uint32_t& bits) const {
-    const BlockExtent ext = t.real ? block_extent(t.jb, a) : BlockExtent{0, 0};
+  __device__ bool partial(const AttnArgs&, const TileRef& t, int wk, int h, uint32_t& bits) const {
+    const BlockExtent ext{t.code >> 4, t.code & 15};
     if (ext.full()) return false;
     bits = real_key_bits(ext, wk, h);
     return true;
@@ -167,10 +178,12 @@ struct ClusterLayout {
     w.list = chunks + qc * cap;
     return true;
   }
+  __device__ uint32_t prep(const AttnArgs&, int32_t e) const { return static_cast<uint32_t>(e); }
   template <int D>
-  __device__ TileRef decode(const AttnArgs&, int32_t e) const {
+  __device__ TileRef decode(const AttnArgs&, uint32_t e) const {
     TileRef r;
-    r.jb = (e & 63) + 1;          // keys of the chunk
+    r.jb = static_cast<int>(e & 63u) + 1;      // keys of the chunk
+    r.code = 0;
     r.real = true;
     r.off = static_cast<int64_t>(e >> 6) * D;
     return r;
@@ -258,9 +271,9 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   auto load_batch = [&](int b) {
     int pos = min(b * 64 + lane, cnt - 1) + start;
     pos -= pos >= cnt ? cnt : 0;
-    return list[pos];
+    return lay.prep(a, list[pos]);
   };
-  int batch_cur = 0, batch_nxt = 0;     // entries 64 B .. and 64 (B + 1) .. of the pass
+  uint32_t batch_cur = 0, batch_nxt = 0;   // entries 64 B .. and 64 (B + 1) .. of the pass
   auto tile = [&](int t) {
     const int p = t < cnt ? t : cnt - 1;
     return lay.template decode<D>(a, __builtin_amdgcn_readlane(batch_cur, p & 63));
