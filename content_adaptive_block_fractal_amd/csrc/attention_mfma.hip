@@ -483,13 +483,19 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
 
 }  // namespace
 
+// Period of the clock-phased order per tile, in ticks of the 100 MHz clock:
+// about the time one workgroup spends on a kept tile at two workgroups per
+// CU (1.27 us at head_dim 128, 720p / 80%). A sweep a little faster than the
+// workgroups works best (120-135 ticks: 31.4-31.9 ms; 150: 32.7 ms); a much
+// faster one leaves them behind it and loses the reuse (95: 42.5 ms), so
+// the value sits on the slow side of the optimum.
+static uint32_t sweep_ticks_for(int D) { return D == 64 ? 90u : 125u; }
+
 void launch_bsa_forward_mfma(const AttnArgs& args, int D, bool phased, hipStream_t stream) {
   const int64_t n = args.BH * args.nb;
   const unsigned grid = static_cast<unsigned>(n);
   AttnArgs a = args;
-  // measured time per kept tile at two workgroups per CU (about 1.5 us at
-  // head_dim 128); the L2 reuse tolerates an error of a few tens of percent
-  a.sweep_ticks = phased ? (D == 64 ? 90u : 150u) : 0u;
+  a.sweep_ticks = phased ? sweep_ticks_for(D) : 0u;
   if (D == 64)
     hipLaunchKernelGGL((bsa_fwd_mfma<64, BlockListLayout>), dim3(grid), dim3(kThreads), 0, stream,
                        a, BlockListLayout{}, n);
@@ -501,7 +507,7 @@ void launch_bsa_forward_mfma(const AttnArgs& args, int D, bool phased, hipStream
 void launch_bsa_forward_subset_mfma(const AttnArgs& args, int D, bool phased,
                                     const int32_t* q_blocks, int64_t n, hipStream_t stream) {
   AttnArgs a = args;
-  a.sweep_ticks = phased ? (D == 64 ? 90u : 150u) : 0u;
+  a.sweep_ticks = phased ? sweep_ticks_for(D) : 0u;
   SubsetLayout lay{};
   lay.items = q_blocks;
   lay.total = a.BH * a.nb;
