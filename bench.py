@@ -556,6 +556,7 @@ def main():
         },
         "stages_ms": main_run["stage_ms_mean"],
         "stages_ms_median": main_run["stage_ms_median"],
+        "stages_ms_min": main_run["stage_ms_min"],
         "ms_per_layer": mask_ms + attn_ms,
         "mask_share": mask_ms / (mask_ms + attn_ms),
         "kept_tiles": main_run["kept_tiles"],
