@@ -22,7 +22,7 @@ SOURCES = ["api.cpp", "permute.hip", "mask.hip", "attention.hip", "attention_sim
 
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
     # keep the compiler from emitting packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

@@ -412,6 +412,24 @@ void launch_select(const SelectArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((select_rows<EPL>), dim3(grid), dim3(256), 0, stream, a);
 }
 
+// register slots per lane of a row: the smallest instantiation that holds
+// nb values (slots unused by the row still cost instructions in the search)
+void dispatch_select(const SelectArgs& a, int slots, hipStream_t stream) {
+  if (slots <= 1) launch_select<1>(a, stream);
+  else if (slots <= 2) launch_select<2>(a, stream);
+  else if (slots <= 4) launch_select<4>(a, stream);
+  else if (slots <= 8) launch_select<8>(a, stream);
+  else if (slots <= 12) launch_select<12>(a, stream);
+  else if (slots <= 16) launch_select<16>(a, stream);
+  else if (slots <= 20) launch_select<20>(a, stream);
+  else if (slots <= 24) launch_select<24>(a, stream);
+  else if (slots <= 32) launch_select<32>(a, stream);
+  else if (slots <= 48) launch_select<48>(a, stream);
+  else if (slots <= 64) launch_select<64>(a, stream);
+  else if (slots <= 96) launch_select<96>(a, stream);
+  else launch_select<128>(a, stream);
+}
+
 }  // namespace
 
 MaskWorkspace mask_workspace_layout(const Geo& g) {
@@ -440,14 +458,7 @@ void launch_select_matrix(const float* z, int ldz, int64_t rows, int cols, float
   a.Ty = 1;
   a.Tx = 1;
   const int slots = (cols + kWave - 1) / kWave;
-  if (slots <= 1) launch_select<1>(a, stream);
-  else if (slots <= 2) launch_select<2>(a, stream);
-  else if (slots <= 4) launch_select<4>(a, stream);
-  else if (slots <= 8) launch_select<8>(a, stream);
-  else if (slots <= 16) launch_select<16>(a, stream);
-  else if (slots <= 32) launch_select<32>(a, stream);
-  else if (slots <= 64) launch_select<64>(a, stream);
-  else launch_select<128>(a, stream);
+  dispatch_select(a, slots, stream);
 }
 
 void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_count,
@@ -517,14 +528,7 @@ void launch_mask_from_pooled(const Geo& g, float scale, float thr, int topk, boo
   a.kv_index = kv_index;
   a.block_prob = block_prob;
   const int slots = (g.nb + kWave - 1) / kWave;
-  if (slots <= 1) launch_select<1>(a, stream);
-  else if (slots <= 2) launch_select<2>(a, stream);
-  else if (slots <= 4) launch_select<4>(a, stream);
-  else if (slots <= 8) launch_select<8>(a, stream);
-  else if (slots <= 16) launch_select<16>(a, stream);
-  else if (slots <= 32) launch_select<32>(a, stream);
-  else if (slots <= 64) launch_select<64>(a, stream);
-  else launch_select<128>(a, stream);
+  dispatch_select(a, slots, stream);
 }
 
 }  // namespace cabf

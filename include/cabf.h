@@ -36,6 +36,9 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; these are its exports. */
+#pragma GCC visibility push(default)
+
 /* Same declaration as HIP's own; a compatible repeat of the typedef is legal. */
 typedef struct ihipStream_t* hipStream_t;
 
@@ -359,6 +362,8 @@ int cabf_mfma_peak_probe(int32_t workgroups, int32_t iters, float* out, hipStrea
 
 /* Static description of a status code (never NULL). */
 const char* cabf_status_string(int status);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,20 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_library_exports_only_the_c_abi():
+    """Built with hidden visibility: the dynamic symbols the library defines
+    are exactly the functions the header declares."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", cabf.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    assert funcs == set(declared_functions()), sorted(funcs ^ set(declared_functions()))
+
+
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
 def test_geometry_matches_oracle_grid(name):
     w = WORKLOADS[name]
