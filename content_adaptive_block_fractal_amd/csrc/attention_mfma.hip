@@ -34,11 +34,13 @@
 // S^T accumulator layout gives P.
 //
 // Pipeline: K and V tiles stream straight from global memory into LDS rings
-// (global_load_lds_dwordx4; two K slots, three V slots), one LDS object per
+// (global_load_lds_dwordx4; three K slots, two V slots), one LDS object per
 // slot so that reads of the current tile never wait for the tiles in
-// flight. K runs one tile ahead of V: S^T of tile e+1 is issued on the
-// matrix cores before the softmax of tile e runs on the vector ALUs. One
-// barrier per tile, which waits for every copy but the newest V tile.
+// flight. In tile e the products S^T of tile e+1 run on the matrix cores
+// while the vector ALUs compute the softmax numerators of tile e (whose max
+// was taken at the end of tile e-1), then P.V of tile e; the copies of V of
+// e+1 and K of e+3 are issued at the top of the tile. One barrier per tile,
+// which waits for every copy but the newest K tile.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -207,14 +209,14 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   constexpr int kDT = D / 32;   // 32-row d subtiles of O^T
   // Ring slots are separate LDS objects so that the compiler can tell the
   // tile being read from the tiles still streaming in (no wait on them).
-  // K has two slots, V three: V of tile e+2 may still be in flight when tile
-  // e+1 starts. Five 16 KB slots (d = 128) leave room for two workgroups per
-  // CU; the start position and the merge scalars borrow the third V slot
-  // when no tile is in it.
-  __shared__ u32x4 k_slot0[S::kTile], k_slot1[S::kTile];
-  __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile], v_slot2[S::kTile];
+  // K has three slots (K of e+3 streams in while S^T of e+1 is read), V two.
+  // Five 16 KB slots (d = 128) leave room for two workgroups per CU; the
+  // start position and the merge scalars borrow V slots when no tile is in
+  // them.
+  __shared__ u32x4 k_slot0[S::kTile], k_slot1[S::kTile], k_slot2[S::kTile];
+  __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile];
   float* const merge_ml = reinterpret_cast<float*>(v_slot0);   // [2 * 2 * 64]
-  int* const start_shared = reinterpret_cast<int*>(v_slot2);
+  int* const start_shared = reinterpret_cast<int*>(v_slot1);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,39 +308,93 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   }
 
   if (cnt > 0) {
-    // ---- prologue: K/V of tile 0 and K of tile 1 in LDS, S^T of tile 0 ----
+    // Softmax statistics of a tile whose S^T is in `s`: pad keys masked, and
+    // the running max raised (the output and the sum rescaled) when the
+    // tile's max exceeds it by more than kRescaleSlack. They run one tile
+    // ahead of the numerators, at the end of the previous tile, so that the
+    // numerators and the products of a tile are one branch-free stretch of
+    // code that the compiler can interleave.
+    float msub = 0.0f;              // max the numerators are taken against (0 while m = -inf)
+    const float inv_c = 1.0f / c;
+    float raise_at = -INFINITY;     // raw tile max above which m is raised: (m + slack) / c
+    auto stats = [&](f32x16& s, const TileRef& t) {
+      uint32_t bits = 0;
+      if (lay.partial(a, t, wk, h, bits)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
+      }
+      float mt = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      mt = pair_max(mt);
+      if (__any(mt > raise_at)) {
+        const float mn = fmaxf(m, mt * c);
+        const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);   // m = -inf gives 0
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        msub = (m == -INFINITY) ? 0.0f : m;
+        raise_at = (m + kRescaleSlack) * inv_c;
+      }
+    };
+    // Numerators of a tile (bf16, for the product) and their sum (fp32).
+    auto numerators = [&](const f32x16& s, bf16x8 (&pb)[2]) {
+      float ps[4];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // v_exp_f32 directly: arguments are <= 2^3 above the running max and
+        // results below the fp32 normal range are flushed, which bf16 P and the
+        // fp32 sums tolerate
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
+        ps[r & 3] = r < 4 ? pr : ps[r & 3] + pr;
+        pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
+      }
+      l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+
+    // ---- prologue: K of tiles 0-2 and V of tile 0 in LDS, S^T of tile 0 ----
     const uint32_t koff = tile_load_offset<D, false>(wave, lane);
     const uint32_t voff = tile_load_offset<D, true>(wave, lane);
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
     const TileRef t0 = tile(0);
-    const TileRef t1 = tile(1);
+    TileRef t_next = tile(1);
+    TileRef t_after = tile(2);
     issue_tile_load<D>(K + t0.off, k_slot0, koff, wave);
     issue_tile_load<D>(V + t0.off, v_slot0, voff, wave);
-    issue_tile_load<D>(K + t1.off, k_slot1, koff, wave);
-    issue_tile_load<D>(V + t1.off, v_slot1, voff, wave);
+    issue_tile_load<D>(K + t_next.off, k_slot1, koff, wave);
+    issue_tile_load<D>(K + t_after.off, k_slot2, koff, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur = scores(k_slot0);
-    TileRef t_cur = t0;
-    TileRef t_next = tile(1);
+    stats(s_cur, t0);
     __syncthreads();            // tile 0's K slot is refilled next
 
-    // tile e: K of e+1 is in k_slot[(e+1)%2], V of e in v_slot[e%3], V of e+1
-    // in v_slot[(e+1)%3] or still arriving; K and V of e+2 stream into
-    // k_slot[e%2] and v_slot[(e+2)%3]
+    // tile e: K of e+1 is in k_slot[(e+1)%3], K of e+2 in k_slot[(e+2)%3] or
+    // still arriving, V of e in v_slot[e%2]; V of e+1 streams into
+    // v_slot[(e+1)%2] and K of e+3 into k_slot[e%3]. The statistics of tile
+    // e are in m.
     auto body = [&](int e, auto parity, auto phase) {
       constexpr int kOdd = decltype(parity)::value;
       constexpr int kPh = decltype(phase)::value;
-      u32x4* const k_here = kOdd ? k_slot1 : k_slot0;    // slot e % 2
-      u32x4* const k_next = kOdd ? k_slot0 : k_slot1;    // slot (e + 1) % 2
-      u32x4* const v_here = kPh == 0 ? v_slot0 : (kPh == 1 ? v_slot1 : v_slot2);   // e % 3
-      u32x4* const v_fill = kPh == 0 ? v_slot2 : (kPh == 1 ? v_slot0 : v_slot1);   // (e + 2) % 3
-      if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
+      u32x4* const k_fill = kPh == 0 ? k_slot0 : (kPh == 1 ? k_slot1 : k_slot2);   // e % 3
+      u32x4* const k_next = kPh == 0 ? k_slot1 : (kPh == 1 ? k_slot2 : k_slot0);   // (e + 1) % 3
+      u32x4* const v_here = kOdd ? v_slot1 : v_slot0;    // slot e % 2
+      u32x4* const v_fill = kOdd ? v_slot0 : v_slot1;    // slot (e + 1) % 2
+      if (((e + 3) & 63) == 0 && e + 3 < cnt) {   // entry e + 3 opens the next batch
         batch_cur = batch_nxt;
-        batch_nxt = load_batch(((e + 2) >> 6) + 1);
+        batch_nxt = load_batch(((e + 3) >> 6) + 1);
       }
-      const TileRef t2 = tile(e + 2);
+      const TileRef t3 = tile(e + 3);
+      // V of e+1 first: the tile barrier waits for it but not for K of e+3.
+      // Both slots were last read before the previous barrier. The copies
+      // stay at the top of the tile, outside the interleaved stretch below.
+      issue_tile_load<D>(V + t_next.off, v_fill, voff, wave);
+      issue_tile_load<D>(K + t3.off, k_fill, koff, wave);
+      __builtin_amdgcn_sched_barrier(0);
 
       // V^T fragments of tile e (16 transposing reads)
       bf16x8 vf[kDT][2];
@@ -353,54 +409,13 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
             __builtin_memcpy(&vf[dt][st], both, sizeof(bf16x8));
           }
       };
-      // S^T of tile e+1 goes to the matrix cores first; nothing below
-      // depends on it until the end of the tile. The V reads are issued
-      // right behind it and kept there (the scheduler would otherwise sink
-      // each pair next to its product and wait on it), so that their LDS
-      // latency hides behind the matrix work and the softmax.
-      const f32x16 s_nxt = scores(k_next);
+      // S^T of tile e+1 on the matrix cores, the V^T reads of tile e and the
+      // numerators of tile e beside the products.
+      f32x16 s_nxt = scores(k_next);
       read_v();
-      __builtin_amdgcn_sched_barrier(0);
-      // The copies of tile e+2 are issued after this tile's LDS reads, so
-      // that no read of this tile has to be ordered behind them.
-      issue_tile_load<D>(K + t2.off, k_here, koff, wave);
-      issue_tile_load<D>(V + t2.off, v_fill, voff, wave);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // ---- softmax of tile e ------------------------------------------------
-      f32x16& s = s_cur;
-      uint32_t bits = 0;
-      if (lay.partial(a, t_cur, wk, h, bits)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
-      }
-      float mt = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-      mt = pair_max(mt) * c;
-      if (__any(mt > m + kRescaleSlack)) {
-        const float mn = fmaxf(m, mt);
-        const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m - mn);   // m = -inf gives 0
-        m = mn;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      const float msub = (m == -INFINITY) ? 0.0f : m;
       bf16x8 pb[2];
-      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // v_exp_f32 directly: arguments are <= 2^3 above the running max and
-        // results below the fp32 normal range are flushed, which bf16 P and the
-        // fp32 sums tolerate
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
-        ps[r & 3] += pr;
-        pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
-      }
-      l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      numerators(s_cur, pb);
+      asm volatile("" : "+v"(l));   // the sum stays beside the products
 
       // ---- O^T += V^T P^T over this wave's 32 keys --------------------------
 #pragma unroll
@@ -408,12 +423,34 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
 #pragma unroll
         for (int st = 0; st < 2; ++st)
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][st], pb[st], o[dt], 0, 0, 0);
+      // Order for the scheduler: the S^T products interleaved with the K and
+      // V reads and the exponentials, then the P.V products interleaved with
+      // the conversions and sums (masks: 0x100 LDS read, 0x8 matrix, 0x402
+      // vector incl. transcendental).
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < kKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 32 / kKS, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * kDT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 24 / (2 * kDT), 0);
+      }
+
+      // statistics of tile e+1 (past the end of the list a repeat of tile e,
+      // which changes nothing)
+      stats(s_nxt, t_next);
       s_cur = s_nxt;
-      t_cur = t_next;
-      t_next = t2;
-      // Every load but the newest tile copy (V of e+2) has landed: K of e+2
-      // and V of e+1 are in LDS for every wave after the barrier. The empty
+      t_next = t_after;
+      t_after = t3;
+      // Every load but the newest tile copy (K of e+3) has landed: K of e+2
+      // and V of e+1 are in LDS for every wave after the barrier. The
+      // scheduling barrier keeps the wait after this tile's work; the empty
       // asm statements keep the compiler from moving LDS accesses across it.
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(kWaitAllButOneTile<D>());
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -422,13 +459,22 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    for (int e = 0; e < cnt; e += 6) {
+    // Unrolled by six (three K slots, two V slots); each body is entered only
+    // from the one before it, so the compiler's wait bookkeeping follows the
+    // ring exactly.
+    for (int e = 0;;) {
       body(e, I0{}, I0{});
-      if (e + 1 < cnt) body(e + 1, I1{}, I1{});
-      if (e + 2 < cnt) body(e + 2, I0{}, I2{});
-      if (e + 3 < cnt) body(e + 3, I1{}, I0{});
-      if (e + 4 < cnt) body(e + 4, I0{}, I1{});
-      if (e + 5 < cnt) body(e + 5, I1{}, I2{});
+      if (++e >= cnt) break;
+      body(e, I1{}, I1{});
+      if (++e >= cnt) break;
+      body(e, I0{}, I2{});
+      if (++e >= cnt) break;
+      body(e, I1{}, I0{});
+      if (++e >= cnt) break;
+      body(e, I0{}, I1{});
+      if (++e >= cnt) break;
+      body(e, I1{}, I2{});
+      if (++e >= cnt) break;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);    // the last tile copies land before the slots are reused
