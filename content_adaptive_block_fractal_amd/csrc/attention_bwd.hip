@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   // first list entry of the pass (0, or clock-phased: see clock_phased_start)
   __shared__ int start_sh;
   if (wave == 0) {
-    const int st = clock_phased_start(a.kv_count + bh * a.nb, a.nb, cnt, a.sweep_ticks, lane);
+    const int st = clock_phased_start(a.kv_count + bh * a.nb, list, a.nb, cnt, a.sweep_ticks,
+                                      lane);
     if (lane == 0) start_sh = st;
   }
   __syncthreads();
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
   // first list entry of the pass (0, or clock-phased: see clock_phased_start)
   __shared__ int start_sh;
   if (wave == 0) {
-    const int st = clock_phased_start(q_count + bh * a.nb, a.nb, cnt, a.sweep_ticks, lane);
+    const int st = clock_phased_start(q_count + bh * a.nb, list, a.nb, cnt, a.sweep_ticks, lane);
     if (lane == 0) start_sh = st;
   }
   __syncthreads();

@@ -258,8 +258,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   // clock_phased_start). Wave 0 computes it and shares it through LDS, so
   // that all waves agree on it.
   if (wave == 0) {
-    const int start = L::kPhased ? clock_phased_start(a.kv_count + bh * a.nb, a.nb, cnt,
-                                                      a.sweep_ticks, lane)
+    const int start = L::kPhased ? clock_phased_start(a.kv_count + bh * a.nb, w.list, a.nb,
+                                                      cnt, a.sweep_ticks, lane)
                                  : 0;
     if (lane == 0) *start_shared = start;
   }
@@ -531,11 +531,10 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
 
 // Period of the clock-phased order per tile, in ticks of the 100 MHz clock:
 // about the time one workgroup spends on a kept tile at two workgroups per
-// CU (1.27 us at head_dim 128, 720p / 80%). A sweep a little faster than the
-// workgroups works best (120-135 ticks: 31.4-31.9 ms; 150: 32.7 ms); a much
-// faster one leaves them behind it and loses the reuse (95: 42.5 ms), so
-// the value sits on the slow side of the optimum.
-static uint32_t sweep_ticks_for(int D) { return D == 64 ? 90u : 125u; }
+// CU (1.24 us at head_dim 128, 720p / 80%). 110-135 ticks give 30.1-30.4 ms
+// there; a much faster sweep leaves the workgroups behind it and loses the
+// reuse, so the value sits on the slow side of the optimum.
+static uint32_t sweep_ticks_for(int D) { return D == 64 ? 90u : 120u; }
 
 void launch_bsa_forward_mfma(const AttnArgs& args, int D, bool phased, hipStream_t stream) {
   const int64_t n = args.BH * args.nb;

@@ -69,17 +69,18 @@ __device__ inline s16x4 read_v_transposed(const uint16_t* sv_row_chunk) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_row_chunk));
 }
 
-// Where a pass over a list of cnt entries starts, for a clock-phased visit
-// order: at the fraction (clock mod P) / P of the list. Lists of a head
-// spread their entries over the block range alike, so equal fractions mean
-// nearby blocks, and workgroups that run at the same time read the same
-// tiles (which then stay in L2). P must be the same for every workgroup of a
+// Where a pass over an ascending list of cnt block indices (in [0, nb))
+// starts, for a clock-phased visit order: a sweep runs over the block range
+// once every P ticks of the 100 MHz clock, and the pass starts at the first
+// entry at or after the block the sweep has reached ((clock mod P) / P * nb),
+// wrapping around. Workgroups that run at the same time then read about the
+// same tiles (which stay in L2). P must be the same for every workgroup of a
 // head, or clock mod P would not be coherent: P = ticks * the mean length of
 // 64 lists spread evenly over the head (head_counts[0 .. nb)), which all of
 // them sample alike; ticks approximates the time of one tile. Called by one
 // whole wave; every lane returns the same value.
-__device__ inline int clock_phased_start(const int32_t* head_counts, int nb, int cnt,
-                                         uint32_t ticks, int lane) {
+__device__ inline int clock_phased_start(const int32_t* head_counts, const int32_t* list, int nb,
+                                         int cnt, uint32_t ticks, int lane) {
   if (ticks == 0 || cnt <= 1) return 0;
   int total = min(max(head_counts[(lane * nb) >> 6], 1), nb);
 #pragma unroll
@@ -87,7 +88,12 @@ __device__ inline int clock_phased_start(const int32_t* head_counts, int nb, int
   // 32 clock bits wrap every 43 s: one incoherent moment, harmless
   const uint32_t period = static_cast<uint32_t>(max(total >> 6, 1)) * ticks;
   const uint32_t now = static_cast<uint32_t>(__builtin_amdgcn_s_memrealtime());
-  return static_cast<int>(static_cast<uint64_t>(now % period) * cnt / period);
+  const int swept = static_cast<int>(static_cast<uint64_t>(now % period) * nb / period);
+  int before = 0;   // entries below the swept block
+  for (int i = lane; i < cnt; i += 64) before += list[i] < swept ? 1 : 0;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) before += __shfl_xor(before, sh);
+  return before >= cnt ? 0 : before;
 }
 
 template <int D>
