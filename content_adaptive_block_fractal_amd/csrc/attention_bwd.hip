@@ -15,9 +15,9 @@
 //                  dQ^T += K^T dS^T with K^T from transposing LDS reads
 //   bwd_transpose  the kept lists turned around: for every key block, the
 //                  query blocks that keep it, ascending (through a bitmap)
-//   bwd_dkdv<DK>   one workgroup per key block over those query blocks, in
-//                  two passes: DK = false: S = Q K^T, then dV^T += dO^T P;
-//                  DK = true: S = Q K^T and dP = dO V^T, then dK^T += Q^T dS
+//   bwd_dv, bwd_dk one workgroup per key block over those query blocks, in
+//                  two passes: bwd_dv: S = Q K^T, then dV^T += dO^T P;
+//                  bwd_dk: S = Q K^T and dP = dO V^T, then dK^T += Q^T dS
 //                  (Q, dO rows from LDS; K, V in registers; dO^T, Q^T from
 //                  transposing LDS reads). One pass computing both would hold
 //                  K, V and both accumulators per lane (over 256 registers,
@@ -43,13 +43,18 @@ namespace {
 
 using namespace tiles;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ inline float bf16_f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
 
-// D[row] = sum_d dO[row, d] O[row, d]; 16 threads per row
+// D[row] = sum_d dO[row, d] O[row, d], and lse2[row] = lse[row] * log2(e)
+// (+inf where lse is not finite: such a row gets P = 0); 16 threads per row
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot(const uint16_t* __restrict__ o,
                                                   const uint16_t* __restrict__ dout,
-                                                  float* __restrict__ delta, int64_t rows) {
+                                                  const float* __restrict__ lse,
+                                                  float* __restrict__ delta,
+                                                  float* __restrict__ lse2, int64_t rows) {
   constexpr int kPer = D / 16;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -63,7 +68,11 @@ __global__ __launch_bounds__(256) void bwd_rowdot(const uint16_t* __restrict__ o
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (sub == 0 && row < rows) delta[row] = s;
+  if (sub == 0 && row < rows) {
+    delta[row] = s;
+    const float l = lse[row];
+    lse2[row] = __builtin_isfinite(l) ? l * kLog2e : INFINITY;
+  }
 }
 
 // Element offsets (within a 64-row K-swizzled tile) of the 4 * kDT transposing
@@ -94,19 +103,6 @@ __device__ inline bf16x8 transposed_fragment(const uint16_t* tile, int off_lo, i
   return a;
 }
 
-// Bits r of the 16 accumulator rows 8 (r / 4) + 4 h + r % 4 of half `half`
-// (of a 64-row block, keys or queries) that are real tokens of a patch with
-// extent ext.
-__device__ inline uint32_t real_row_bits(const BlockExtent& ext, int half, int h) {
-  uint32_t bits = 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int iy = 4 * half + (r >> 2), ix = 4 * h + (r & 3);
-    bits |= (iy < ext.vy && ix < ext.vx) ? (1u << r) : 0u;
-  }
-  return bits;
-}
-
 // Loads the D-wide rows of one 64-row tile of `a` and `b` (K/V, or Q/dO) into
 // a K-swizzled LDS slot each.
 template <int D>
@@ -123,6 +119,7 @@ __device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t* __restrict__ dop,
                                                       const float* __restrict__ delta,
+                                                      const float* __restrict__ lse2g,
                                                       uint16_t* __restrict__ dqp, int64_t n_items) {
   using S = Stage<D>;
   constexpr int kKS = D / 16;
@@ -148,9 +145,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Q + qrow * D + 16 * ks + 8 * h));
     df[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dop + qrow * D + 16 * ks + 8 * h));
   }
-  const float lse = a.lse[qrow];
-  // a row without keys has lse = -inf: P = exp2(x - inf) = 0 everywhere
-  const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  // +inf for a row without keys (lse = -inf): P = exp2(x - inf) = 0 everywhere
+  const float lse2 = lse2g[qrow];
   const float dlt = delta[qrow];
   const float c = a.scale_log2;
   f32x16 acc[kDT];
@@ -205,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     f32x16 s = rows_times(ks_, qf);
     const f32x16 dp = rows_times(vs_, df);
     const BlockExtent ext = jb >= 0 ? block_extent(jb, a) : BlockExtent{0, 0};
-    const uint32_t bits = ext.full() ? 0xffffu : real_row_bits(ext, wk, h);
+    const uint32_t bits = ext.full() ? 0xffffu : real_accumulator_bits(ext, wk, h);
     bf16x8 dsb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -337,18 +333,256 @@ __global__ __launch_bounds__(256) void bwd_transpose(const uint32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dV (DK = false) or dK (DK = true): one workgroup per key block. Wave
-// (wk, wq): key half wk, query half wq of every tile; lane holds key li of
-// its half. S = Q K^T (and dP = dO V^T) give each lane one key column and 16
-// query rows, which serve as the B operand (contraction over queries) of
-// dV^T += dO^T P, or dK^T += Q^T dS.
+// dV: one workgroup per key block over the query blocks that keep it, laid
+// out as the forward. Wave (wk, wq): key half wk, query half wq of every
+// tile; lane holds key li of its half. S = Q K^T gives each lane one key
+// column and 16 query rows, which serve as the B operand (contraction over
+// queries) of dV^T += dO^T P, dO^T from transposing reads of the dO tile
+// (stored with the forward's V swizzle). In tile e the products S of tile
+// e+1 run beside the exponentials of tile e, then dV^T += dO^T P of tile e;
+// Q of e+2, dO of e+1 and the lse of e+1 arrive during tile e (two-slot
+// rings). Pad query rows of a tile get S = -inf one tile ahead, hence P = 0.
 // ---------------------------------------------------------------------------
-template <int D, bool DK>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16_t* __restrict__ dop,
-                                                        const float* __restrict__ delta,
-                                                        const int32_t* __restrict__ q_count,
-                                                        const int32_t* __restrict__ q_index,
-                                                        uint16_t* __restrict__ grad, int64_t n_items) {
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dv(AttnArgs a, const uint16_t* __restrict__ dop,
+                                                      const float* __restrict__ lse2,
+                                                      const int32_t* __restrict__ q_count,
+                                                      const int32_t* __restrict__ q_index,
+                                                      uint16_t* __restrict__ dvp, int64_t n_items) {
+  using S = Stage<D>;
+  constexpr int kKS = D / 16;
+  constexpr int kDT = D / 32;
+  __shared__ u32x4 q_slot0[S::kTile], q_slot1[S::kTile];
+  __shared__ u32x4 d_slot0[S::kTile], d_slot1[S::kTile];
+  __shared__ f32x4 lse_slot[2][kBlock / 4];   // lse2 of the tile's 64 query rows
+  __shared__ int start_shared;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave & 1, wq = wave >> 1;
+  const int li = lane & 31, h = lane >> 5;
+  const int64_t item = xcd_order(blockIdx.x, n_items);     // bh * nb + key block j
+  const int64_t bh = item / a.nb;
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp) + bh * a.N * D;
+  const uint16_t* __restrict__ dO = dop + bh * a.N * D;
+  const float* __restrict__ lse_h = lse2 + bh * a.N;
+  const int64_t krow = item * kBlock + wk * 32 + li;        // global key row of this lane
+  const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(a.kp);
+  bf16x8 kf[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks)
+    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + krow * D + 16 * ks + 8 * h));
+  const float c = a.scale_log2;
+  f32x16 acc[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+
+  const int cnt = min(max(q_count[item], 0), a.nb);
+  const int32_t* __restrict__ list = q_index + item * a.nb;
+  const int row0 = 32 * wq;                                 // first query row of this wave's half
+  if (wave == 0) {
+    const int st = clock_phased_start(q_count + bh * a.nb, list, a.nb, cnt, a.sweep_ticks, lane);
+    if (lane == 0) start_shared = st;
+  }
+  __syncthreads();
+  const int start = __builtin_amdgcn_readfirstlane(start_shared);
+  // list entries, packed with their extents, 64 at a time a batch ahead (as
+  // in the forward); entry t of the pass is list entry start + t (wrapped),
+  // t clamped to the last one
+  auto load_batch = [&](int b) {
+    int pos = min(b * 64 + lane, cnt - 1) + start;
+    pos -= pos >= cnt ? cnt : 0;
+    return pack_block_entry(a, list[pos]);
+  };
+  uint32_t batch_cur = 0, batch_nxt = 0;
+  auto entry = [&](int t) {
+    const int p = t < cnt ? t : cnt - 1;
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(batch_cur, p & 63));
+  };
+  // first row of query block `p` in the head (block 0 for an invalid entry,
+  // which is masked)
+  auto first_row = [&](uint32_t p) {
+    return static_cast<int64_t>(p != 0u ? packed_block(p) : 0) * kBlock;
+  };
+  // S of this wave's 32 queries x 32 keys from the Q tile in `qt`
+  auto scores = [&](const u32x4* qt) {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const u32x4 u = qt[k_chunk_slot<D>(row0 + li, 2 * ks + h)];
+      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), kf[ks], r, 0, 0, 0);
+    }
+    return r;
+  };
+  // pad query rows (and every row of an invalid entry) -> S = -inf
+  auto mask = [&](f32x16& sv, uint32_t p) {
+    const BlockExtent ext = packed_extent(p);
+    if (!ext.full()) {
+      const uint32_t bits = real_accumulator_bits(ext, wq, h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = ((bits >> r) & 1u) ? sv[r] : -INFINITY;
+    }
+  };
+  // dO^T fragment addressing as the forward's V^T: the lane reads rows
+  // drow + 16 st (+ 8), columns 32 dt + dcol; one element offset per dt
+  const int vgrp = lane >> 4, vsl = lane & 15;
+  const int dcol = 16 * (vgrp & 1) + 4 * (vsl & 3);
+  const int drow = row0 + 4 * (vgrp >> 1) + (vsl >> 2);
+  int daddr[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) {
+    const int cc = 32 * dt + dcol;
+    daddr[dt] = v_chunk_slot<D>(drow, cc >> 3) * 8 + (cc & 7);
+  }
+  float lse_raw = 0.0f;     // the next tile's lse2, one row per thread of wave 0
+
+  if (cnt > 0) {
+    const uint32_t qoff = tile_load_offset<D, false>(wave, lane);
+    const uint32_t doff = tile_load_offset<D, true>(wave, lane);
+    batch_cur = load_batch(0);
+    batch_nxt = load_batch(1);
+    const uint32_t p0 = entry(0);
+    uint32_t p_next = entry(1);
+    if (wave == 0) lse_raw = lse_h[first_row(p0) + lane];
+    issue_tile_load<D>(Q + first_row(p0) * D, q_slot0, qoff, wave);
+    issue_tile_load<D>(dO + first_row(p0) * D, d_slot0, doff, wave);
+    issue_tile_load<D>(Q + first_row(p_next) * D, q_slot1, qoff, wave);
+    if (wave == 0) reinterpret_cast<float*>(lse_slot[0])[lane] = lse_raw;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 s_cur = scores(q_slot0);
+    mask(s_cur, p0);
+    __syncthreads();            // tile 0's Q slot is refilled next
+
+    // tile e: Q of e+1 in q_slot[(e+1)%2], dO of e in d_slot[e%2]; Q of e+2
+    // streams into q_slot[e%2], dO of e+1 into d_slot[(e+1)%2]
+    auto body = [&](int e, auto parity) {
+      constexpr int kOdd = decltype(parity)::value;
+      u32x4* const q_fill = kOdd ? q_slot1 : q_slot0;
+      u32x4* const q_next = kOdd ? q_slot0 : q_slot1;
+      u32x4* const d_here = kOdd ? d_slot1 : d_slot0;
+      u32x4* const d_fill = kOdd ? d_slot0 : d_slot1;
+      if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
+        batch_cur = batch_nxt;
+        batch_nxt = load_batch(((e + 2) >> 6) + 1);
+      }
+      const uint32_t p2 = entry(e + 2);
+      if (wave == 0) lse_raw = lse_h[first_row(p_next) + lane];
+      issue_tile_load<D>(dO + first_row(p_next) * D, d_fill, doff, wave);
+      issue_tile_load<D>(Q + first_row(p2) * D, q_fill, qoff, wave);
+      __builtin_amdgcn_sched_barrier(0);
+
+      f32x16 s_nxt = scores(q_next);
+      const uint16_t* sd = reinterpret_cast<const uint16_t*>(d_here);
+      bf16x8 vf[kDT][2];
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint16_t* pd = sd + daddr[dt] + 16 * st * D;
+          const s16x4 both[2] = {read_v_transposed(pd), read_v_transposed(pd + 8 * D)};
+          __builtin_memcpy(&vf[dt][st], both, sizeof(bf16x8));
+        }
+      bf16x8 pb[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lv = lse_slot[kOdd][(row0 >> 2) + 2 * g + h];   // rows row0 + 8 g + 4 h ..
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * g + x;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -lv[x]));
+          pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][st], pb[st], acc[dt], 0, 0, 0);
+      // the S products interleaved with the LDS reads and the exponentials,
+      // then the dV products with the conversions (masks: 0x100 LDS read,
+      // 0x8 matrix, 0x402 vector incl. transcendental)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < kKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 32 / kKS, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * kDT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 8 / (2 * kDT), 0);
+      }
+      mask(s_nxt, p_next);
+      s_cur = s_nxt;
+      p_next = p2;
+      // every copy of the tile has landed; the lse of e+1 goes to its slot
+      // (last read in tile e-1) before the barrier
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (wave == 0) reinterpret_cast<float*>(lse_slot[kOdd ^ 1])[lane] = lse_raw;
+      __syncthreads();
+    };
+    for (int e = 0;;) {
+      body(e, std::integral_constant<int, 0>{});
+      if (++e >= cnt) break;
+      body(e, std::integral_constant<int, 1>{});
+      if (++e >= cnt) break;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);    // the last tile copies land before the slots are reused
+  __syncthreads();
+
+  // ---- add the two query halves, store (pad keys: 0) -----------------------
+  float* const part = reinterpret_cast<float*>(wk ? q_slot1 : q_slot0);
+  static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
+  if (wq == 1) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+  }
+  __syncthreads();
+  if (wq == 1) return;
+  const BlockExtent kext = block_extent(static_cast<int>(item % a.nb), a);
+  const float sc = kext.real(wk * 32 + li) ? 1.0f : 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * h;
+      float x[4];
+#pragma unroll
+      for (int xx = 0; xx < 4; ++xx) {
+        const int r = 4 * g + xx;
+        x[xx] = (acc[dt][r] + part[(dt * 16 + r) * 64 + lane]) * sc;
+      }
+      uint2 w;
+      w.x = static_cast<uint32_t>(f32_to_bf16_rne(x[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[1])) << 16);
+      w.y = static_cast<uint32_t>(f32_to_bf16_rne(x[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16);
+      *reinterpret_cast<uint2*>(dvp + krow * D + d) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK: one workgroup per key block. Wave (wk, wq): key half wk, query half wq
+// of every tile; lane holds key li of its half. S = Q K^T and dP = dO V^T
+// give each lane one key column and 16 query rows, which serve as the B
+// operand (contraction over queries) of dK^T += Q^T dS.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t* __restrict__ dop,
+                                                      const float* __restrict__ delta,
+                                                      const float* __restrict__ lse2,
+                                                      const int32_t* __restrict__ q_count,
+                                                      const int32_t* __restrict__ q_index,
+                                                      uint16_t* __restrict__ grad, int64_t n_items) {
   using S = Stage<D>;
   constexpr int kKS = D / 16;
   constexpr int kDT = D / 32;
@@ -365,20 +599,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
   const int64_t bh = item / a.nb;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp) + bh * a.N * D;
   const uint16_t* __restrict__ dO = dop + bh * a.N * D;
-  const float* __restrict__ lse_h = a.lse + bh * a.N;
+  const float* __restrict__ lse_h = lse2 + bh * a.N;
   const float* __restrict__ dl_h = delta + bh * a.N;
   const int64_t krow = item * kBlock + wk * 32 + li;        // global key row of this lane
   const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(a.kp);
   const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(a.vp);
-  bf16x8 kf[kKS], vf[DK ? kKS : 1];
+  bf16x8 kf[kKS], vf[kKS];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks)
     kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + krow * D + 16 * ks + 8 * h));
-  if constexpr (DK) {
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks)
-      vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
-  }
+  for (int ks = 0; ks < kKS; ++ks)
+    vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
   const float c = a.scale_log2;
   f32x16 acc[kDT];
 #pragma unroll
@@ -416,11 +648,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
     }
     return r;
   };
-  // P (dV pass) or dS (dK pass) of query block ib in bf16, from S (and dP)
+  // dS of query block ib in bf16, from S and dP
   auto weights = [&](int ib, const f32x16& s, const f32x16& dp, const float (&vec)[2][kBlock],
                      bf16x8 (&wb)[2]) {
     const BlockExtent ext = block_extent(ib, a);
-    const uint32_t bits = ext.full() ? 0xffffu : real_row_bits(ext, wq, h);
+    const uint32_t bits = ext.full() ? 0xffffu : real_accumulator_bits(ext, wq, h);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int m = row0 + 8 * g + 4 * h;                  // rows m .. m + 3
@@ -428,25 +660,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
       // tiles being copied, and does not wait for the copies; vector-cast
       // reads made it wait)
       const float lv[4] = {vec[0][m], vec[0][m + 1], vec[0][m + 2], vec[0][m + 3]};
-      float dv4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (DK) {
-        dv4[0] = vec[1][m];
-        dv4[1] = vec[1][m + 1];
-        dv4[2] = vec[1][m + 2];
-        dv4[3] = vec[1][m + 3];
-      }
+      const float dv4[4] = {vec[1][m], vec[1][m + 1], vec[1][m + 2], vec[1][m + 3]};
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * g + x;
         const float p = ((bits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x])) : 0.0f;
-        if constexpr (DK)
-          wb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dv4[x]));
-        else
-          wb[r >> 3][r & 7] = static_cast<__bf16>(p);
+        wb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dv4[x]));
       }
     }
   };
-  // dV^T += dO^T P (xs: the dO tile), or dK^T += Q^T dS (xs: the Q tile)
+  // dK^T += Q^T dS (xs: the Q tile)
   auto accumulate = [&](const u32x4* xs, const bf16x8 (&wb)[2]) {
     const uint16_t* xt = reinterpret_cast<const uint16_t*>(xs);
 #pragma unroll
@@ -456,7 +679,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             transposed_fragment(xt, toff[dt][st][0], toff[dt][st][1]), wb[st], acc[dt], 0, 0, 0);
   };
-  // lse (base 2, +inf for rows without keys) and D of a query block -> vec
+  // lse2 and D of a query block -> vec
   // slot, in two steps: the loads are issued before the tile copies (waiting
   // for them later does not wait for the copies) and stored at the end of
   // the tile
@@ -464,21 +687,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
   auto fetch_vecs = [&](int ib) {
     if (tid < kBlock) {
       l_raw = lse_h[static_cast<int64_t>(ib) * kBlock + tid];
-      if constexpr (DK) d_raw = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
+      d_raw = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
     }
   };
   auto store_vecs = [&](float (&vec)[2][kBlock]) {
     if (tid < kBlock) {
-      vec[0][tid] = l_raw == -INFINITY ? INFINITY : l_raw * kLog2e;
-      if constexpr (DK) vec[1][tid] = d_raw;
+      vec[0][tid] = l_raw;
+      vec[1][tid] = d_raw;
     }
   };
 
   const uint32_t off = tile_load_offset<D, false>(wave, lane);
   auto q_tile = [&](int ib) { return Q + static_cast<int64_t>(ib) * kBlock * D; };
   auto d_tile = [&](int ib) { return dO + static_cast<int64_t>(ib) * kBlock * D; };
-  if constexpr (DK) {
-   if (cnt > 0) {
+  if (cnt > 0) {
     // dK pass: Q and dO of tile e+1 stream in while tile e is computed
     int ib_cur = block_of(0);
     fetch_vecs(ib_cur);
@@ -512,51 +734,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
       body(e, std::integral_constant<int, 0>{});
       if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
     }
-   }
-  } else {
-   if (cnt > 0) {
-    // dV pass, software-pipelined as the forward: Q runs one tile ahead of
-    // dO, and S of tile e+1 is issued to the matrix cores before P of tile e
-    // is formed. Tile e: Q of e+1 in q_slot[(e+1)%2], dO of e in d_slot[e%2];
-    // Q of e+2 streams into q_slot[e%2], dO of e+1 into d_slot[(e+1)%2].
-    int ib_cur = block_of(0), ib_nxt = block_of(1);
-    fetch_vecs(ib_cur);
-    issue_tile_load<D>(q_tile(ib_cur), q_slot0, off, wave);
-    issue_tile_load<D>(d_tile(ib_cur), d_slot0, off, wave);
-    issue_tile_load<D>(q_tile(ib_nxt), q_slot1, off, wave);
-    store_vecs(vec_slot[0]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x16 s_cur = rows_times(q_slot0, kf);
-    __syncthreads();            // tile 0's Q slot is refilled next
-    const f32x16 no_dp = {};
-    auto body = [&](int e, auto parity) {
-      constexpr int kOdd = decltype(parity)::value;
-      u32x4* const q_here = kOdd ? q_slot1 : q_slot0;    // slot e % 2
-      u32x4* const q_next = kOdd ? q_slot0 : q_slot1;
-      u32x4* const d_here = kOdd ? d_slot1 : d_slot0;
-      u32x4* const d_next = kOdd ? d_slot0 : d_slot1;
-      const int ib2 = block_of(e + 2);                     // clamped: redundant but in bounds
-      fetch_vecs(ib_nxt);
-      __builtin_amdgcn_sched_barrier(0);        // the vector loads stay ahead of the copies
-      issue_tile_load<D>(q_tile(ib2), q_here, off, wave);
-      issue_tile_load<D>(d_tile(ib_nxt), d_next, off, wave);
-      const f32x16 s_nxt = rows_times(q_next, kf);
-      bf16x8 wb[2];
-      weights(ib_cur, s_cur, no_dp, vec_slot[kOdd], wb);
-      accumulate(d_here, wb);
-      store_vecs(vec_slot[kOdd ^ 1]);
-      s_cur = s_nxt;
-      ib_cur = ib_nxt;
-      ib_nxt = ib2;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    };
-    for (int e = 0; e < cnt; e += 2) {
-      body(e, std::integral_constant<int, 0>{});
-      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
-    }
-   }
   }
 
   // ---- add the two query halves, scale dK, store (pad keys: 0) -------------
@@ -573,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(AttnArgs a, const uint16
   const BlockExtent kext = block_extent(static_cast<int>(item % a.nb), a);
   const bool real_key = kext.real(wk * 32 + li);
   // dK carries the softmax scale s; pad keys get 0
-  const float sc = real_key ? (DK ? a.scale_log2 * kLn2 : 1.0f) : 0.0f;
+  const float sc = real_key ? a.scale_log2 * kLn2 : 0.0f;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -603,6 +780,7 @@ BwdWorkspace bwd_workspace_layout(const Geo& g) {
   w.words = (g.nb + 31) / 32;
   size_t o = 0;
   w.delta = o;    o += align256(static_cast<size_t>(g.BH) * g.N * sizeof(float));
+  w.lse2 = o;     o += align256(static_cast<size_t>(g.BH) * g.N * sizeof(float));
   w.bitmap = o;   o += align256(static_cast<size_t>(g.BH) * g.nb * w.words * sizeof(uint32_t));
   w.q_count = o;  o += align256(static_cast<size_t>(g.BH) * g.nb * sizeof(int32_t));
   w.q_index = o;  o += align256(static_cast<size_t>(g.BH) * g.nb * g.nb * sizeof(int32_t));
@@ -617,6 +795,7 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   const BwdWorkspace w = bwd_workspace_layout(g);
   char* ws = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws + w.delta);
+  float* lse2 = reinterpret_cast<float*>(ws + w.lse2);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + w.bitmap);
   int32_t* q_count = reinterpret_cast<int32_t*>(ws + w.q_count);
   int32_t* q_index = reinterpret_cast<int32_t*>(ws + w.q_index);
@@ -624,9 +803,11 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   const uint16_t* o16 = static_cast<const uint16_t*>(op);
   const uint16_t* do16 = static_cast<const uint16_t*>(dop);
   if (g.D == 64)
-    hipLaunchKernelGGL((bwd_rowdot<64>), grid_for(rows, 16), dim3(256), 0, stream, o16, do16, delta, rows);
+    hipLaunchKernelGGL((bwd_rowdot<64>), grid_for(rows, 16), dim3(256), 0, stream, o16, do16, lse,
+                       delta, lse2, rows);
   else
-    hipLaunchKernelGGL((bwd_rowdot<128>), grid_for(rows, 16), dim3(256), 0, stream, o16, do16, delta, rows);
+    hipLaunchKernelGGL((bwd_rowdot<128>), grid_for(rows, 16), dim3(256), 0, stream, o16, do16, lse,
+                       delta, lse2, rows);
   const int64_t words = g.BH * g.nb * w.words;
   hipLaunchKernelGGL(bwd_fill_zero, grid_for(words, 256), dim3(256), 0, stream, bitmap, words);
   const int64_t entries = g.BH * g.nb * g.nb;
@@ -641,7 +822,7 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   a.vp = vp;
   a.kv_count = kv_count;
   a.kv_index = kv_index;
-  a.lse = const_cast<float*>(lse);
+  a.lse = nullptr;            // the kernels read lse2
   a.scale_log2 = scale * kLog2e;
   a.nb = g.nb;
   a.Ty = g.Ty;
@@ -665,19 +846,19 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   a_dv.sweep_ticks = t_dv;
   a_dk.sweep_ticks = t_dk;
   if (g.D == 64) {
-    hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta, dq16,
-                       items);
-    hipLaunchKernelGGL((bwd_dkdv<64, false>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16,
-                       delta, q_count, q_index, dv16, items);
-    hipLaunchKernelGGL((bwd_dkdv<64, true>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
-                       delta, q_count, q_index, dk16, items);
+    hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta,
+                       lse2, dq16, items);
+    hipLaunchKernelGGL((bwd_dv<64>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16, lse2,
+                       q_count, q_index, dv16, items);
+    hipLaunchKernelGGL((bwd_dk<64>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
+                       delta, lse2, q_count, q_index, dk16, items);
   } else {
-    hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta, dq16,
-                       items);
-    hipLaunchKernelGGL((bwd_dkdv<128, false>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16,
-                       delta, q_count, q_index, dv16, items);
-    hipLaunchKernelGGL((bwd_dkdv<128, true>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
-                       delta, q_count, q_index, dk16, items);
+    hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta,
+                       lse2, dq16, items);
+    hipLaunchKernelGGL((bwd_dv<128>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16, lse2,
+                       q_count, q_index, dv16, items);
+    hipLaunchKernelGGL((bwd_dk<128>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
+                       delta, lse2, q_count, q_index, dk16, items);
   }
 }
 

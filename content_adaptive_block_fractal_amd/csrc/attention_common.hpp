@@ -53,6 +53,33 @@ __device__ inline BlockExtent block_extent(int b, const AttnArgs& a) {
   return e;
 }
 
+// Bit r set when row 8 * (r / 4) + 4 * h + r % 4 of half `half` of a 64-token
+// block (the rows or columns one lane holds in a 32x32 accumulator; block
+// row k is patch cell (k / 8, k % 8)) is a real token of the patch.
+__device__ inline uint32_t real_accumulator_bits(const BlockExtent& ext, int half, int h) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int iy = 4 * half + (r >> 2), ix = 4 * h + (r & 3);
+    bits |= (iy < ext.vy && ix < ext.vx) ? (1u << r) : 0u;
+  }
+  return bits;
+}
+
+// A block-list entry as the tile loops hold it: the block index in bits
+// 0..23 and its real extent in bits 24..31 (vy << 4 | vx; 0 for an entry
+// outside [0, nb)), so that a loop finds partial blocks without a division.
+__device__ inline uint32_t pack_block_entry(const AttnArgs& a, int32_t e) {
+  if (static_cast<unsigned>(e) >= static_cast<unsigned>(a.nb)) return 0u;
+  const BlockExtent ext = block_extent(e, a);
+  return static_cast<uint32_t>(e) | (static_cast<uint32_t>((ext.vy << 4) | ext.vx) << 24);
+}
+__device__ inline BlockExtent packed_extent(uint32_t p) {
+  const int code = static_cast<int>(p >> 24);
+  return BlockExtent{code >> 4, code & 15};
+}
+__device__ inline int packed_block(uint32_t p) { return static_cast<int>(p & 0xffffffu); }
+
 __device__ inline float load_elem(const float* p) { return *p; }
 __device__ inline float load_elem(const uint16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);

@@ -58,16 +58,6 @@ namespace {
 using namespace tiles;
 constexpr float kRescaleSlack = 8.0f;   // base-2 headroom before the running max is raised
 
-// s_waitcnt immediate: vmcnt = the loads of one tile copy (Stage::kIters),
-// expcnt and lgkmcnt not waited on (gfx9 encoding: vmcnt[3:0] and [15:14],
-// expcnt[6:4], lgkmcnt[11:8])
-template <int D>
-constexpr int kWaitAllButOneTile() {
-  constexpr int n = Stage<D>::kIters;
-  static_assert(n < 64, "vmcnt range");
-  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-
 // A list entry decoded: element offset of its 64 K/V rows in the head, and
 // what the layout needs to mask it (block index, or number of valid keys).
 struct TileRef {
@@ -76,18 +66,6 @@ struct TileRef {
   int code;     // block list: the extent code of the entry (see BlockListLayout::prep)
   bool real;
 };
-
-// Bit r of the mask: key 8 * (4 wk + r / 4) + 4 h + r % 4 of the lane's
-// accumulator is a real token of the block.
-__device__ inline uint32_t real_key_bits(const BlockExtent& ext, int wk, int h) {
-  uint32_t bits = 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int iy = 4 * wk + (r >> 2), ix = 4 * h + (r & 3);
-    bits |= (iy < ext.vy && ix < ext.vx) ? (1u << r) : 0u;
-  }
-  return bits;
-}
 
 // What a workgroup computes: 64 consecutive rows of Q and O starting at the
 // global row qrow0 (over all batch-heads), of which the first `rows` are
@@ -113,22 +91,16 @@ struct BlockListLayout {
     w.list = a.kv_index + item * a.nb;
     return true;
   }
-  // A list entry as the batch holds it: the block index in bits 0..23 and
-  // its real extent in bits 24..31 (vy << 4 | vx; 0 for an entry outside
-  // [0, nb)). Computed once per batch of 64 entries, one per lane, so the
-  // tile loop needs no division to find a block's extent.
-  __device__ uint32_t prep(const AttnArgs& a, int32_t e) const {
-    if (static_cast<unsigned>(e) >= static_cast<unsigned>(a.nb)) return 0u;
-    const BlockExtent ext = block_extent(e, a);
-    return static_cast<uint32_t>(e) | (static_cast<uint32_t>((ext.vy << 4) | ext.vx) << 24);
-  }
+  // A list entry as the batch holds it (pack_block_entry), computed once per
+  // batch of 64 entries, one per lane.
+  __device__ uint32_t prep(const AttnArgs& a, int32_t e) const { return pack_block_entry(a, e); }
   // entries outside [0, nb) load block 0 and are masked out entirely
   template <int D>
   __device__ TileRef decode(const AttnArgs&, uint32_t p) const {
     TileRef r;
     r.code = static_cast<int>(p >> 24);
     r.real = r.code != 0;
-    r.jb = static_cast<int>(p & 0xffffffu);
+    r.jb = packed_block(p);
     r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
     return r;
   }
@@ -136,7 +108,7 @@ struct BlockListLayout {
   __device__ bool partial(const AttnArgs&, const TileRef& t, int wk, int h, uint32_t& bits) const {
     const BlockExtent ext{t.code >> 4, t.code & 15};
     if (ext.full()) return false;
-    bits = real_key_bits(ext, wk, h);
+    bits = real_accumulator_bits(ext, wk, h);
     return true;
   }
 };

@@ -124,6 +124,16 @@ __device__ inline uint32_t tile_load_offset(int wave, int lane) {
   return static_cast<uint32_t>((row * D + chunk * 8) * 2);
 }
 
+// s_waitcnt immediate: vmcnt = the loads of one tile copy (Stage::kIters),
+// expcnt and lgkmcnt not waited on (gfx9 encoding: vmcnt[3:0] and [15:14],
+// expcnt[6:4], lgkmcnt[11:8])
+template <int D>
+constexpr int kWaitAllButOneTile() {
+  constexpr int n = Stage<D>::kIters;
+  static_assert(n < 64, "vmcnt range");
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 template <int D>
 __device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4* slot,
                                                 uint32_t off, int wave) {

@@ -42,7 +42,7 @@ void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_cou
 // transposed lists (query blocks of every key block).
 struct BwdWorkspace {
   int words;
-  size_t delta, bitmap, q_count, q_index, total;
+  size_t delta, lse2, bitmap, q_count, q_index, total;
 };
 BwdWorkspace bwd_workspace_layout(const Geo& g);
 void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const void* vp,

@@ -228,8 +228,8 @@ int cabf_bsa_forward_subset(const cabf_geom* g, cabf_dtype dtype,
                             void* op, float* lse, unsigned flags, hipStream_t stream);
 
 /* Bytes of workspace cabf_bsa_backward needs (0 if the geometry is
- * unsupported): fp32 D per row, a kept-list bitmap and the transposed lists
- * (about B*heads*nb*nb*4 bytes). */
+ * unsupported): fp32 D and base-2 lse per row, a kept-list bitmap and the
+ * transposed lists (about B*heads*nb*nb*4 bytes). */
 size_t cabf_bsa_backward_workspace_bytes(const cabf_geom* g);
 
 /* Gradients of cabf_bsa_forward (NABLA summary, closing remarks: the sparse
@@ -240,7 +240,8 @@ size_t cabf_bsa_backward_workspace_bytes(const cabf_geom* g);
  *   dS_nm = P_nm (do_n . v_m - D_n),
  *   dq_n = scale sum_m dS_nm k_m, dk_m = scale sum_n dS_nm q_n,
  *   dv_m = sum_n P_nm do_n.
- * Pad query rows do not contribute; pad rows of dq, dk, dv are zero.
+ * Pad query rows do not contribute; pad rows of dq, dk, dv are zero. A row
+ * whose lse is not finite (-inf: a row without kept keys) gets P = 0.
  * dtype: CABF_BF16 only (else CABF_EUNSUPPORTED). qp, kp, vp, op (the
  * forward's output) and dop: [B, heads, N, head_dim] bf16; lse: the
  * forward's [B, heads, N] fp32; kv_count / kv_index: the forward's lists
