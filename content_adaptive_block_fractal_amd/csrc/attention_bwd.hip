@@ -75,25 +75,24 @@ __global__ __launch_bounds__(256) void bwd_rowdot(const uint16_t* __restrict__ o
   }
 }
 
-// Element offsets (within a 64-row K-swizzled tile) of the 4 * kDT transposing
-// reads that give a lane its fragments of X^T (d x rows) for rows
-// rbase + 4 (vgrp / 2) + vsl / 4 + 16 st + 8 half and columns 32 dt + vcol;
-// constant per lane.
+// Element offsets (within a 64-row K-swizzled tile) of the transposing reads
+// that give a lane its fragments of X^T (d x rows) for rows
+// rbase + 4 (vgrp / 2) + vsl / 4 + 16 st + 8 half and columns 32 dt + vcol:
+// off[dt][half] for st = 0; the K swizzle repeats every 16 rows, so st = 1
+// is 16 D elements further (kept out of the array, one register each less).
 template <int D>
-__device__ inline void transposed_offsets(int (&off)[D / 32][2][2], int rbase, int lane) {
+__device__ inline void transposed_offsets(int (&off)[D / 32][2], int rbase, int lane) {
   const int vgrp = lane >> 4, vsl = lane & 15;
   const int vcol = 16 * (vgrp & 1) + 4 * (vsl & 3);
   const int vrow = rbase + 4 * (vgrp >> 1) + (vsl >> 2);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int row = vrow + 16 * st + 8 * hf;
-        const int col = 32 * dt + vcol;
-        off[dt][st][hf] = k_chunk_slot<D>(row, col >> 3) * 8 + (col & 7);
-      }
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = vrow + 8 * hf;
+      const int col = 32 * dt + vcol;
+      off[dt][hf] = k_chunk_slot<D>(row, col >> 3) * 8 + (col & 7);
+    }
 }
 
 __device__ inline bf16x8 transposed_fragment(const uint16_t* tile, int off_lo, int off_hi) {
@@ -158,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   const int cnt = min(max(a.kv_count[item], 0), a.nb);
   const int32_t* __restrict__ list = a.kv_index + item * a.nb;
   const int key0 = 32 * wk;
-  int toff[kDT][2][2];
+  int toff[kDT][2];
   transposed_offsets<D>(toff, key0, lane);
   // first list entry of the pass (0, or clock-phased: see clock_phased_start)
   __shared__ int start_sh;
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
 #pragma unroll
       for (int st = 0; st < 2; ++st)
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            transposed_fragment(kt, toff[dt][st][0], toff[dt][st][1]), dsb[st], acc[dt], 0, 0, 0);
+            transposed_fragment(kt + 16 * st * D, toff[dt][0], toff[dt][1]), dsb[st], acc[dt], 0, 0, 0);
   };
 
   if (cnt > 0) {
@@ -621,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
   const int cnt = min(max(q_count[item], 0), a.nb);
   const int32_t* __restrict__ list = q_index + item * a.nb;
   const int row0 = 32 * wq;                                 // first query row of this wave's half
-  int toff[kDT][2][2];
+  int toff[kDT][2];
   transposed_offsets<D>(toff, row0, lane);
   // first list entry of the pass (0, or clock-phased: see clock_phased_start)
   __shared__ int start_sh;
@@ -677,7 +676,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
 #pragma unroll
       for (int st = 0; st < 2; ++st)
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            transposed_fragment(xt, toff[dt][st][0], toff[dt][st][1]), wb[st], acc[dt], 0, 0, 0);
+            transposed_fragment(xt + 16 * st * D, toff[dt][0], toff[dt][1]), wb[st], acc[dt], 0, 0, 0);
   };
   // lse2 and D of a query block -> vec
   // slot, in two steps: the loads are issued before the tile copies (waiting

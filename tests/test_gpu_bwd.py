@@ -98,6 +98,30 @@ def test_backward_rows_without_blocks_and_unused_keys():
             compare_grad(got[0, hd], r, valid, f"arbitrary lists head {hd} {nm}")
 
 
+
+def test_backward_nonfinite_lse_rows_contribute_nothing():
+    """A row whose lse is not finite gets P = 0 (documented for cabf_bsa_backward): its dq is 0
+    and dK, dV equal those of a run where that row's dO is zero instead (whose P is finite but
+    whose dS and dO products vanish). Deterministic order, so the sums agree exactly."""
+    g, og, s, qp, kp, vp, cnt, idx, op, lse, dop = setup(3, 21, 35, 2, 128, 0.5, None, seed=6)
+    rows = [(0, 64 + 3), (1, 2 * 64 + 17), (0, 5 * 64 + 40)]     # real rows of kept blocks
+    lse_bad = lse.clone()
+    dop_zero = dop.clone()
+    for (hd, r), val in zip(rows, (float("inf"), float("nan"), float("-inf"))):
+        assert torch.isfinite(lse[0, hd, r])
+        lse_bad[0, hd, r] = val
+        dop_zero[0, hd, r] = 0
+    dq_a, dk_a, dv_a = cabf.bsa_backward(qp, kp, vp, op, lse_bad, dop, cnt, idx, g, s,
+                                         deterministic=True)
+    dq_b, dk_b, dv_b = cabf.bsa_backward(qp, kp, vp, op, lse, dop_zero, cnt, idx, g, s,
+                                         deterministic=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk_a.float(), dk_b.float()) and torch.equal(dv_a.float(), dv_b.float())
+    for hd, r in rows:
+        assert torch.all(dq_a[0, hd, r] == 0)
+        dq_b[0, hd, r] = 0
+    assert torch.equal(dq_a.float(), dq_b.float())
+
 def test_backward_full_size_sampled():
     """Wan-14B 720p at 80% sparsity: the gradients of two key blocks (every
     query block that keeps them is included, so those rows are exact) and the
