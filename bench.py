@@ -139,8 +139,8 @@ def kernel_source_digest() -> str:
 
 
 def profiled_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    or None when that summary was taken on a different kernel source or workload."""
+    """Bytes per attention launch beyond L2 (MALL/HBM) from the committed rocprofv3 counter
+    summary, or None when that summary was taken on a different kernel source or workload."""
     path = os.path.join(ROOT, "profiles", f"bsa_fwd_mfma.{workload}.hbm.md")
     if not os.path.exists(path):
         return None
@@ -404,18 +404,18 @@ def measure_semantic(cabf, steps: int, warmup: int, seed: int):
     }
 
 
-def cpu_baseline(q, k, v, w, thr, sta, budget_s):
-    """The CPU oracle on a bounded sample of the same layer: head 0's permute and
-    block mask (all rows) plus attention for the first query blocks that fit the
-    time budget. Single thread (BLAS pinned to one thread)."""
+def _oracle_head_sample(job):
+    """One worker of the CPU baseline: the oracle on one head (float32 copies of its raster Q, K,
+    V): permute and block mask of all rows, then attention of query blocks in order until the
+    time budget is spent. Single thread (BLAS pinned to one thread)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
-    g = oracle.Grid(w.T, w.H, w.W, w.P)
-    scale = 1.0 / math.sqrt(w.head_dim)
-    f = lambda t: t[0, 0].float().cpu().numpy().astype(np.float64)
-    qh, kh, vh = f(q), f(k), f(v)
+    qh, kh, vh, grid, head_dim, thr, sta, budget_s = job
+    g = oracle.Grid(*grid)
+    scale = 1.0 / math.sqrt(head_dim)
+    qh, kh, vh = (x.astype(np.float64) for x in (qh, kh, vh))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         qp, kp, vp = oracle.permute(qh, g), oracle.permute(kh, g), oracle.permute(vh, g)
@@ -431,20 +431,52 @@ def cpu_baseline(q, k, v, w, thr, sta, budget_s):
             t_attn += time.perf_counter() - t1
             tiles += int(cnt_all[done])
             done += 1
-    flops = 4.0 * 64 * 64 * w.head_dim * tiles
-    t_equiv = t_attn + t_mask * done / g.nb     # mask cost of the sampled rows
-    per_layer_s = (t_mask + t_attn / done * g.nb) * w.heads * w.batch
+    return dict(flops=4.0 * 64 * 64 * head_dim * tiles, tiles=tiles, done=done, nb=g.nb,
+                t_mask=t_mask, t_attn=t_attn, t_equiv=t_attn + t_mask * done / g.nb)
+
+
+def cpu_baseline(q, k, v, w, thr, sta, budget_s):
+    """The CPU oracle on a bounded sample of the same layer, heads sharded over worker processes
+    (one per host core, up to 16 and up to the head count): each worker runs head h's permute and
+    block mask (all rows) plus attention for the first query blocks that fit the time budget, on
+    one thread. value = the sum of the workers' throughputs (each measured while all run)."""
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, 16, w.heads))
+    f = lambda t, hd: t[0, hd].float().cpu().numpy()
+    jobs = [(f(q, hd), f(k, hd), f(v, hd), (w.T, w.H, w.W, w.P), w.head_dim, thr, sta, budget_s)
+            for hd in range(workers)]
+    results = None
+    if workers > 1:
+        try:
+            import multiprocessing as mp
+            from concurrent.futures import ProcessPoolExecutor
+            with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+                results = list(ex.map(_oracle_head_sample, jobs))
+        except Exception as exc:       # a host without working worker processes: one core
+            print(f"cpu baseline: worker processes unavailable ({exc!r}); using one core",
+                  file=sys.stderr)
+            results = None
+    if results is None:
+        workers = 1
+        results = [_oracle_head_sample(jobs[0])]
+    value = sum(r["flops"] / r["t_equiv"] for r in results) / 1e12
+    r0 = results[0]
+    per_layer_s = (r0["t_mask"] + r0["t_attn"] / r0["done"] * r0["nb"]) * w.heads * w.batch
+    tiles = sum(r["tiles"] for r in results)
+    done = sum(r["done"] for r in results)
     return {
-        "value": flops / t_equiv / 1e12,
+        "value": value,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"head 0 of {w.heads}: permute + block mask of all {g.nb} rows ({t_mask:.2f} s, "
-                   f"charged pro rata) + attention of the first {done} query blocks "
-                   f"({tiles} kept tiles, {t_attn:.2f} s); fp64 numpy, 1 thread"),
-        "extrapolated_s_per_layer": per_layer_s,
+        "sample": (f"heads 0-{workers - 1} of {w.heads}, one worker process and thread each: "
+                   f"permute + block mask of all {r0['nb']} rows of the head ({r0['t_mask']:.2f} s "
+                   f"on head 0, charged pro rata) + attention of its first query blocks "
+                   f"({done} query blocks, {tiles} kept tiles in all, ~{budget_s:.0f} s per worker); "
+                   f"fp64 numpy"),
+        "extrapolated_s_per_layer_one_core": per_layer_s,
         "host_cpu": platform.processor() or platform.machine(),
-        "host_cores_available": len(os.sched_getaffinity(0)),
+        "host_cores_available": cores,
     }
 
 
@@ -550,7 +582,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": attn_tflops / PEAK_BF16_TFLOPS,
             "traffic": profiled_traffic(w.name),
-            "traffic_unit": "bytes per launch (2 x FETCH_SIZE + WRITE_SIZE)",
+            "traffic_unit": ("bytes per launch beyond L2: FETCH_SIZE and WRITE_SIZE, each scaled by "
+                             "what it reads for a 1 GiB copy in the same profiled run"),
             "algorithmic_unit": "4*64*64*head_dim flops per kept 64x64 tile",
             "avg_launch_ms": attn_ms,
         },
