@@ -543,6 +543,10 @@ def main():
     flags = cabf.BSA_DETERMINISTIC if args.deterministic else 0
     main_run = measure(args.sparsity, sta, args.steps, args.warmup, flags, fused=not args.unfused)
     ms = main_run["wall_ms"]
+    # spread of the block logits (scaled, base e): mean over rows of the row std of log p
+    _, _, probs = cabf.build_block_mask(qp, kp, geom, main_run["thr"], sta, return_probs=True)
+    logit_std = float(torch.log(probs.clamp_min(1e-30)).std(dim=-1).mean().item())
+    del probs
     attn_ms = main_run["stage_ms_mean"]["attention"]
     mask_ms = main_run["stage_ms_mean"]["mask"]
     attn_tflops = main_run["flops"] / (attn_ms * 1e-3) / 1e12
@@ -567,6 +571,7 @@ def main():
             "grid": [w.T, w.H, w.W], "patch": w.P,
             "target_sparsity": args.sparsity, "sparsity": main_run["sparsity"],
             "thr": main_run["thr"], "sta_window": list(sta) if sta else None,
+            "block_logit_row_std": logit_std,
             "parallelism": "single GPU",
             "attention_order": "list order (deterministic)" if args.deterministic
                                else "clock-phased start (default)",
