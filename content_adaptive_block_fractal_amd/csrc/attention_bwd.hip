@@ -106,9 +106,9 @@ __device__ inline bf16x8 transposed_fragment(const uint16_t* tile, int off_lo, i
 // a K-swizzled LDS slot each.
 template <int D>
 __device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, u32x4* sa, u32x4* sb,
-                                          uint32_t off, int wave) {
-  issue_tile_load<D>(a, sa, off, wave);
-  issue_tile_load<D>(b, sb, off, wave);
+                                          uint32_t off, int wave, int real_rows = kBlock) {
+  issue_tile_load<D>(a, sa, off, wave, real_rows);
+  issue_tile_load<D>(b, sb, off, wave, real_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -172,18 +172,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   // use, and read out with readlane (as in the forward): no list load is
   // waited on per tile. Entry t of the pass is list entry start + t
   // (wrapped); t is clamped to the last one.
+  // Entries are packed with their extents (pack_block_entry).
   auto load_batch = [&](int b) {
     int pos = min(b * 64 + lane, cnt - 1) + start;
     pos -= pos >= cnt ? cnt : 0;
-    return list[pos];
+    return pack_block_entry(a, list[pos]);
   };
-  int batch_cur = 0, batch_nxt = 0;     // entries 64 B .. and 64 (B + 1) .. of the pass
+  uint32_t batch_cur = 0, batch_nxt = 0;   // entries 64 B .. and 64 (B + 1) .. of the pass
   auto tile_of = [&](int t) {
     const int p = t < cnt ? t : cnt - 1;
-    const int jb = __builtin_amdgcn_readlane(batch_cur, p & 63);
-    const bool real = static_cast<unsigned>(jb) < static_cast<unsigned>(a.nb);
-    return real ? jb : -1;
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(batch_cur, p & 63));
   };
+  // first element of key block `p` (block 0 for an invalid entry, which is masked) and
+  // the rows of it that can hold real keys
+  auto tile_off = [&](uint32_t p) {
+    return static_cast<int64_t>(p != 0u ? packed_block(p) : 0) * kBlock * D;
+  };
+  auto tile_rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };
   // S^T or dP^T of this wave's 32 keys: rows of `tile` against fragments f
   auto rows_times = [&](const u32x4* tile, const bf16x8 (&f)[kKS]) {
     f32x16 r;
@@ -196,10 +201,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     }
     return r;
   };
-  auto step = [&](int jb, const u32x4* ks_, const u32x4* vs_) {
+  auto step = [&](uint32_t p, const u32x4* ks_, const u32x4* vs_) {
     f32x16 s = rows_times(ks_, qf);
     const f32x16 dp = rows_times(vs_, df);
-    const BlockExtent ext = jb >= 0 ? block_extent(jb, a) : BlockExtent{0, 0};
+    const BlockExtent ext = packed_extent(p);
     const uint32_t bits = ext.full() ? 0xffffu : real_accumulator_bits(ext, wk, h);
     bf16x8 dsb[2];
 #pragma unroll
@@ -220,9 +225,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     const uint32_t off = tile_load_offset<D, false>(wave, lane);
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
-    int jb_cur = tile_of(0);
-    load_pair<D>(K + static_cast<int64_t>(max(jb_cur, 0)) * kBlock * D,
-                 V + static_cast<int64_t>(max(jb_cur, 0)) * kBlock * D, k_slot0, v_slot0, off, wave);
+    uint32_t jb_cur = tile_of(0);
+    load_pair<D>(K + tile_off(jb_cur), V + tile_off(jb_cur), k_slot0, v_slot0, off, wave,
+                 tile_rows(jb_cur));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     auto body = [&](int e, auto parity) {
@@ -235,10 +240,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
         batch_cur = batch_nxt;
         batch_nxt = load_batch(((e + 1) >> 6) + 1);
       }
-      const int jb_next = tile_of(e + 1);
+      const uint32_t jb_next = tile_of(e + 1);
       if (e + 1 < cnt)
-        load_pair<D>(K + static_cast<int64_t>(max(jb_next, 0)) * kBlock * D,
-                     V + static_cast<int64_t>(max(jb_next, 0)) * kBlock * D, kn, vn, off, wave);
+        load_pair<D>(K + tile_off(jb_next), V + tile_off(jb_next), kn, vn, off, wave,
+                     tile_rows(jb_next));
       step(jb_cur, kc, vc);
       jb_cur = jb_next;
       __builtin_amdgcn_s_waitcnt(0);
@@ -448,9 +453,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dv(AttnArgs a, const uint16_t
     const uint32_t p0 = entry(0);
     uint32_t p_next = entry(1);
     if (wave == 0) lse_raw = lse_h[first_row(p0) + lane];
-    issue_tile_load<D>(Q + first_row(p0) * D, q_slot0, qoff, wave);
-    issue_tile_load<D>(dO + first_row(p0) * D, d_slot0, doff, wave);
-    issue_tile_load<D>(Q + first_row(p_next) * D, q_slot1, qoff, wave);
+    auto rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };   // rows with real queries
+    issue_tile_load<D>(Q + first_row(p0) * D, q_slot0, qoff, wave, rows(p0));
+    issue_tile_load<D>(dO + first_row(p0) * D, d_slot0, doff, wave, rows(p0));
+    issue_tile_load<D>(Q + first_row(p_next) * D, q_slot1, qoff, wave, rows(p_next));
     if (wave == 0) reinterpret_cast<float*>(lse_slot[0])[lane] = lse_raw;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -472,8 +478,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dv(AttnArgs a, const uint16_t
       }
       const uint32_t p2 = entry(e + 2);
       if (wave == 0) lse_raw = lse_h[first_row(p_next) + lane];
-      issue_tile_load<D>(dO + first_row(p_next) * D, d_fill, doff, wave);
-      issue_tile_load<D>(Q + first_row(p2) * D, q_fill, qoff, wave);
+      issue_tile_load<D>(dO + first_row(p_next) * D, d_fill, doff, wave, rows(p_next));
+      issue_tile_load<D>(Q + first_row(p2) * D, q_fill, qoff, wave, rows(p2));
       __builtin_amdgcn_sched_barrier(0);
 
       f32x16 s_nxt = scores(q_next);

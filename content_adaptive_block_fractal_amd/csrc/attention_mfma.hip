@@ -64,6 +64,7 @@ struct TileRef {
   int64_t off;
   int jb;
   int code;     // block list: the extent code of the entry (see BlockListLayout::prep)
+  int rows;     // rows of the tile that can hold a used token (the rest need not be loaded)
   bool real;
 };
 
@@ -101,6 +102,7 @@ struct BlockListLayout {
     r.code = static_cast<int>(p >> 24);
     r.real = r.code != 0;
     r.jb = packed_block(p);
+    r.rows = 8 * (r.code >> 4);     // patch rows below vy are pads (0 for an invalid entry)
     r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
     return r;
   }
@@ -158,6 +160,7 @@ struct ClusterLayout {
     TileRef r;
     r.jb = static_cast<int>(e & 63u) + 1;      // keys of the chunk
     r.code = 0;
+    r.rows = r.jb;
     r.real = true;
     r.off = static_cast<int64_t>(e >> 6) * D;
     return r;
@@ -335,10 +338,10 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     const TileRef t0 = tile(0);
     TileRef t_next = tile(1);
     TileRef t_after = tile(2);
-    issue_tile_load<D>(K + t0.off, k_slot0, koff, wave);
-    issue_tile_load<D>(V + t0.off, v_slot0, voff, wave);
-    issue_tile_load<D>(K + t_next.off, k_slot1, koff, wave);
-    issue_tile_load<D>(K + t_after.off, k_slot2, koff, wave);
+    issue_tile_load<D>(K + t0.off, k_slot0, koff, wave, t0.rows);
+    issue_tile_load<D>(V + t0.off, v_slot0, voff, wave, t0.rows);
+    issue_tile_load<D>(K + t_next.off, k_slot1, koff, wave, t_next.rows);
+    issue_tile_load<D>(K + t_after.off, k_slot2, koff, wave, t_after.rows);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur = scores(k_slot0);
@@ -364,8 +367,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
       // V of e+1 first: the tile barrier waits for it but not for K of e+3.
       // Both slots were last read before the previous barrier. The copies
       // stay at the top of the tile, outside the interleaved stretch below.
-      issue_tile_load<D>(V + t_next.off, v_fill, voff, wave);
-      issue_tile_load<D>(K + t3.off, k_fill, koff, wave);
+      issue_tile_load<D>(V + t_next.off, v_fill, voff, wave, t_next.rows);
+      issue_tile_load<D>(K + t3.off, k_fill, koff, wave, t3.rows);
       __builtin_amdgcn_sched_barrier(0);
 
       // V^T fragments of tile e (16 transposing reads)
