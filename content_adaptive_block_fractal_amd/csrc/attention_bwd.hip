@@ -636,11 +636,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
   }
   __syncthreads();
   const int start = __builtin_amdgcn_readfirstlane(start_sh);
-  auto block_of = [&](int t) {
-    int p = (t < cnt ? t : cnt - 1) + start;
-    p -= p >= cnt ? cnt : 0;
-    return list[p];
+  // list entries, packed with their extents, 64 at a time a batch ahead (as
+  // in the forward); entry t of the pass is list entry start + t (wrapped),
+  // t clamped to the last one
+  auto load_batch = [&](int b) {
+    int pos = min(b * 64 + lane, cnt - 1) + start;
+    pos -= pos >= cnt ? cnt : 0;
+    return pack_block_entry(a, list[pos]);
   };
+  uint32_t batch_cur = 0, batch_nxt = 0;
+  auto entry = [&](int t) {
+    const int p = t < cnt ? t : cnt - 1;
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(batch_cur, p & 63));
+  };
+  auto rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };   // rows with real queries
   // S or dP of this wave's 32 queries x 32 keys: rows of `tile` against f
   auto rows_times = [&](const u32x4* tile, const bf16x8 (&f)[kKS]) {
     f32x16 r;
@@ -654,9 +663,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
     return r;
   };
   // dS of query block ib in bf16, from S and dP
-  auto weights = [&](int ib, const f32x16& s, const f32x16& dp, const float (&vec)[2][kBlock],
+  auto weights = [&](uint32_t pe, const f32x16& s, const f32x16& dp, const float (&vec)[2][kBlock],
                      bf16x8 (&wb)[2]) {
-    const BlockExtent ext = block_extent(ib, a);
+    const BlockExtent ext = packed_extent(pe);
     const uint32_t bits = ext.full() ? 0xffffu : real_accumulator_bits(ext, wq, h);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -689,7 +698,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
   // for them later does not wait for the copies) and stored at the end of
   // the tile
   float l_raw = 0.0f, d_raw = 0.0f;
-  auto fetch_vecs = [&](int ib) {
+  auto fetch_vecs = [&](uint32_t pe) {
+    const int ib = packed_block(pe);
     if (tid < kBlock) {
       l_raw = lse_h[static_cast<int64_t>(ib) * kBlock + tid];
       d_raw = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
@@ -703,13 +713,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
   };
 
   const uint32_t off = tile_load_offset<D, false>(wave, lane);
-  auto q_tile = [&](int ib) { return Q + static_cast<int64_t>(ib) * kBlock * D; };
-  auto d_tile = [&](int ib) { return dO + static_cast<int64_t>(ib) * kBlock * D; };
+  auto q_tile = [&](uint32_t pe) {
+    return Q + static_cast<int64_t>(packed_block(pe)) * kBlock * D;
+  };
+  auto d_tile = [&](uint32_t pe) {
+    return dO + static_cast<int64_t>(packed_block(pe)) * kBlock * D;
+  };
   if (cnt > 0) {
     // dK pass: Q and dO of tile e+1 stream in while tile e is computed
-    int ib_cur = block_of(0);
+    batch_cur = load_batch(0);
+    batch_nxt = load_batch(1);
+    uint32_t ib_cur = entry(0);
     fetch_vecs(ib_cur);
-    load_pair<D>(q_tile(ib_cur), d_tile(ib_cur), q_slot0, d_slot0, off, wave);
+    load_pair<D>(q_tile(ib_cur), d_tile(ib_cur), q_slot0, d_slot0, off, wave, rows(ib_cur));
     store_vecs(vec_slot[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -719,11 +735,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
       u32x4* const dc = kOdd ? d_slot1 : d_slot0;
       u32x4* const qn = kOdd ? q_slot0 : q_slot1;
       u32x4* const dn = kOdd ? d_slot0 : d_slot1;
-      const int ib_next = block_of(e + 1);
+      if (((e + 1) & 63) == 0 && e + 1 < cnt) {   // entry e + 1 opens the next batch
+        batch_cur = batch_nxt;
+        batch_nxt = load_batch(((e + 1) >> 6) + 1);
+      }
+      const uint32_t ib_next = entry(e + 1);
       if (e + 1 < cnt) {
         fetch_vecs(ib_next);
         __builtin_amdgcn_sched_barrier(0);      // the vector loads stay ahead of the copies
-        load_pair<D>(q_tile(ib_next), d_tile(ib_next), qn, dn, off, wave);
+        load_pair<D>(q_tile(ib_next), d_tile(ib_next), qn, dn, off, wave, rows(ib_next));
       }
       const f32x16 sv = rows_times(qc, kf);
       const f32x16 dp = rows_times(dc, vf);
