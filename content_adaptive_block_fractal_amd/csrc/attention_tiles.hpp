@@ -136,9 +136,10 @@ constexpr int kWaitAllButOneTile() {
 
 // Rows of the tile at or past `real_rows` hold no token the kernel uses (pad
 // rows of a partial patch, keys past a chunk, or every row of an invalid
-// entry): a pass that covers only such rows reloads pass 0's source instead
-// (L1/L2-resident, finite data where masked rows read it), which keeps the
-// number of loads per copy, and so the vmcnt bookkeeping, unchanged.
+// entry): a wave's share of a pass that covers only such rows reloads its
+// share of pass 0 instead (L1/L2-resident, finite data where masked rows read
+// it), which keeps the number of loads per copy, and so the vmcnt
+// bookkeeping, unchanged.
 template <int D>
 __device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4* slot,
                                                 uint32_t off, int wave, int real_rows = kBlock) {
@@ -151,8 +152,9 @@ __device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4*
   asm volatile("" : "+v"(o));
 #pragma unroll
   for (int i = 0; i < S::kIters; ++i) {
-    const int first_row = i * S::kRowsPerIter;
-    const uint16_t* src = first_row < real_rows ? tile_src + first_row * D : tile_src;
+    // rows of this wave's instruction: first_row .. first_row + kRowsPerIter / kWaves - 1
+    const int first_row = i * S::kRowsPerIter + wave * (S::kRowsPerIter / kWaves);
+    const uint16_t* src = first_row < real_rows ? tile_src + i * S::kRowsPerIter * D : tile_src;
     const char* base = reinterpret_cast<const char*>(src);
     asm volatile("" : "+s"(base));
     __builtin_amdgcn_global_load_lds(base + o, slot + (i * kWaves + wave) * 64, 16, 0, 0);
