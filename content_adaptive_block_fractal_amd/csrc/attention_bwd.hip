@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
   constexpr int kDT = D / 32;
   __shared__ u32x4 q_slot0[S::kTile], q_slot1[S::kTile];
   __shared__ u32x4 d_slot0[S::kTile], d_slot1[S::kTile];
-  __shared__ __align__(16) float vec_slot[2][2][kBlock];   // [slot][lse2, D][row]
+  __shared__ f32x4 vec_slot[2][2][kBlock / 4];   // [slot][lse2, D][4 rows]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -662,23 +662,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
     }
     return r;
   };
-  // dS of query block ib in bf16, from S and dP
-  auto weights = [&](uint32_t pe, const f32x16& s, const f32x16& dp, const float (&vec)[2][kBlock],
+  // dS of the tile's query block `pe` in bf16, from S and dP; pad query rows
+  // (partial patches only: a uniform branch) get S = -inf, hence P = dS = 0
+  auto weights = [&](uint32_t pe, f32x16 s, const f32x16& dp, const f32x4 (&vec)[2][kBlock / 4],
                      bf16x8 (&wb)[2]) {
     const BlockExtent ext = packed_extent(pe);
-    const uint32_t bits = ext.full() ? 0xffffu : real_accumulator_bits(ext, wq, h);
+    if (!ext.full()) {
+      const uint32_t bits = real_accumulator_bits(ext, wq, h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int m = row0 + 8 * g + 4 * h;                  // rows m .. m + 3
-      // element reads (the compiler then sees that they do not touch the
-      // tiles being copied, and does not wait for the copies; vector-cast
-      // reads made it wait)
-      const float lv[4] = {vec[0][m], vec[0][m + 1], vec[0][m + 2], vec[0][m + 3]};
-      const float dv4[4] = {vec[1][m], vec[1][m + 1], vec[1][m + 2], vec[1][m + 3]};
+      const int m4 = (row0 >> 2) + 2 * g + h;              // rows row0 + 8 g + 4 h .. + 3
+      const f32x4 lv = vec[0][m4];
+      const f32x4 dv4 = vec[1][m4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * g + x;
-        const float p = ((bits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x])) : 0.0f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x]));
         wb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dv4[x]));
       }
     }
@@ -705,10 +707,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
       d_raw = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
     }
   };
-  auto store_vecs = [&](float (&vec)[2][kBlock]) {
+  auto store_vecs = [&](f32x4 (&vec)[2][kBlock / 4]) {
     if (tid < kBlock) {
-      vec[0][tid] = l_raw;
-      vec[1][tid] = d_raw;
+      reinterpret_cast<float*>(vec[0])[tid] = l_raw;
+      reinterpret_cast<float*>(vec[1])[tid] = d_raw;
     }
   };
 
