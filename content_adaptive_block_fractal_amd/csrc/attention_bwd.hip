@@ -201,16 +201,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     }
     return r;
   };
-  auto step = [&](uint32_t p, const u32x4* ks_, const u32x4* vs_) {
+  // pad keys of a partial patch (a uniform branch) get S = -inf, hence P = dS = 0
+  auto step = [&](uint32_t pe, const u32x4* ks_, const u32x4* vs_) {
     f32x16 s = rows_times(ks_, qf);
     const f32x16 dp = rows_times(vs_, df);
-    const BlockExtent ext = packed_extent(p);
-    const uint32_t bits = ext.full() ? 0xffffu : real_accumulator_bits(ext, wk, h);
+    const BlockExtent ext = packed_extent(pe);
+    if (!ext.full()) {
+      const uint32_t bits = real_accumulator_bits(ext, wk, h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
+    }
     bf16x8 dsb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = ((bits >> r) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2)) : 0.0f;
-      dsb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dlt));
+      const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+      dsb[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dlt));
     }
     const uint16_t* kt = reinterpret_cast<const uint16_t*>(ks_);
 #pragma unroll
