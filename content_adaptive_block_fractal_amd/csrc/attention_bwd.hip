@@ -106,9 +106,10 @@ __device__ inline bf16x8 transposed_fragment(const uint16_t* tile, int off_lo, i
 // a K-swizzled LDS slot each.
 template <int D>
 __device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, u32x4* sa, u32x4* sb,
-                                          uint32_t off, int wave, int real_rows = kBlock) {
-  issue_tile_load<D>(a, sa, off, wave, real_rows);
-  issue_tile_load<D>(b, sb, off, wave, real_rows);
+                                          uint32_t off, int wave, int real_rows = kBlock,
+                                          int real_cols = kP) {
+  issue_tile_load<D>(a, sa, off, wave, real_rows, real_cols);
+  issue_tile_load<D>(b, sb, off, wave, real_rows, real_cols);
 }
 
 // ---------------------------------------------------------------------------
@@ -189,6 +190,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     return static_cast<int64_t>(p != 0u ? packed_block(p) : 0) * kBlock * D;
   };
   auto tile_rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };
+  auto tile_cols = [&](uint32_t p) { return packed_extent(p).vx; };
   // S^T or dP^T of this wave's 32 keys: rows of `tile` against fragments f
   auto rows_times = [&](const u32x4* tile, const bf16x8 (&f)[kKS]) {
     f32x16 r;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     batch_nxt = load_batch(1);
     uint32_t jb_cur = tile_of(0);
     load_pair<D>(K + tile_off(jb_cur), V + tile_off(jb_cur), k_slot0, v_slot0, off, wave,
-                 tile_rows(jb_cur));
+                 tile_rows(jb_cur), tile_cols(jb_cur));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     auto body = [&](int e, auto parity) {
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
       const uint32_t jb_next = tile_of(e + 1);
       if (e + 1 < cnt)
         load_pair<D>(K + tile_off(jb_next), V + tile_off(jb_next), kn, vn, off, wave,
-                     tile_rows(jb_next));
+                     tile_rows(jb_next), tile_cols(jb_next));
       step(jb_cur, kc, vc);
       jb_cur = jb_next;
       __builtin_amdgcn_s_waitcnt(0);
@@ -458,10 +460,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dv(AttnArgs a, const uint16_t
     const uint32_t p0 = entry(0);
     uint32_t p_next = entry(1);
     if (wave == 0) lse_raw = lse_h[first_row(p0) + lane];
-    auto rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };   // rows with real queries
-    issue_tile_load<D>(Q + first_row(p0) * D, q_slot0, qoff, wave, rows(p0));
-    issue_tile_load<D>(dO + first_row(p0) * D, d_slot0, doff, wave, rows(p0));
-    issue_tile_load<D>(Q + first_row(p_next) * D, q_slot1, qoff, wave, rows(p_next));
+    // rows and patch columns that can hold real queries
+    auto rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };
+    auto cols = [&](uint32_t p) { return packed_extent(p).vx; };
+    issue_tile_load<D>(Q + first_row(p0) * D, q_slot0, qoff, wave, rows(p0), cols(p0));
+    issue_tile_load<D>(dO + first_row(p0) * D, d_slot0, doff, wave, rows(p0), cols(p0));
+    issue_tile_load<D>(Q + first_row(p_next) * D, q_slot1, qoff, wave, rows(p_next), cols(p_next));
     if (wave == 0) reinterpret_cast<float*>(lse_slot[0])[lane] = lse_raw;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -483,8 +487,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dv(AttnArgs a, const uint16_t
       }
       const uint32_t p2 = entry(e + 2);
       if (wave == 0) lse_raw = lse_h[first_row(p_next) + lane];
-      issue_tile_load<D>(dO + first_row(p_next) * D, d_fill, doff, wave, rows(p_next));
-      issue_tile_load<D>(Q + first_row(p2) * D, q_fill, qoff, wave, rows(p2));
+      issue_tile_load<D>(dO + first_row(p_next) * D, d_fill, doff, wave, rows(p_next),
+                         cols(p_next));
+      issue_tile_load<D>(Q + first_row(p2) * D, q_fill, qoff, wave, rows(p2), cols(p2));
       __builtin_amdgcn_sched_barrier(0);
 
       f32x16 s_nxt = scores(q_next);
@@ -654,7 +659,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
     const int p = t < cnt ? t : cnt - 1;
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(batch_cur, p & 63));
   };
-  auto rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };   // rows with real queries
+  // rows and patch columns that can hold real queries
+  auto rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };
+  auto cols = [&](uint32_t p) { return packed_extent(p).vx; };
   // S or dP of this wave's 32 queries x 32 keys: rows of `tile` against f
   auto rows_times = [&](const u32x4* tile, const bf16x8 (&f)[kKS]) {
     f32x16 r;
@@ -732,7 +739,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
     batch_nxt = load_batch(1);
     uint32_t ib_cur = entry(0);
     fetch_vecs(ib_cur);
-    load_pair<D>(q_tile(ib_cur), d_tile(ib_cur), q_slot0, d_slot0, off, wave, rows(ib_cur));
+    load_pair<D>(q_tile(ib_cur), d_tile(ib_cur), q_slot0, d_slot0, off, wave, rows(ib_cur),
+                 cols(ib_cur));
     store_vecs(vec_slot[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -750,7 +758,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
       if (e + 1 < cnt) {
         fetch_vecs(ib_next);
         __builtin_amdgcn_sched_barrier(0);      // the vector loads stay ahead of the copies
-        load_pair<D>(q_tile(ib_next), d_tile(ib_next), qn, dn, off, wave, rows(ib_next));
+        load_pair<D>(q_tile(ib_next), d_tile(ib_next), qn, dn, off, wave, rows(ib_next),
+                     cols(ib_next));
       }
       const f32x16 sv = rows_times(qc, kf);
       const f32x16 dp = rows_times(dc, vf);

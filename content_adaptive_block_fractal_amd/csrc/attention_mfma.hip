@@ -65,6 +65,7 @@ struct TileRef {
   int jb;
   int code;     // block list: the extent code of the entry (see BlockListLayout::prep)
   int rows;     // rows of the tile that can hold a used token (the rest need not be loaded)
+  int cols;     // patch columns (row % 8) that can hold one
   bool real;
 };
 
@@ -102,7 +103,8 @@ struct BlockListLayout {
     r.code = static_cast<int>(p >> 24);
     r.real = r.code != 0;
     r.jb = packed_block(p);
-    r.rows = 8 * (r.code >> 4);     // patch rows below vy are pads (0 for an invalid entry)
+    r.rows = 8 * (r.code >> 4);     // patch rows at or past vy are pads (0 for an invalid entry)
+    r.cols = r.code & 15;           // and so are columns at or past vx
     r.off = static_cast<int64_t>(r.real ? r.jb : 0) * kBlock * D;
     return r;
   }
@@ -161,6 +163,7 @@ struct ClusterLayout {
     r.jb = static_cast<int>(e & 63u) + 1;      // keys of the chunk
     r.code = 0;
     r.rows = r.jb;
+    r.cols = kP;
     r.real = true;
     r.off = static_cast<int64_t>(e >> 6) * D;
     return r;
@@ -338,10 +341,11 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     const TileRef t0 = tile(0);
     TileRef t_next = tile(1);
     TileRef t_after = tile(2);
-    issue_tile_load<D>(K + t0.off, k_slot0, koff, wave, t0.rows);
-    issue_tile_load<D>(V + t0.off, v_slot0, voff, wave, t0.rows);
-    issue_tile_load<D>(K + t_next.off, k_slot1, koff, wave, t_next.rows);
-    issue_tile_load<D>(K + t_after.off, k_slot2, koff, wave, t_after.rows);
+    issue_tile_load<D>(K + t0.off, k_slot0, koff, wave, t0.rows, t0.cols);
+    issue_tile_load<D>(V + t0.off, v_slot0, voff, wave, t0.rows, t0.cols);
+    issue_tile_load<D>(K + t_next.off, k_slot1, koff, wave, t_next.rows, t_next.cols);
+    issue_tile_load<D>(K + t_after.off, k_slot2, koff, wave, t_after.rows,
+                       t_after.cols);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur = scores(k_slot0);
@@ -367,8 +371,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
       // V of e+1 first: the tile barrier waits for it but not for K of e+3.
       // Both slots were last read before the previous barrier. The copies
       // stay at the top of the tile, outside the interleaved stretch below.
-      issue_tile_load<D>(V + t_next.off, v_fill, voff, wave, t_next.rows);
-      issue_tile_load<D>(K + t3.off, k_fill, koff, wave, t3.rows);
+      issue_tile_load<D>(V + t_next.off, v_fill, voff, wave, t_next.rows, t_next.cols);
+      issue_tile_load<D>(K + t3.off, k_fill, koff, wave, t3.rows, t3.cols);
       __builtin_amdgcn_sched_barrier(0);
 
       // V^T fragments of tile e (16 transposing reads)

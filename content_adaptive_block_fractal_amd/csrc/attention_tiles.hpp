@@ -134,15 +134,18 @@ constexpr int kWaitAllButOneTile() {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-// Rows of the tile at or past `real_rows` hold no token the kernel uses (pad
-// rows of a partial patch, keys past a chunk, or every row of an invalid
-// entry): a wave's share of a pass that covers only such rows reloads its
-// share of pass 0 instead (L1/L2-resident, finite data where masked rows read
-// it), which keeps the number of loads per copy, and so the vmcnt
-// bookkeeping, unchanged.
+// Rows of the tile at or past `real_rows`, or whose patch column (row % 8) is
+// at or past `real_cols`, hold no token the kernel uses (pad rows and columns
+// of a partial patch, keys past a chunk, or every row of an invalid entry): a
+// wave's share of a pass that covers only such rows reloads its share of
+// pass 0 instead (L1/L2-resident, finite data where masked rows read it),
+// which keeps the number of loads per copy, and so the vmcnt bookkeeping,
+// unchanged. A wave's share is 4 rows at d = 128 (half a patch row) and 8 at
+// d = 64 (a whole patch row).
 template <int D>
 __device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4* slot,
-                                                uint32_t off, int wave, int real_rows = kBlock) {
+                                                uint32_t off, int wave, int real_rows = kBlock,
+                                                int real_cols = kP) {
   using S = Stage<D>;
   // An empty asm makes each load's scalar base (tile and pass) and lane
   // offset opaque, so the compiler cannot fold (base + lane offset) once and
@@ -154,7 +157,8 @@ __device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4*
   for (int i = 0; i < S::kIters; ++i) {
     // rows of this wave's instruction: first_row .. first_row + kRowsPerIter / kWaves - 1
     const int first_row = i * S::kRowsPerIter + wave * (S::kRowsPerIter / kWaves);
-    const uint16_t* src = first_row < real_rows ? tile_src + i * S::kRowsPerIter * D : tile_src;
+    const bool used = first_row < real_rows && (first_row & (kP - 1)) < real_cols;
+    const uint16_t* src = used ? tile_src + i * S::kRowsPerIter * D : tile_src;
     const char* base = reinterpret_cast<const char*>(src);
     asm volatile("" : "+s"(base));
     __builtin_amdgcn_global_load_lds(base + o, slot + (i * kWaves + wave) * 64, 16, 0, 0);
