@@ -15,17 +15,18 @@
 //                  dQ^T += K^T dS^T with K^T from transposing LDS reads
 //   bwd_transpose  the kept lists turned around: for every key block, the
 //                  query blocks that keep it, ascending (through a bitmap)
-//   bwd_dv, bwd_dk one workgroup per key block over those query blocks, in
-//                  two passes: bwd_dv: S = Q K^T, then dV^T += dO^T P;
-//                  bwd_dk: S = Q K^T and dP = dO V^T, then dK^T += Q^T dS
-//                  (Q, dO rows from LDS; K, V in registers; dO^T, Q^T from
-//                  transposing LDS reads). One pass computing both would hold
-//                  K, V and both accumulators per lane (over 256 registers,
-//                  one workgroup per CU); split, each pass runs two per CU,
-//                  which outweighs recomputing S in the second.
+//   bwd_dkv        one workgroup of two four-wave groups per key block over
+//                  those query blocks, both groups on the same Q and dO
+//                  tiles: the dV group forms S = Q K^T, then dV^T += dO^T P;
+//                  the dK group S and dP = dO V^T, then dK^T += Q^T dS (Q, dO
+//                  rows from LDS; K, V in registers; dO^T, Q^T from
+//                  transposing LDS reads). Holding K, V and both accumulators
+//                  in every lane would take over 256 registers; split over
+//                  the groups, each wave stays within 256.
 // Every gradient kernel splits the 64 x 64 tile over 4 waves (two halves of
-// each side) and adds the two partial sums of a row once at the end, so every
-// result is deterministic. Pad query rows do not contribute and get dq = 0;
+// each side) and adds the two partial sums of a row once at the end, so with
+// list-order walks (the deterministic flag) every result is reproducible.
+// Pad query rows do not contribute and get dq = 0;
 // pad key rows get dk = dv = 0.
 #include <hip/hip_runtime.h>
 
@@ -344,42 +345,50 @@ __global__ __launch_bounds__(256) void bwd_transpose(const uint32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dV: one workgroup per key block over the query blocks that keep it, laid
-// out as the forward. Wave (wk, wq): key half wk, query half wq of every
-// tile; lane holds key li of its half. S = Q K^T gives each lane one key
-// column and 16 query rows, which serve as the B operand (contraction over
-// queries) of dV^T += dO^T P, dO^T from transposing reads of the dO tile
-// (stored with the forward's V swizzle). In tile e the products S of tile
-// e+1 run beside the exponentials of tile e, then dV^T += dO^T P of tile e;
-// Q of e+2, dO of e+1 and the lse of e+1 arrive during tile e (two-slot
-// rings). Pad query rows of a tile get S = -inf one tile ahead, hence P = 0.
+// dK and dV in one pass: one workgroup of eight waves per key block over the
+// query blocks that keep it. Waves 0-3 form the dV group, waves 4-7 the dK
+// group; in each group wave (wk, wq) takes key half wk and query half wq of
+// every tile, lane li holding key li of its half. Both groups read the same
+// Q and dO tiles, so a kept tile crosses the memory system once for both
+// gradients: the dV group copies Q, the dK
+// group dO. Per tile the dV group forms S and P and adds dV^T += dO^T P; the
+// dK group forms S, dP = dO V^T and dS = P (dP - D) and adds dK^T += Q^T dS.
+// A SIMD holds one wave of each group. Q, dO, lse and D of tile e+1 arrive
+// during tile e (two-slot rings; a third slot, with copies two tiles ahead,
+// was slower).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dv(AttnArgs a, const uint16_t* __restrict__ dop,
-                                                      const float* __restrict__ lse2,
-                                                      const int32_t* __restrict__ q_count,
-                                                      const int32_t* __restrict__ q_index,
-                                                      uint16_t* __restrict__ dvp, int64_t n_items) {
+__global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uint16_t* __restrict__ dop,
+                                                           const float* __restrict__ delta,
+                                                           const float* __restrict__ lse2,
+                                                           const int32_t* __restrict__ q_count,
+                                                           const int32_t* __restrict__ q_index,
+                                                           uint16_t* __restrict__ dkp,
+                                                           uint16_t* __restrict__ dvp, int64_t n_items) {
   using S = Stage<D>;
   constexpr int kKS = D / 16;
   constexpr int kDT = D / 32;
   __shared__ u32x4 q_slot0[S::kTile], q_slot1[S::kTile];
   __shared__ u32x4 d_slot0[S::kTile], d_slot1[S::kTile];
-  __shared__ f32x4 lse_slot[2][kBlock / 4];   // lse2 of the tile's 64 query rows
-  __shared__ int start_shared;
+  __shared__ f32x4 vec_slot[2][2][kBlock / 4];   // [slot][lse2, D][4 rows]
+  __shared__ int start_sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wk = wave & 1, wq = wave >> 1;
+  const int grp = wave >> 2;                                // 0: dV group, 1: dK group
+  const int w = wave & 3;                                   // wave within the group
+  const int wk = w & 1, wq = w >> 1;
   const int li = lane & 31, h = lane >> 5;
   const int64_t item = xcd_order(blockIdx.x, n_items);     // bh * nb + key block j
   const int64_t bh = item / a.nb;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp) + bh * a.N * D;
   const uint16_t* __restrict__ dO = dop + bh * a.N * D;
   const float* __restrict__ lse_h = lse2 + bh * a.N;
+  const float* __restrict__ dl_h = delta + bh * a.N;
   const int64_t krow = item * kBlock + wk * 32 + li;        // global key row of this lane
   const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(a.kp);
+  const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(a.vp);
   bf16x8 kf[kKS];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks)
@@ -394,252 +403,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dv(AttnArgs a, const uint16_t
   const int cnt = min(max(q_count[item], 0), a.nb);
   const int32_t* __restrict__ list = q_index + item * a.nb;
   const int row0 = 32 * wq;                                 // first query row of this wave's half
-  if (wave == 0) {
-    const int st = clock_phased_start(q_count + bh * a.nb, list, a.nb, cnt, a.sweep_ticks, lane);
-    if (lane == 0) start_shared = st;
-  }
-  __syncthreads();
-  const int start = __builtin_amdgcn_readfirstlane(start_shared);
-  // list entries, packed with their extents, 64 at a time a batch ahead (as
-  // in the forward); entry t of the pass is list entry start + t (wrapped),
-  // t clamped to the last one
-  auto load_batch = [&](int b) {
-    int pos = min(b * 64 + lane, cnt - 1) + start;
-    pos -= pos >= cnt ? cnt : 0;
-    return pack_block_entry(a, list[pos]);
-  };
-  uint32_t batch_cur = 0, batch_nxt = 0;
-  auto entry = [&](int t) {
-    const int p = t < cnt ? t : cnt - 1;
-    return static_cast<uint32_t>(__builtin_amdgcn_readlane(batch_cur, p & 63));
-  };
-  // first row of query block `p` in the head (block 0 for an invalid entry,
-  // which is masked)
-  auto first_row = [&](uint32_t p) {
-    return static_cast<int64_t>(p != 0u ? packed_block(p) : 0) * kBlock;
-  };
-  // S of this wave's 32 queries x 32 keys from the Q tile in `qt`
-  auto scores = [&](const u32x4* qt) {
-    f32x16 r;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const u32x4 u = qt[k_chunk_slot<D>(row0 + li, 2 * ks + h)];
-      r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), kf[ks], r, 0, 0, 0);
-    }
-    return r;
-  };
-  // pad query rows (and every row of an invalid entry) -> S = -inf
-  auto mask = [&](f32x16& sv, uint32_t p) {
-    const BlockExtent ext = packed_extent(p);
-    if (!ext.full()) {
-      const uint32_t bits = real_accumulator_bits(ext, wq, h);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = ((bits >> r) & 1u) ? sv[r] : -INFINITY;
-    }
-  };
-  // dO^T fragment addressing as the forward's V^T: the lane reads rows
-  // drow + 16 st (+ 8), columns 32 dt + dcol; one element offset per dt
-  const int vgrp = lane >> 4, vsl = lane & 15;
-  const int dcol = 16 * (vgrp & 1) + 4 * (vsl & 3);
-  const int drow = row0 + 4 * (vgrp >> 1) + (vsl >> 2);
-  int daddr[kDT];
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) {
-    const int cc = 32 * dt + dcol;
-    daddr[dt] = v_chunk_slot<D>(drow, cc >> 3) * 8 + (cc & 7);
-  }
-  float lse_raw = 0.0f;     // the next tile's lse2, one row per thread of wave 0
-
-  if (cnt > 0) {
-    const uint32_t qoff = tile_load_offset<D, false>(wave, lane);
-    const uint32_t doff = tile_load_offset<D, true>(wave, lane);
-    batch_cur = load_batch(0);
-    batch_nxt = load_batch(1);
-    const uint32_t p0 = entry(0);
-    uint32_t p_next = entry(1);
-    if (wave == 0) lse_raw = lse_h[first_row(p0) + lane];
-    // rows and patch columns that can hold real queries
-    auto rows = [&](uint32_t p) { return 8 * packed_extent(p).vy; };
-    auto cols = [&](uint32_t p) { return packed_extent(p).vx; };
-    issue_tile_load<D>(Q + first_row(p0) * D, q_slot0, qoff, wave, rows(p0), cols(p0));
-    issue_tile_load<D>(dO + first_row(p0) * D, d_slot0, doff, wave, rows(p0), cols(p0));
-    issue_tile_load<D>(Q + first_row(p_next) * D, q_slot1, qoff, wave, rows(p_next), cols(p_next));
-    if (wave == 0) reinterpret_cast<float*>(lse_slot[0])[lane] = lse_raw;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x16 s_cur = scores(q_slot0);
-    mask(s_cur, p0);
-    __syncthreads();            // tile 0's Q slot is refilled next
-
-    // tile e: Q of e+1 in q_slot[(e+1)%2], dO of e in d_slot[e%2]; Q of e+2
-    // streams into q_slot[e%2], dO of e+1 into d_slot[(e+1)%2]
-    auto body = [&](int e, auto parity) {
-      constexpr int kOdd = decltype(parity)::value;
-      u32x4* const q_fill = kOdd ? q_slot1 : q_slot0;
-      u32x4* const q_next = kOdd ? q_slot0 : q_slot1;
-      u32x4* const d_here = kOdd ? d_slot1 : d_slot0;
-      u32x4* const d_fill = kOdd ? d_slot0 : d_slot1;
-      if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
-        batch_cur = batch_nxt;
-        batch_nxt = load_batch(((e + 2) >> 6) + 1);
-      }
-      const uint32_t p2 = entry(e + 2);
-      if (wave == 0) lse_raw = lse_h[first_row(p_next) + lane];
-      issue_tile_load<D>(dO + first_row(p_next) * D, d_fill, doff, wave, rows(p_next),
-                         cols(p_next));
-      issue_tile_load<D>(Q + first_row(p2) * D, q_fill, qoff, wave, rows(p2), cols(p2));
-      __builtin_amdgcn_sched_barrier(0);
-
-      f32x16 s_nxt = scores(q_next);
-      const uint16_t* sd = reinterpret_cast<const uint16_t*>(d_here);
-      bf16x8 vf[kDT][2];
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const uint16_t* pd = sd + daddr[dt] + 16 * st * D;
-          const s16x4 both[2] = {read_v_transposed(pd), read_v_transposed(pd + 8 * D)};
-          __builtin_memcpy(&vf[dt][st], both, sizeof(bf16x8));
-        }
-      bf16x8 pb[2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lv = lse_slot[kOdd][(row0 >> 2) + 2 * g + h];   // rows row0 + 8 g + 4 h ..
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = 4 * g + x;
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -lv[x]));
-          pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][st], pb[st], acc[dt], 0, 0, 0);
-      // the S products interleaved with the LDS reads and the exponentials,
-      // then the dV products with the conversions (masks: 0x100 LDS read,
-      // 0x8 matrix, 0x402 vector incl. transcendental)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < kKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 32 / kKS, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * kDT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 8 / (2 * kDT), 0);
-      }
-      mask(s_nxt, p_next);
-      s_cur = s_nxt;
-      p_next = p2;
-      // every copy of the tile has landed; the lse of e+1 goes to its slot
-      // (last read in tile e-1) before the barrier
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0);
-      if (wave == 0) reinterpret_cast<float*>(lse_slot[kOdd ^ 1])[lane] = lse_raw;
-      __syncthreads();
-    };
-    for (int e = 0;;) {
-      body(e, std::integral_constant<int, 0>{});
-      if (++e >= cnt) break;
-      body(e, std::integral_constant<int, 1>{});
-      if (++e >= cnt) break;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);    // the last tile copies land before the slots are reused
-  __syncthreads();
-
-  // ---- add the two query halves, store (pad keys: 0) -----------------------
-  float* const part = reinterpret_cast<float*>(wk ? q_slot1 : q_slot0);
-  static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
-  if (wq == 1) {
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * 64 + lane] = acc[dt][r];
-  }
-  __syncthreads();
-  if (wq == 1) return;
-  const BlockExtent kext = block_extent(static_cast<int>(item % a.nb), a);
-  const float sc = kext.real(wk * 32 + li) ? 1.0f : 0.0f;
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = 32 * dt + 8 * g + 4 * h;
-      float x[4];
-#pragma unroll
-      for (int xx = 0; xx < 4; ++xx) {
-        const int r = 4 * g + xx;
-        x[xx] = (acc[dt][r] + part[(dt * 16 + r) * 64 + lane]) * sc;
-      }
-      uint2 w;
-      w.x = static_cast<uint32_t>(f32_to_bf16_rne(x[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[1])) << 16);
-      w.y = static_cast<uint32_t>(f32_to_bf16_rne(x[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16);
-      *reinterpret_cast<uint2*>(dvp + krow * D + d) = w;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dK: one workgroup per key block. Wave (wk, wq): key half wk, query half wq
-// of every tile; lane holds key li of its half. S = Q K^T and dP = dO V^T
-// give each lane one key column and 16 query rows, which serve as the B
-// operand (contraction over queries) of dK^T += Q^T dS.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t* __restrict__ dop,
-                                                      const float* __restrict__ delta,
-                                                      const float* __restrict__ lse2,
-                                                      const int32_t* __restrict__ q_count,
-                                                      const int32_t* __restrict__ q_index,
-                                                      uint16_t* __restrict__ grad, int64_t n_items) {
-  using S = Stage<D>;
-  constexpr int kKS = D / 16;
-  constexpr int kDT = D / 32;
-  __shared__ u32x4 q_slot0[S::kTile], q_slot1[S::kTile];
-  __shared__ u32x4 d_slot0[S::kTile], d_slot1[S::kTile];
-  __shared__ f32x4 vec_slot[2][2][kBlock / 4];   // [slot][lse2, D][4 rows]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wk = wave & 1, wq = wave >> 1;
-  const int li = lane & 31, h = lane >> 5;
-  const int64_t item = xcd_order(blockIdx.x, n_items);     // bh * nb + key block j
-  const int64_t bh = item / a.nb;
-  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp) + bh * a.N * D;
-  const uint16_t* __restrict__ dO = dop + bh * a.N * D;
-  const float* __restrict__ lse_h = lse2 + bh * a.N;
-  const float* __restrict__ dl_h = delta + bh * a.N;
-  const int64_t krow = item * kBlock + wk * 32 + li;        // global key row of this lane
-  const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(a.kp);
-  const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(a.vp);
-  bf16x8 kf[kKS], vf[kKS];
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks)
-    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + krow * D + 16 * ks + 8 * h));
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks)
-    vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
-  const float c = a.scale_log2;
-  f32x16 acc[kDT];
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
-
-  const int cnt = min(max(q_count[item], 0), a.nb);
-  const int32_t* __restrict__ list = q_index + item * a.nb;
-  const int row0 = 32 * wq;                                 // first query row of this wave's half
   int toff[kDT][2];
   transposed_offsets<D>(toff, row0, lane);
   // first list entry of the pass (0, or clock-phased: see clock_phased_start)
-  __shared__ int start_sh;
   if (wave == 0) {
     const int st = clock_phased_start(q_count + bh * a.nb, list, a.nb, cnt, a.sweep_ticks, lane);
     if (lane == 0) start_sh = st;
@@ -674,16 +440,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
     }
     return r;
   };
-  // dS of the tile's query block `pe` in bf16, from S and dP; pad query rows
-  // (partial patches only: a uniform branch) get S = -inf, hence P = dS = 0
-  auto weights = [&](uint32_t pe, f32x16 s, const f32x16& dp, const f32x4 (&vec)[2][kBlock / 4],
-                     bf16x8 (&wb)[2]) {
+  // pad query rows (partial patches only: a uniform branch) get S = -inf,
+  // hence P = dS = 0
+  auto mask = [&](uint32_t pe, f32x16& s) {
     const BlockExtent ext = packed_extent(pe);
     if (!ext.full()) {
       const uint32_t bits = real_accumulator_bits(ext, wq, h);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
     }
+  };
+  // P of the tile in bf16 (dV group)
+  auto probs = [&](uint32_t pe, f32x16 s, const f32x4 (&vec)[2][kBlock / 4], bf16x8 (&wb)[2]) {
+    mask(pe, s);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 lv = vec[0][(row0 >> 2) + 2 * g + h];     // rows row0 + 8 g + 4 h .. + 3
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * g + x;
+        wb[r >> 3][r & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x])));
+      }
+    }
+  };
+  // dS of the tile in bf16, from S and dP (dK group)
+  auto weights = [&](uint32_t pe, f32x16 s, const f32x16& dp, const f32x4 (&vec)[2][kBlock / 4],
+                     bf16x8 (&wb)[2]) {
+    mask(pe, s);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int m4 = (row0 >> 2) + 2 * g + h;              // rows row0 + 8 g + 4 h .. + 3
@@ -692,12 +475,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * g + x;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x]));
-        wb[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - dv4[x]));
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x]));
+        wb[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dv4[x]));
       }
     }
   };
-  // dK^T += Q^T dS (xs: the Q tile)
+  // acc^T += X^T W with X^T from transposing reads of the tile `xs` (dO for
+  // the dV group, Q for the dK group)
   auto accumulate = [&](const u32x4* xs, const bf16x8 (&wb)[2]) {
     const uint16_t* xt = reinterpret_cast<const uint16_t*>(xs);
 #pragma unroll
@@ -707,43 +491,48 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             transposed_fragment(xt + 16 * st * D, toff[dt][0], toff[dt][1]), wb[st], acc[dt], 0, 0, 0);
   };
-  // lse2 and D of a query block -> vec
-  // slot, in two steps: the loads are issued before the tile copies (waiting
-  // for them later does not wait for the copies) and stored at the end of
-  // the tile
-  float l_raw = 0.0f, d_raw = 0.0f;
-  auto fetch_vecs = [&](uint32_t pe) {
-    const int ib = packed_block(pe);
-    if (tid < kBlock) {
-      l_raw = lse_h[static_cast<int64_t>(ib) * kBlock + tid];
-      d_raw = dl_h[static_cast<int64_t>(ib) * kBlock + tid];
+  // lse2 and D of query block pe -> vec slot, copied straight into LDS by
+  // wave 0 (one dword per lane) ahead of its Q copy, so the tile's wait
+  // covers them and no register waits on them. The LDS operand goes in as
+  // float*: passed as a vector pointer, the compiler turned it into the null
+  // LDS address.
+  auto copy_vecs = [&](uint32_t pe, f32x4 (&vec)[2][kBlock / 4]) {
+    if (wave == 0) {
+      const int64_t r0 = static_cast<int64_t>(packed_block(pe)) * kBlock;
+      __builtin_amdgcn_global_load_lds(lse_h + r0 + lane, reinterpret_cast<float*>(vec[0]), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(dl_h + r0 + lane, reinterpret_cast<float*>(vec[1]), 4, 0, 0);
     }
   };
-  auto store_vecs = [&](f32x4 (&vec)[2][kBlock / 4]) {
-    if (tid < kBlock) {
-      reinterpret_cast<float*>(vec[0])[tid] = l_raw;
-      reinterpret_cast<float*>(vec[1])[tid] = d_raw;
+  const uint32_t off = tile_load_offset<D, false>(w, lane);
+  // The two groups run the same tile loop, instantiated once per group so
+  // that the dV group holds no V fragments; both pass the same barriers.
+  auto run = [&](auto group) {
+    constexpr int kDk = decltype(group)::value;
+    // this group's share of the copies of query block pe: Q (dV group) or
+    // dO (dK group)
+    auto copy_tile = [&](uint32_t pe, u32x4* qs, u32x4* ds) {
+      const int64_t r0 = static_cast<int64_t>(packed_block(pe)) * kBlock * D;
+      if constexpr (kDk)
+        issue_tile_load<D>(dO + r0, ds, off, w, rows(pe), cols(pe));
+      else
+        issue_tile_load<D>(Q + r0, qs, off, w, rows(pe), cols(pe));
+    };
+    bf16x8 vf[kKS];
+    if constexpr (kDk) {
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+        vf[ks] = __builtin_bit_cast(bf16x8,
+                                    *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
     }
-  };
-
-  const uint32_t off = tile_load_offset<D, false>(wave, lane);
-  auto q_tile = [&](uint32_t pe) {
-    return Q + static_cast<int64_t>(packed_block(pe)) * kBlock * D;
-  };
-  auto d_tile = [&](uint32_t pe) {
-    return dO + static_cast<int64_t>(packed_block(pe)) * kBlock * D;
-  };
-  if (cnt > 0) {
-    // dK pass: Q and dO of tile e+1 stream in while tile e is computed
+    if (cnt == 0) return;
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
     uint32_t ib_cur = entry(0);
-    fetch_vecs(ib_cur);
-    load_pair<D>(q_tile(ib_cur), d_tile(ib_cur), q_slot0, d_slot0, off, wave, rows(ib_cur),
-                 cols(ib_cur));
-    store_vecs(vec_slot[0]);
+    copy_vecs(ib_cur, vec_slot[0]);
+    copy_tile(ib_cur, q_slot0, d_slot0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // tile e in slot e % 2; the copies of e+1 go to the other slot
     auto body = [&](int e, auto parity) {
       constexpr int kOdd = decltype(parity)::value;
       u32x4* const qc = kOdd ? q_slot1 : q_slot0;
@@ -756,29 +545,43 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
       }
       const uint32_t ib_next = entry(e + 1);
       if (e + 1 < cnt) {
-        fetch_vecs(ib_next);
-        __builtin_amdgcn_sched_barrier(0);      // the vector loads stay ahead of the copies
-        load_pair<D>(q_tile(ib_next), d_tile(ib_next), qn, dn, off, wave, rows(ib_next),
-                     cols(ib_next));
+        copy_vecs(ib_next, vec_slot[kOdd ^ 1]);
+        copy_tile(ib_next, qn, dn);
       }
       const f32x16 sv = rows_times(qc, kf);
-      const f32x16 dp = rows_times(dc, vf);
       bf16x8 wb[2];
-      weights(ib_cur, sv, dp, vec_slot[kOdd], wb);
-      accumulate(qc, wb);
-      if (e + 1 < cnt) store_vecs(vec_slot[kOdd ^ 1]);
+      if constexpr (kDk) {
+        const f32x16 dp = rows_times(dc, vf);
+        weights(ib_cur, sv, dp, vec_slot[kOdd], wb);
+        accumulate(qc, wb);
+      } else {
+        probs(ib_cur, sv, vec_slot[kOdd], wb);
+        accumulate(dc, wb);
+      }
       ib_cur = ib_next;
+      // Every copy has landed, so Q, dO, lse and D of e+1 are in LDS for
+      // every wave after the barrier. The scheduling barrier keeps the wait
+      // after this tile's work; the empty asm statements keep the compiler
+      // from moving LDS accesses across the barrier.
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     };
     for (int e = 0; e < cnt; e += 2) {
       body(e, std::integral_constant<int, 0>{});
       if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
     }
-  }
+  };
+  if (grp == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
 
-  // ---- add the two query halves, scale dK, store (pad keys: 0) -------------
-  float* const part = reinterpret_cast<float*>(wk ? q_slot1 : q_slot0);
+  // ---- add the two query halves of each group, store (pad keys: 0) --------
+  float* const part = reinterpret_cast<float*>(grp == 0 ? (wk ? q_slot1 : q_slot0)
+                                                        : (wk ? d_slot1 : d_slot0));
   static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
   if (wq == 1) {
 #pragma unroll
@@ -791,7 +594,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
   const BlockExtent kext = block_extent(static_cast<int>(item % a.nb), a);
   const bool real_key = kext.real(wk * 32 + li);
   // dK carries the softmax scale s; pad keys get 0
-  const float sc = real_key ? a.scale_log2 * kLn2 : 0.0f;
+  const float sc = real_key ? (grp == 0 ? 1.0f : a.scale_log2 * kLn2) : 0.0f;
+  uint16_t* const out = grp == 0 ? dvp : dkp;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -803,10 +607,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk(AttnArgs a, const uint16_t
         const int r = 4 * g + xx;
         x[xx] = (acc[dt][r] + part[(dt * 16 + r) * 64 + lane]) * sc;
       }
-      uint2 w;
-      w.x = static_cast<uint32_t>(f32_to_bf16_rne(x[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[1])) << 16);
-      w.y = static_cast<uint32_t>(f32_to_bf16_rne(x[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16);
-      *reinterpret_cast<uint2*>(grad + krow * D + d) = w;
+      uint2 o2;
+      o2.x = static_cast<uint32_t>(f32_to_bf16_rne(x[0])) |
+             (static_cast<uint32_t>(f32_to_bf16_rne(x[1])) << 16);
+      o2.y = static_cast<uint32_t>(f32_to_bf16_rne(x[2])) |
+             (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16);
+      *reinterpret_cast<uint2*>(out + krow * D + d) = o2;
     }
 }
 
@@ -880,26 +686,20 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   // clock-phased periods: ticks of the 100 MHz clock per tile of each pass
   // (d = 128 at 720p; d = 64 tiles take about half as long)
   const uint32_t t_dq = phased ? (g.D == 64 ? 95u : 185u) : 0u;
-  const uint32_t t_dv = phased ? (g.D == 64 ? 95u : 185u) : 0u;
-  const uint32_t t_dk = phased ? (g.D == 64 ? 110u : 220u) : 0u;
-  AttnArgs a_dq = a, a_dv = a, a_dk = a;
+  const uint32_t t_dkv = phased ? (g.D == 64 ? 110u : 220u) : 0u;
+  AttnArgs a_dq = a, a_dkv = a;
   a_dq.sweep_ticks = t_dq;
-  a_dv.sweep_ticks = t_dv;
-  a_dk.sweep_ticks = t_dk;
+  a_dkv.sweep_ticks = t_dkv;
   if (g.D == 64) {
     hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta,
                        lse2, dq16, items);
-    hipLaunchKernelGGL((bwd_dv<64>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16, lse2,
-                       q_count, q_index, dv16, items);
-    hipLaunchKernelGGL((bwd_dk<64>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
-                       delta, lse2, q_count, q_index, dk16, items);
+    hipLaunchKernelGGL((bwd_dkv<64>), dim3(grid), dim3(2 * kThreads), 0, stream, a_dkv, do16,
+                       delta, lse2, q_count, q_index, dk16, dv16, items);
   } else {
     hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta,
                        lse2, dq16, items);
-    hipLaunchKernelGGL((bwd_dv<128>), dim3(grid), dim3(kThreads), 0, stream, a_dv, do16, lse2,
-                       q_count, q_index, dv16, items);
-    hipLaunchKernelGGL((bwd_dk<128>), dim3(grid), dim3(kThreads), 0, stream, a_dk, do16,
-                       delta, lse2, q_count, q_index, dk16, items);
+    hipLaunchKernelGGL((bwd_dkv<128>), dim3(grid), dim3(2 * kThreads), 0, stream, a_dkv, do16,
+                       delta, lse2, q_count, q_index, dk16, dv16, items);
   }
 }
 
