@@ -249,7 +249,7 @@ def measure_backward(cabf, geom, bufs, thr, sta, steps: int):
     keeps lse), timed with HIP events, in the default clock-phased order and
     in deterministic order. Effective TFLOP/s counts 2.5x the forward's flops
     (five 64x64xd products per kept tile); the kernels actually run eight
-    (S in all three passes, dP in two)."""
+    (S in the dQ pass and in both wave groups of the dK/dV pass, dP in two)."""
     import torch
     q, k, v, qp, kp, vp, op, o, cnt, idx, ws = bufs
     scale = cabf.default_scale(geom)
