@@ -63,7 +63,7 @@ enum {
 /* Layer geometry. The padded grid and block count are derived:
  *   Ty = ceil(H/P), Tx = ceil(W/P), Hp = Ty*P, Wp = Tx*P,
  *   nb = T*Ty*Tx blocks of P*P tokens, N = nb*P*P.
- * This build supports P = 8 (64-token blocks) and head_dim 64 or 128.
+ * The library supports P = 8 (64-token blocks) and head_dim 64 or 128.
  * Block b = (t*Ty + ty)*Tx + tx is patch (ty, tx) of frame t. */
 typedef struct {
   int32_t batch;
