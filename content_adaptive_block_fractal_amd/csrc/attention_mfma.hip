@@ -57,6 +57,7 @@ namespace {
 
 using namespace tiles;
 constexpr float kRescaleSlack = 8.0f;   // base-2 headroom before the running max is raised
+constexpr uint32_t kPaceMinEntries = 512;   // mean list length from which a pass is paced
 
 // A list entry decoded: element offset of its 64 K/V rows in the head, and
 // what the layout needs to mask it (block index, or number of valid keys).
@@ -243,6 +244,19 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   }
   __syncthreads();
   const int start = __builtin_amdgcn_readfirstlane(*start_shared);
+  // Sweep period for the pacing of a clock-phased pass over long lists (0:
+  // no pacing). A workgroup's position drifts from the sweep like a random
+  // walk, about 4.5 sqrt(n) blocks after n tiles of a 20% list; from about
+  // 512 entries the workgroups of an XCD spread over more K/V tiles than its
+  // L2 holds, and holding the ones ahead back restores part of the reuse
+  // (241 frames at 768p: 1-2% to 23% faster, depending on how far the box's
+  // own tile rate runs ahead of the sweep's). Shorter lists stay within L2 and
+  // gain nothing from it.
+  uint32_t pace_period = 0;
+  if (L::kPhased && a.sweep_ticks != 0 && wave == 0) {
+    const uint32_t period = sweep_period(a.kv_count + bh * a.nb, a.nb, a.sweep_ticks, lane);
+    if (period >= kPaceMinEntries * a.sweep_ticks) pace_period = __builtin_amdgcn_readfirstlane(period);
+  }
   // Entries of the pass are fetched 64 at a time, one per lane, a batch ahead
   // of use, and read out with readlane: no list load is waited on per tile.
   // Entry t of the pass is list entry start + t (wrapped); t is clamped to the
@@ -442,6 +456,9 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     // from the one before it, so the compiler's wait bookkeeping follows the
     // ring exactly.
     for (int e = 0;;) {
+      // every 24 tiles, wave 0 holds the workgroup back if it runs ahead of
+      // the sweep by more than 48 key blocks (long lists only)
+      if (pace_period != 0 && e % 24 == 12) hold_back_to_sweep(t_next.jb, a.nb, pace_period, 48);
       body(e, I0{}, I0{});
       if (++e >= cnt) break;
       body(e, I1{}, I1{});

@@ -79,21 +79,46 @@ __device__ inline s16x4 read_v_transposed(const uint16_t* sv_row_chunk) {
 // 64 lists spread evenly over the head (head_counts[0 .. nb)), which all of
 // them sample alike; ticks approximates the time of one tile. Called by one
 // whole wave; every lane returns the same value.
-__device__ inline int clock_phased_start(const int32_t* head_counts, const int32_t* list, int nb,
-                                         int cnt, uint32_t ticks, int lane) {
-  if (ticks == 0 || cnt <= 1) return 0;
+// The sweep period P in clock ticks (see clock_phased_start). Called by one
+// whole wave; every lane returns the same value.
+__device__ inline uint32_t sweep_period(const int32_t* head_counts, int nb, uint32_t ticks, int lane) {
   int total = min(max(head_counts[(lane * nb) >> 6], 1), nb);
 #pragma unroll
   for (int sh = 1; sh < 64; sh <<= 1) total += __shfl_xor(total, sh);
-  // 32 clock bits wrap every 43 s: one incoherent moment, harmless
-  const uint32_t period = static_cast<uint32_t>(max(total >> 6, 1)) * ticks;
+  return static_cast<uint32_t>(max(total >> 6, 1)) * ticks;
+}
+
+// The block the sweep has reached now. 32 clock bits wrap every 43 s: one
+// incoherent moment, harmless.
+__device__ inline int swept_block(uint32_t period, int nb) {
   const uint32_t now = static_cast<uint32_t>(__builtin_amdgcn_s_memrealtime());
-  const int swept = static_cast<int>(static_cast<uint64_t>(now % period) * nb / period);
+  return static_cast<int>(static_cast<uint64_t>(now % period) * nb / period);
+}
+
+__device__ inline int clock_phased_start(const int32_t* head_counts, const int32_t* list, int nb,
+                                         int cnt, uint32_t ticks, int lane) {
+  if (ticks == 0 || cnt <= 1) return 0;
+  const int swept = swept_block(sweep_period(head_counts, nb, ticks, lane), nb);
   int before = 0;   // entries below the swept block
   for (int i = lane; i < cnt; i += 64) before += list[i] < swept ? 1 : 0;
 #pragma unroll
   for (int sh = 1; sh < 64; sh <<= 1) before += __shfl_xor(before, sh);
   return before >= cnt ? 0 : before;
+}
+
+// Pacing of a clock-phased pass: while key block jb (the next one the pass
+// reads) lies more than `lead` blocks ahead of the sweep (and less than half
+// the range, which would mean behind it), the calling wave sleeps about 1000
+// cycles at a time, at most 32 times; its workgroup then waits for it at the
+// next barrier. A workgroup that has run ahead of the others of its head
+// would fetch tiles that no other one needs yet.
+__device__ inline void hold_back_to_sweep(int jb, int nb, uint32_t period, int lead) {
+  for (int i = 0; i < 32; ++i) {
+    int ahead = jb - swept_block(period, nb);
+    ahead += ahead < 0 ? nb : 0;
+    if (ahead <= lead || 2 * ahead >= nb) break;
+    __builtin_amdgcn_s_sleep(16);
+  }
 }
 
 template <int D>
