@@ -192,7 +192,10 @@ int cabf_build_sta_mask(const cabf_geom* g, const cabf_sta* sta,
  * computed with an fp32 online softmax. bf16: Q K^T and P V on bf16 matrix
  * cores with fp32 accumulation, P rounded to bf16, o rounded to bf16.
  * A row with kv_count = 0 gets o = 0, lse = -inf.
- * qp, kp, vp: reordered [B, heads, N, head_dim] (input).
+ * qp, kp, vp: reordered [B, heads, N, head_dim] (input). Pad slots never
+ *   change a real row's result, but must hold finite values (cabf_permute
+ *   writes zeros there): a pad key's weight is exactly 0, and 0 times an
+ *   infinite or NaN V value is NaN.
  * kv_count [B, heads, nb], kv_index [B, heads, nb, nb] (input; entries must be
  *   valid block indices; duplicates would be attended twice).
  * op: reordered [B, heads, N, head_dim] (output, pad rows included).
@@ -245,7 +248,9 @@ size_t cabf_bsa_backward_workspace_bytes(const cabf_geom* g);
  * dtype: CABF_BF16 only (else CABF_EUNSUPPORTED). qp, kp, vp, op (the
  * forward's output) and dop: [B, heads, N, head_dim] bf16; lse: the
  * forward's [B, heads, N] fp32; kv_count / kv_index: the forward's lists
- * (inputs). dqp, dkp, dvp: [B, heads, N, head_dim] bf16 (outputs).
+ * (inputs). Pad slots of the inputs must hold finite values, as for
+ * cabf_bsa_forward (their weights are exactly 0). dqp, dkp, dvp:
+ * [B, heads, N, head_dim] bf16 (outputs).
  * bf16 matrix products with fp32 accumulation.
  * flags: 0 or CABF_BSA_DETERMINISTIC (other bits give CABF_EINVAL), as for
  *   cabf_bsa_forward: with 0 each pass over a list starts at a clock-derived

@@ -278,6 +278,7 @@ def build_block_mask(qp, kp, g: Grid, scale: float, thr: float, sta=None, precis
     Returns a dict with
       mask       bool [..., nb, nb]  final kept blocks (M = M_nabla OR M_STA)
       adaptive   bool [..., nb, nb]  the CDF (or top-k) part alone
+      window     bool [nb, nb]       the sliding-tile window (all False without one)
       p          [..., nb, nb]       block probabilities
       k, s_prev, s_k, p_k, p_next    per-row cut quantities (see cdf_cut_details;
                                      s_prev and s_k are NaN for top-k)
@@ -304,11 +305,10 @@ def build_block_mask(qp, kp, g: Grid, scale: float, thr: float, sta=None, precis
                 a = b = math.nan
             adaptive[pos][i][kept] = True
             k[pos][i], s_prev[pos][i], s_k[pos][i], p_k[pos][i], p_next[pos][i] = kk, a, b, c, d
-    mask = adaptive.copy()
-    if sta is not None:
-        mask |= sta_mask(g, *sta)
+    window = sta_mask(g, *sta) if sta is not None else np.zeros((g.nb, g.nb), dtype=bool)
+    mask = adaptive | window
     kv_count, kv_index = mask_to_lists(mask)
-    return dict(mask=mask, adaptive=adaptive, p=p, k=k, s_prev=s_prev, s_k=s_k,
+    return dict(mask=mask, adaptive=adaptive, window=window, p=p, k=k, s_prev=s_prev, s_k=s_k,
                 p_k=p_k, p_next=p_next, kv_count=kv_count, kv_index=kv_index,
                 mode="cdf" if topk is None else "topk")
 

@@ -201,7 +201,10 @@ def svg_layer(q, k, v, init_q, init_k, iters: int, scale: float, top_p: float):
 
 
 def kept_density(info) -> float:
-    """Fraction of (query, key) token pairs the selection keeps."""
+    """Fraction of (query, key) token pairs the selection keeps: the sum over
+    query clusters of |cluster| times the tokens of its kept key clusters,
+    over all query tokens times all key tokens.
+    Pinned by: keep-all = 1, a hand-counted selection (tests/test_oracle_svg2.py)."""
     q_sizes = np.diff(info["q_off"])
     k_sizes = np.diff(info["k_off"])
     sel = info["sel"]
@@ -210,11 +213,5 @@ def kept_density(info) -> float:
     return kept / float(n * int(k_sizes.sum()))
 
 
-def gap_exempt(gap: np.ndarray, rel: float = 1e-5, scale_ref: float = 1.0) -> np.ndarray:
-    """Rows whose nearest and second-nearest centroids are within rel *
-    scale_ref in squared distance: fp32 and fp64 may pick either."""
-    return np.asarray(gap) <= rel * scale_ref
-
-
 __all__ = ["kmeans_assign", "kmeans_update", "kmeans", "cluster_permutation", "centroid_probs",
-           "top_p_select", "cluster_attention", "svg_layer", "kept_density", "gap_exempt"]
+           "top_p_select", "cluster_attention", "svg_layer", "kept_density"]

@@ -62,6 +62,33 @@ def fourier_video_qkv(T: int, H: int, W: int, heads: int, d: int, amplitude: flo
     return tuple(outs)
 
 
+def gaussian_video_qkv(T: int, H: int, W: int, heads: int, d: int, seed: int = 0,
+                       v_std: float = 0.5, dtype: str = "bf16", batch: int = 1,
+                       device: str | torch.device = "cpu"):
+    """Token-independent inputs on a latent video grid: Q and K ~ N(0, 1) and
+    V ~ N(0, v_std^2) per element, raster order [batch, heads, T*H*W, d].
+
+    Unlike ``fourier_video_qkv`` neighbouring tokens share nothing, so with a
+    softmax scale of a few units over sqrt(d) each query's weights concentrate
+    on a handful of keys (logits spread over tens of units in base 2). Draws
+    from one seeded torch generator: per batch and head, Q, K, V in that order.
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    out_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+    n = T * H * W
+    outs = [torch.empty(batch, heads, n, d, dtype=out_dtype, device=dev) for _ in range(3)]
+    for b in range(batch):
+        for h in range(heads):
+            for X, std in enumerate((1.0, 1.0, v_std)):
+                val = torch.randn(n, d, generator=gen, dtype=torch.float32, device=dev) * std
+                outs[X][b, h] = val.to(out_dtype)
+    return tuple(outs)
+
+
 def gaussian_mixture_qk(n: int, heads: int, d: int, components: int = 64, spread: float = 0.15,
                         amplitude: float = 1.0, seed: int = 0, dtype: str = "bf16",
                         device: str | torch.device = "cpu"):

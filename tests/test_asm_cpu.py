@@ -48,25 +48,30 @@ def assembly(tmp_path_factory):
 
 
 def _kernels(text):
-    """(name, body) of every kernel in an assembly file."""
-    parts = re.split(r"^(_Z[^\s:]+):.*$", text, flags=re.M)
-    return [(parts[i], parts[i + 1].split("s_endpgm")[0]) for i in range(1, len(parts) - 1, 2)]
+    """(name, body) of every kernel in an assembly file: from its symbol to its
+    .Lfunc_end label, so every basic block (all exits included) is covered."""
+    pat = re.compile(r"^(_Z[^\s:]+):.*?$(.*?)^\.Lfunc_end\d+:", flags=re.M | re.S)
+    return [(m.group(1), m.group(2)) for m in pat.finditer(text)]
 
 
 @pytest.mark.parametrize("f", FILES)
 def test_lds_copies_get_a_real_base(assembly, f):
     kernels = _kernels(assembly[f])
     assert kernels, f"{f}: no kernels found in the assembly"
+    copies = 0
     for name, body in kernels:
-        lines = body.splitlines()
         m0 = None
-        for ln in lines:
+        for ln in body.splitlines():
             t = ln.strip()
+            if re.match(r"^[.\w]+:", t):
+                m0 = None           # a label starts a basic block: M0 must be set inside it
             if re.match(r"s_\w+\s+m0,", t):
                 m0 = t
             if t.startswith("global_load_lds"):
-                assert m0 is not None, f"{name}: LDS copy without an M0 write"
+                copies += 1
+                assert m0 is not None, f"{name}: LDS copy without an M0 write in its block"
                 assert not re.match(r"s_mov_b32\s+m0,\s*-1\b", m0), f"{name}: null LDS base ({m0})"
+    assert copies > 0, f"{f}: no LDS copies found"
 
 
 @pytest.mark.parametrize("f", FILES)

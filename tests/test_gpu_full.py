@@ -2,12 +2,22 @@
 benchmark uses (the same C-ABI calls on full [1, heads, N, d] tensors).
 
 The oracle cannot redo a whole layer here, so each case samples: the block
-mask of two heads (every row of them) and the attention of query blocks spread
-over those heads, chosen to include padded patches and the first and last
-blocks. Attention rows are compared where the GPU kept the same blocks as the
-oracle (rows of ill-posed cuts are counted by the mask check); a second check
-feeds the oracle's own lists of the sampled heads to cabf_bsa_forward (in
-deterministic list order; the first check uses the default clock-phased order).
+mask of two heads (every row of them, against the oracle's fp64 cut, with
+every differing row checked to be a correct cut) and the attention of query
+blocks spread over those heads, chosen to include padded patches and the
+first and last blocks. The attention reference is the oracle's, recomputed
+over the GPU's own kept lists, so no query block is left out. The timed path
+(cabf_permute_pool -> cabf_build_block_mask_pooled -> cabf_bsa_forward ->
+cabf_unpermute) is checked in both visit orders; the unfused path
+(cabf_permute -> cabf_build_block_mask) at the headline shape.
+
+Block logits of the seeded smooth-field workloads are nearly flat at the
+default scale 1/sqrt(d), so the cases include the unit-scale reading of the
+reduced-attention temperature, and the sharp cases use token-independent
+inputs at scale 3.5/sqrt(d), where a query's weights sit on a few keys: there
+a kernel with uniform weights or a wrong V key order misses by far more than
+the tolerance (checked on the CPU, with the mistakes planted in the oracle's
+inputs), and the lazy rescale of the online softmax fires.
 """
 import math
 
@@ -17,23 +27,24 @@ import torch
 
 import content_adaptive_block_fractal_amd as cabf
 import oracle
-from synth import WORKLOADS, fourier_video_qkv
-from tests.parity import compare_attention, compare_masks, say, to_np
+from synth import WORKLOADS, fourier_video_qkv, gaussian_video_qkv
+from tests.parity import (assert_inputs_discriminate, attention_on_gpu_lists, compare_attention,
+                          compare_masks, rescale_rows, sample_rows, say, to_np)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+SHARP_SCALE = 3.5        # kernel scale of the sharp cases, times 1/sqrt(d)
 
 
-def calibrate(qp, kp, g, target, sta, ws):
+def calibrate(build, g, target):
+    """thr giving the target block sparsity, by bisection on the GPU mask;
+    build(thr) -> kv_count."""
     nb = g.sizes()["n_blocks"]
-    cnt = torch.empty((1, g.heads, nb), dtype=torch.int32, device=DEV)
-    idx = torch.empty((1, g.heads, nb, nb), dtype=torch.int32, device=DEV)
-    total = g.heads * nb * nb
+    total = g.batch * g.heads * nb * nb
     lo, hi = 0.0, 1.0
     for _ in range(24):
         mid = 0.5 * (lo + hi)
-        cabf.cabf_build_block_mask(g, qp, kp, cabf.default_scale(g), mid, sta, cnt, idx, None, ws)
-        sp = 1.0 - cnt.sum(dtype=torch.int64).item() / total
+        sp = 1.0 - build(mid).sum(dtype=torch.int64).item() / total
         if sp < target:
             lo = mid
         else:
@@ -50,70 +61,140 @@ def sample_blocks(og, n):
     return sorted(pick)
 
 
+def geometry(name):
+    w = WORKLOADS[name]
+    return w, cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P), oracle.Grid(w.T, w.H, w.W, w.P)
+
+
+def timed_path(q, k, v, g, target, sta, scale):
+    """The benchmark's path: reorder with pooling, mask from the pooled means
+    (thr calibrated to the target sparsity), attention in the default and the
+    deterministic visit order, restore order."""
+    qp, kp, vp, ws = cabf.permute_pool(q, k, v, g)
+    nb = g.sizes()["n_blocks"]
+    cnt = torch.empty((g.batch, g.heads, nb), dtype=torch.int32, device=DEV)
+    idx = torch.empty((g.batch, g.heads, nb, nb), dtype=torch.int32, device=DEV)
+
+    def build(thr):
+        cabf.cabf_build_block_mask_pooled(g, scale, thr, 0, sta, cnt, idx, None, ws)
+        return cnt
+
+    thr = calibrate(build, g, target)
+    build(thr)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, scale, return_lse=True)
+    op_det, lse_det = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, scale, return_lse=True,
+                                       deterministic=True)
+    o = cabf.unpermute(op, g)
+    torch.cuda.synchronize()
+    return dict(qp=qp, kp=kp, vp=vp, cnt=cnt, idx=idx, thr=thr, op=op, lse=lse, op_det=op_det,
+                lse_det=lse_det, o=o)
+
+
+def check_head(r, g, og, hd, scale, sta, blocks, label):
+    """Mask of head hd against the oracle; attention of `blocks` (both orders)
+    against the oracle over the GPU's lists; raster rows equal reordered rows.
+    Returns (numpy q, k, v of the head, its counts and lists, the reference)."""
+    qh, kh, vh = (to_np(r[t][0, hd]) for t in ("qp", "kp", "vp"))
+    info = oracle.build_block_mask(qh, kh, og, scale, r["thr"], sta)
+    counts = compare_masks(r["cnt"][0, hd], r["idx"][0, hd], info, r["thr"], label=f"{label} head {hd}")
+    cnt_h = r["cnt"][0, hd].cpu().numpy()
+    idx_h = r["idx"][0, hd].cpu().numpy()
+    ref_o, ref_lse = attention_on_gpu_lists(qh, kh, vh, cnt_h, idx_h, og, scale, blocks)
+    rows = sample_rows(blocks)
+    compare_attention(r["op"][0, hd], ref_o, True, r["lse"][0, hd], ref_lse, rows=rows,
+                      label=f"{label} head {hd} clock-phased")
+    compare_attention(r["op_det"][0, hd], ref_o, True, r["lse_det"][0, hd], ref_lse, rows=rows,
+                      label=f"{label} head {hd} deterministic")
+    pos = oracle.fractal_positions(og)
+    inv = np.full(og.N, -1)
+    inv[pos] = np.arange(pos.size)
+    real_rows = rows[inv[rows] >= 0]
+    assert torch.equal(r["o"][0, hd, torch.from_numpy(inv[real_rows]).to(DEV)],
+                       r["op"][0, hd, torch.from_numpy(real_rows).to(DEV)])
+    return qh, kh, vh, cnt_h, idx_h, ref_o, counts
+
+
 CASES = [
-    ("wan1.3b-480p", 0.80, None),
-    ("wan14b-720p", 0.80, None),
-    ("wan14b-720p", 0.90, (1, 1, 1)),
-    ("hunyuan-241f-768p", 0.85, None),
+    # workload, target sparsity, window, scale (None: 1/sqrt(d))
+    ("wan1.3b-480p", 0.80, None, None),
+    ("wan14b-720p", 0.80, None, None),
+    ("wan14b-720p", 0.80, None, 1.0),          # unit-scale reading of the block temperature
+    ("wan14b-720p", 0.90, (1, 1, 1), None),
+    ("hunyuan-241f-768p", 0.85, None, None),
+    ("hunyuan-241f-768p", 0.85, None, 1.0),
 ]
 
 
-@pytest.mark.parametrize("name,target,sta", CASES)
-def test_full_size_layer(name, target, sta):
-    w = WORKLOADS[name]
-    say(f"full-size {name} sparsity {target} sta {sta}")
-    g = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
-    og = oracle.Grid(w.T, w.H, w.W, w.P)
+@pytest.mark.parametrize("name,target,sta,scale", CASES)
+def test_full_size_timed_path(name, target, sta, scale):
+    w, g, og = geometry(name)
+    s = cabf.default_scale(g) if scale is None else scale
+    say(f"full-size timed path {name} sparsity {target} sta {sta} scale {s:.4f}")
     q, k, v = fourier_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, w.amplitude, seed=1,
                                 dtype=w.dtype, device=DEV)
-    scale = cabf.default_scale(g)
-    ws = cabf.mask_workspace(g, DEV)
-    qp, kp, vp = cabf.permute(q, k, v, g)
-    thr = calibrate(qp, kp, g, target, sta, ws)
-    cnt, idx = cabf.build_block_mask(qp, kp, g, thr, sta, scale, workspace=ws)
-    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, scale, return_lse=True)
-    o = cabf.unpermute(op, g)
-    torch.cuda.synchronize()
-    sparsity = 1.0 - cnt.sum(dtype=torch.int64).item() / (w.heads * og.nb ** 2)
-    say(f"thr={thr:.6f} sparsity={sparsity:.4f}")
+    r = timed_path(q, k, v, g, target, sta, s)
+    sparsity = 1.0 - r["cnt"].sum(dtype=torch.int64).item() / (w.heads * og.nb ** 2)
+    say(f"thr={r['thr']:.6f} sparsity={sparsity:.4f}")
     assert abs(sparsity - target) < 0.01
-
-    heads = [0, w.heads - 1]
     blocks = sample_blocks(og, 6)
-    for hd in heads:
-        qh, kh, vh = (to_np(t[0, hd]) for t in (qp, kp, vp))
-        info = oracle.build_block_mask(qh, kh, og, scale, thr, sta)
-        compare_masks(cnt[0, hd], idx[0, hd], info, thr, label=f"{name} head {hd}")
-        gmask = oracle.lists_to_mask(cnt[0, hd].cpu().numpy(), idx[0, hd].cpu().numpy(), og.nb)
-        same = ~(gmask != info["mask"]).any(-1)
-        use = [b for b in blocks if same[b]]
-        assert len(use) >= len(blocks) - 2
-        sub_cnt = np.zeros_like(info["kv_count"])
-        sub_cnt[use] = info["kv_count"][use]
-        ref_o, ref_lse = oracle.bsa_forward(qh, kh, vh, sub_cnt, info["kv_index"], og, scale)
-        rows = np.concatenate([np.arange(b * 64, (b + 1) * 64) for b in use])
-        compare_attention(op[0, hd], ref_o, True, lse[0, hd], ref_lse, rows=rows,
-                          label=f"{name} head {hd} blocks {use}")
-        # raster output of the same rows equals the reordered output
-        pos = oracle.fractal_positions(og)
-        inv = np.full(og.N, -1)
-        inv[pos] = np.arange(pos.size)
-        real_rows = rows[inv[rows] >= 0]
-        assert torch.equal(o[0, hd, torch.from_numpy(inv[real_rows]).to(DEV)],
-                           op[0, hd, torch.from_numpy(real_rows).to(DEV)])
+    for hd in (0, w.heads - 1):
+        check_head(r, g, og, hd, s, sta, blocks, name)
 
-        # attention fed the oracle's lists for this head (the rest keeps the
-        # GPU's), in deterministic list order
-        cnt2, idx2 = cnt.clone(), idx.clone()
-        cnt2[0, hd] = torch.from_numpy(info["kv_count"]).to(DEV)
-        idx2[0, hd] = torch.from_numpy(info["kv_index"]).to(DEV)
-        op2 = cabf.bsa_forward(qp, kp, vp, cnt2, idx2, g, scale, deterministic=True)
-        torch.cuda.synchronize()
-        sub_cnt = np.zeros_like(info["kv_count"])
-        sub_cnt[blocks] = info["kv_count"][blocks]
-        ref_o2, _ = oracle.bsa_forward(qh, kh, vh, sub_cnt, info["kv_index"], og, scale)
-        rows2 = np.concatenate([np.arange(b * 64, (b + 1) * 64) for b in blocks])
-        compare_attention(op2[0, hd], ref_o2, True, rows=rows2, label=f"{name} head {hd} oracle lists")
+
+@pytest.mark.parametrize("name,target", [("wan14b-720p", 0.80), ("hunyuan-241f-768p", 0.85)])
+def test_full_size_sharp_attention(name, target):
+    """Token-independent inputs at scale 3.5/sqrt(d) on the full geometry
+    (partial patches; 252-entry lists at 720p, ~600 at 768p, where the passes
+    are paced): the data can fail a wrong kernel, and the GPU stays within the
+    tolerance of the oracle over its own lists."""
+    w, g, og = geometry(name)
+    s = SHARP_SCALE / math.sqrt(w.head_dim)
+    say(f"full-size sharp attention {name} sparsity {target}")
+    q, k, v = gaussian_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, seed=4, device=DEV)
+    r = timed_path(q, k, v, g, target, None, s)
+    mean_len = r["cnt"].float().mean().item()
+    say(f"thr={r['thr']:.6f} mean list length {mean_len:.1f}")
+    if name.startswith("hunyuan"):
+        assert mean_len >= 512       # the paced long-list passes run
+    blocks = sample_blocks(og, 4)
+    for hd in (0, w.heads - 1):
+        qh, kh, vh, cnt_h, idx_h, ref_o, _ = check_head(r, g, og, hd, s, None, blocks, f"{name} sharp")
+        assert_inputs_discriminate(qh, kh, vh, cnt_h, idx_h, og, s, blocks, ref_o)
+        hit, total = rescale_rows(qh, kh, cnt_h, idx_h, og, s, blocks)
+        say(f"rows whose list-order pass must rescale: {hit} of {total}")
+        assert hit >= total // 10
+
+
+def test_full_size_unfused_path():
+    """cabf_permute -> cabf_build_block_mask (its own pooling pass) at the
+    headline shape: lists against the oracle, attention over them."""
+    w, g, og = geometry("wan14b-720p")
+    s = cabf.default_scale(g)
+    q, k, v = fourier_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, w.amplitude, seed=2,
+                                dtype=w.dtype, device=DEV)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    ws = cabf.mask_workspace(g, DEV)
+    nb = og.nb
+    cnt = torch.empty((1, w.heads, nb), dtype=torch.int32, device=DEV)
+    idx = torch.empty((1, w.heads, nb, nb), dtype=torch.int32, device=DEV)
+
+    def build(thr):
+        cabf.cabf_build_block_mask(g, qp, kp, s, thr, None, cnt, idx, None, ws)
+        return cnt
+
+    thr = calibrate(build, g, 0.80)
+    build(thr)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True)
+    torch.cuda.synchronize()
+    blocks = sample_blocks(og, 4)
+    for hd in (0, w.heads - 1):
+        qh, kh, vh = (to_np(t[0, hd]) for t in (qp, kp, vp))
+        info = oracle.build_block_mask(qh, kh, og, s, thr, None)
+        compare_masks(cnt[0, hd], idx[0, hd], info, thr, label=f"unfused head {hd}")
+        ref_o, ref_lse = attention_on_gpu_lists(qh, kh, vh, cnt[0, hd].cpu().numpy(),
+                                                idx[0, hd].cpu().numpy(), og, s, blocks)
+        compare_attention(op[0, hd], ref_o, True, lse[0, hd], ref_lse, rows=sample_rows(blocks),
+                          label=f"unfused head {hd}")
 
 
 def test_longest_supported_rows():
@@ -134,7 +215,8 @@ def test_longest_supported_rows():
     rows = [0, 1, 777, og.nb // 2, og.nb - 2, og.nb - 1]
     info = dict(mask=np.zeros((len(rows), og.nb), dtype=bool), k=np.zeros(len(rows), dtype=np.int64),
                 s_prev=np.zeros(len(rows)), s_k=np.zeros(len(rows)), p_k=np.zeros(len(rows)),
-                p_next=np.zeros(len(rows)))
+                p_next=np.zeros(len(rows)), p=p[rows],
+                window=np.zeros((og.nb, og.nb), dtype=bool)[rows])
     for n, i in enumerate(rows):
         kept, kk, a, b, c, dd = oracle.cdf_cut_details(p[i], thr)
         info["mask"][n, kept] = True
@@ -148,17 +230,15 @@ def test_longest_supported_rows():
 def test_full_size_topk_static_ratio(ratio, sta):
     """Static-ratio selection at the Wan-14B 720p shape: k = ceil(ratio * nb)
     per row, both edge heads' lists against the oracle, and the attention of
-    sampled query blocks on those lists."""
-    w = WORKLOADS["wan14b-720p"]
-    g = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
-    og = oracle.Grid(w.T, w.H, w.W, w.P)
+    sampled query blocks over the GPU's lists."""
+    w, g, og = geometry("wan14b-720p")
     k = cabf.topk_for_ratio(g, ratio)
     say(f"full-size top-k {w.name} ratio {ratio} k {k} sta {sta}")
     q, kk, v = fourier_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, w.amplitude, seed=3,
                                  dtype=w.dtype, device=DEV)
     scale = cabf.default_scale(g)
-    qp, kp, vp = cabf.permute(q, kk, v, g)
-    cnt, idx = cabf.build_block_mask(qp, kp, g, 0.0, sta, scale, topk=k)
+    qp, kp, vp, ws = cabf.permute_pool(q, kk, v, g)
+    cnt, idx = cabf.build_block_mask_pooled(ws, g, 0.0, sta, scale, topk=k)
     op = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, scale)
     torch.cuda.synchronize()
     if sta is None:
@@ -168,11 +248,6 @@ def test_full_size_topk_static_ratio(ratio, sta):
         qh, kh, vh = (to_np(t[0, hd]) for t in (qp, kp, vp))
         info = oracle.build_block_mask(qh, kh, og, scale, 0.0, sta, topk=k)
         compare_masks(cnt[0, hd], idx[0, hd], info, 0.0, label=f"top-k head {hd}")
-        gmask = oracle.lists_to_mask(cnt[0, hd].cpu().numpy(), idx[0, hd].cpu().numpy(), og.nb)
-        same = ~(gmask != info["mask"]).any(-1)
-        use = [b for b in blocks if same[b]]
-        sub = np.zeros_like(info["kv_count"])
-        sub[use] = info["kv_count"][use]
-        ref_o, _ = oracle.bsa_forward(qh, kh, vh, sub, info["kv_index"], og, scale)
-        rows = np.concatenate([np.arange(b * 64, (b + 1) * 64) for b in use])
-        compare_attention(op[0, hd], ref_o, True, rows=rows, label=f"top-k head {hd}")
+        ref_o, _ = attention_on_gpu_lists(qh, kh, vh, cnt[0, hd].cpu().numpy(),
+                                          idx[0, hd].cpu().numpy(), og, scale, blocks)
+        compare_attention(op[0, hd], ref_o, True, rows=sample_rows(blocks), label=f"top-k head {hd}")

@@ -94,14 +94,18 @@ def test_pooled_mask_matches_oracle(name, thr, sta, scale, topk):
 
 
 def test_pooled_mask_full_size_agrees_with_unfused():
-    """Wan-14B 720p: the fused pair and the unfused pair build the same lists
-    except on rows whose cut the oracle's exemption rule calls ill-posed; the
-    probabilities agree to 2e-5 relative."""
+    """Wan-14B 720p: the fused pair and the unfused pair reorder identically and
+    their probabilities agree to 2e-5 relative; on every head where their lists
+    differ, both are checked against the oracle (every differing row must be a
+    correct cut of the fp64 row). The fused path alone is checked against the
+    oracle at full size in test_gpu_full."""
     w = WORKLOADS["wan14b-720p"]
     g = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
+    og = oracle.Grid(w.T, w.H, w.W, w.P)
     q, k, v = fourier_video_qkv(w.T, w.H, w.W, w.heads, w.head_dim, w.amplitude, seed=2,
                                 dtype=w.dtype, device=DEV)
     thr = 0.7935
+    scale = cabf.default_scale(g)
     qp, kp, vp = cabf.permute(q, k, v, g)
     c1, i1, p1 = cabf.build_block_mask(qp, kp, g, thr, return_probs=True)
     fq, fk, fv, ws = cabf.permute_pool(q, k, v, g)
@@ -115,16 +119,12 @@ def test_pooled_mask_full_size_agrees_with_unfused():
     same = (c1 == c2) & (i1 == i2).logical_or(
         torch.arange(i1.shape[-1], device=DEV) >= c1.unsqueeze(-1)).all(-1)
     differ = int((~same).sum())
-    say(f"full-size fused vs unfused: {differ} of {same.numel()} rows differ")
-    # rows that differ must be ill-posed for the oracle on that head
-    for pos in torch.nonzero(~same)[:8].tolist():
-        b, h, i = pos
-        og = oracle.Grid(w.T, w.H, w.W, w.P)
-        info = oracle.build_block_mask(to_np(qp[b, h])[None, None], to_np(kp[b, h])[None, None],
-                                       og, cabf.default_scale(g), thr)
-        e1, e2 = oracle.exempt_rows(info, thr)
-        assert (e1 | e2)[0, 0, i], pos
-    assert differ <= max(8, same.numel() // 1000)
+    heads = sorted({h for _, h, _ in torch.nonzero(~same).tolist()})
+    say(f"full-size fused vs unfused: {differ} of {same.numel()} rows differ, heads {heads}")
+    for hd in heads:
+        info = oracle.build_block_mask(to_np(qp[0, hd]), to_np(kp[0, hd]), og, scale, thr)
+        compare_masks(c1[0, hd], i1[0, hd], info, thr, label=f"unfused head {hd}")
+        compare_masks(c2[0, hd], i2[0, hd], info, thr, label=f"fused head {hd}")
 
 
 SUBSET_CASES = [

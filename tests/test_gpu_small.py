@@ -12,8 +12,9 @@ import torch
 
 import content_adaptive_block_fractal_amd as cabf
 import oracle
-from synth import fourier_video_qkv
-from tests.parity import compare_attention, compare_masks, say, to_np
+from synth import fourier_video_qkv, gaussian_video_qkv
+from tests.parity import (assert_inputs_discriminate, compare_attention, compare_masks,
+                          rescale_rows, say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -208,6 +209,46 @@ def test_attention_on_oracle_lists(name, thr, sta):
     compare_attention(op, ref_o, q.dtype == torch.bfloat16, lse, ref_lse, label=name)
 
 
+SHARP_SCALE = 3.5   # times 1/sqrt(d): token-independent inputs, weights on a few keys
+
+
+@pytest.mark.parametrize("name,thr", [("ragged-bf16-d128", 0.3), ("wide-bf16-d128", 0.6),
+                                      ("ragged-bf16-d64", 0.5), ("one-row-high-bf16", 0.2)])
+def test_attention_sharp_on_oracle_lists(name, thr):
+    """Inputs that a wrong kernel cannot pass: token-independent Q, K, V at
+    scale 3.5/sqrt(d), on ragged grids with partial patches, over the oracle's
+    lists. A kernel with uniform weights or a wrong V key order misses by more
+    than ten times the tolerance (planted in the oracle's inputs on the CPU),
+    and the lazy rescale of the online softmax fires; the GPU, in both visit
+    orders, stays within the tolerance."""
+    T, H, W, heads, d, _, _ = GRIDS[name]
+    say(f"sharp attention {name} thr={thr}")
+    q, k, v = gaussian_video_qkv(T, H, W, heads, d, seed=6, device=DEV)
+    g = cabf.Geom(1, heads, d, T, H, W, 8)
+    og = oracle.Grid(T, H, W, 8)
+    s = SHARP_SCALE / math.sqrt(d)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    torch.cuda.synchronize()
+    qn, kn, vn = to_np(qp), to_np(kp), to_np(vp)
+    info = oracle.build_block_mask(qn, kn, og, s, thr, None)
+    cnt = torch.from_numpy(info["kv_count"]).to(DEV)
+    idx = torch.from_numpy(info["kv_index"]).to(DEV)
+    ref_o, ref_lse = oracle.bsa_forward(qn, kn, vn, info["kv_count"], info["kv_index"], og, s)
+    blocks = list(range(og.nb))
+    hits = 0
+    for hd in range(heads):
+        c, ix = info["kv_count"][0, hd], info["kv_index"][0, hd]
+        assert_inputs_discriminate(qn[0, hd], kn[0, hd], vn[0, hd], c, ix, og, s, blocks,
+                                   ref_o[0, hd])
+        hits += rescale_rows(qn[0, hd], kn[0, hd], c, ix, og, s, blocks)[0]
+    say(f"rows whose list-order pass must rescale: {hits}")
+    assert hits > 0
+    for det in (True, False):
+        op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=det)
+        torch.cuda.synchronize()
+        compare_attention(op, ref_o, True, lse, ref_lse, label=f"sharp {name} det={det}")
+
+
 @pytest.mark.parametrize("name", ["wide-bf16-d128", "ragged-bf16-d64"])
 def test_attention_visit_orders(name):
     """Deterministic mode (lists walked from their first entry) is bit-identical
@@ -235,6 +276,39 @@ def test_attention_visit_orders(name):
         compare_attention(o3, ref_o, True, l3, ref_lse, label=f"{name} clock-phased #{rep}")
 
 
+@pytest.mark.parametrize("name", ["ragged-bf16-d128", "ragged-bf16-d64", "ragged-f32-d128"])
+def test_attention_ignores_finite_pad_values(name):
+    """Pad slots of qp, kp, vp holding large finite values (instead of the
+    zeros cabf_permute writes) leave every real row within the tolerance of
+    the oracle's attention computed with zero pads (pad keys get weight 0).
+    fp32 rows are bit-identical; bf16 rows may differ in the last bits,
+    because a running max raised for any row of a wave (pad rows included)
+    re-bases the exponentials of all its rows."""
+    g, og, q, k, v = make(name)
+    s = cabf.default_scale(g)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, 0.4, None, s)
+    o1, l1 = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=True)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle.bsa_forward(to_np(qp), to_np(kp), to_np(vp), cnt.cpu().numpy(),
+                                        idx.cpu().numpy(), og, s)
+    pad_np = ~oracle.valid_slots(og)
+    pad = torch.from_numpy(pad_np).to(DEV)
+    assert bool(pad.any())
+    for t, val in ((qp, -300.0), (kp, 250.0), (vp, 1000.0)):
+        t[:, :, pad] = val
+    o2, l2 = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=True)
+    torch.cuda.synchronize()
+    real = np.nonzero(~pad_np)[0]
+    assert torch.isfinite(o2[:, :, ~pad]).all()
+    bf16 = q.dtype == torch.bfloat16
+    compare_attention(o2[0].permute(1, 0, 2), ref_o[0].transpose(1, 0, 2), bf16,
+                      l2[0].T, ref_lse[0].T, rows=real, label=f"{name} pad values")
+    if not bf16:
+        assert torch.equal(o1[:, :, ~pad], o2[:, :, ~pad])
+        assert torch.equal(l1[:, :, ~pad], l2[:, :, ~pad])
+
+
 def test_attention_rows_with_no_blocks_and_arbitrary_lists():
     g, og, q, k, v = make("ragged-bf16-d128")
     nb = og.nb
@@ -255,25 +329,25 @@ def test_attention_rows_with_no_blocks_and_arbitrary_lists():
 
 
 @pytest.mark.parametrize("name,thr,sta", [("tiny-f32-d64", 0.2, (1, 1, 1)),
-                                          ("ragged-bf16-d128", 0.5, (1, 1, 1))])
+                                          ("ragged-bf16-d128", 0.5, (1, 1, 1)),
+                                          ("wide-bf16-d128", 0.8, None)])
 def test_layer_end_to_end(name, thr, sta):
     """permute_pool -> build_block_mask_pooled -> bsa_forward -> unpermute (the
-    layer helper) on the GPU against the oracle's layer; query blocks whose
-    lists differ (exempt rows) are excluded."""
+    layer helper) on the GPU against the oracle: the lists against the
+    oracle's cut (differing rows must be correct cuts), every raster row
+    against the oracle's attention over the GPU's own lists."""
     say(f"layer {name}")
     g, og, q, k, v = make(name)
     s = cabf.default_scale(g)
     o, (cnt, idx) = cabf.layer(q, k, v, g, thr, sta, s)
     torch.cuda.synchronize()
-    ref_o, info = oracle.layer(to_np(q), to_np(k), to_np(v), og, s, thr, sta)
-    gmask = oracle.lists_to_mask(cnt.cpu().numpy(), idx.cpu().numpy(), og.nb)
-    same_blocks = ~(gmask != info["mask"]).any(-1)                   # [B, h, nb]
-    # raster rows whose block kept the same list
-    blk_of_row = oracle.fractal_positions(og) // og.block
-    rows = same_blocks[..., blk_of_row]
-    say(f"layer rows compared: {int(rows.sum())} of {rows.size}")
-    o_np, r_np = to_np(o)[rows], ref_o[rows]
-    err = np.abs(o_np - r_np)
+    qn, kn, vn = (oracle.permute(to_np(t), og) for t in (q, k, v))
+    info = oracle.build_block_mask(qn, kn, og, s, thr, sta)
+    compare_masks(cnt, idx, info, thr, label=f"layer {name}")
+    ref_op, _ = oracle.bsa_forward(qn, kn, vn, cnt.cpu().numpy(), idx.cpu().numpy(), og, s)
+    ref_o = oracle.unpermute(ref_op, og)
+    err = np.abs(to_np(o) - ref_o)
+    say(f"layer {name}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
     if q.dtype == torch.bfloat16:
         assert err.max() <= 2e-2 and err.mean() <= 2e-3
     else:

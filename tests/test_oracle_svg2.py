@@ -163,3 +163,15 @@ def test_mixture_generator_has_recoverable_clusters():
     out = svg2.kmeans(x, init, 10)
     sizes = np.sort(out["counts"])
     assert sizes[0] > 100          # no component lost: every cluster holds a real group
+
+
+def test_kept_density_counts_token_pairs():
+    """Hand-counted: query clusters of 2 and 3 tokens, key clusters of 1, 3
+    and 2 tokens; the first query cluster keeps key clusters 0 and 2 (2 x 3
+    pairs), the second keeps cluster 1 (3 x 3 pairs): 15 of 5 x 6 pairs."""
+    q_off = np.array([0, 2, 5])
+    k_off = np.array([0, 1, 4, 6])
+    mask = np.array([[True, False, True], [False, True, False]])
+    assert svg2.kept_density(dict(q_off=q_off, k_off=k_off, sel=dict(mask=mask))) == 0.5
+    every = np.ones((2, 3), dtype=bool)
+    assert svg2.kept_density(dict(q_off=q_off, k_off=k_off, sel=dict(mask=every))) == 1.0
