@@ -27,6 +27,7 @@ CABF_BF16, CABF_F32 = 0, 1
 
 EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_permute_pool", "cabf_unpermute",
             "cabf_mask_workspace_bytes", "cabf_build_block_mask", "cabf_build_block_mask_topk",
+            "cabf_build_block_mask_noalloc",
             "cabf_build_block_mask_pooled", "cabf_build_sta_mask", "cabf_bsa_forward",
             "cabf_bsa_forward_subset", "cabf_bsa_backward_workspace_bytes", "cabf_bsa_backward",
             "cabf_kmeans_workspace_bytes", "cabf_kmeans", "cabf_gather_rows",
@@ -81,6 +82,8 @@ def _load():
                                                  ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
         "cabf_build_block_mask_topk": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, I32,
                                                       ctypes.POINTER(_Sta), P, P, P, P, SZ, P]),
+        "cabf_build_block_mask_noalloc": (ctypes.c_int, [G, ctypes.c_int, P, P, F32, F32,
+                                                         ctypes.POINTER(_Sta), P, P, P, P]),
         "cabf_build_block_mask_pooled": (ctypes.c_int, [G, F32, F32, I32, ctypes.POINTER(_Sta),
                                                         P, P, P, P, SZ, P]),
         "cabf_build_sta_mask": (ctypes.c_int, [G, ctypes.POINTER(_Sta), P, P, P]),
@@ -245,6 +248,30 @@ def cabf_build_block_mask(geom: Geom, qp, kp, scale: float, thr: float, sta, kv_
             _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), bp,
             ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(qp))
     _check("cabf_build_block_mask" if topk is None else "cabf_build_block_mask_topk", st)
+
+
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # CABF_NOALLOC_SCRATCH_BYTES
+
+
+def cabf_build_block_mask_noalloc(geom: Geom, qp, kp, scale: float, thr: float, sta, kv_count,
+                                  kv_index, block_prob=None):
+    """cabf_build_block_mask with the library's static device scratch instead of a
+    workspace: allocates nothing (for callers that cannot allocate)."""
+    s = geom.sizes()
+    nb = s["n_blocks"]
+    ps = (geom.batch, geom.heads, s["tokens_padded"], geom.head_dim)
+    lead = (geom.batch, geom.heads, nb)
+    sta_c = None
+    if sta is not None:
+        sta_c = ctypes.byref(_Sta(1, int(sta[0]), int(sta[1]), int(sta[2])))
+    bp = None if block_prob is None else _dev(block_prob, lead + (nb,), torch.float32,
+                                              "block_prob")
+    st = _lib.cabf_build_block_mask_noalloc(
+        ctypes.byref(geom.c()), _dtype_code(qp), _dev(qp, ps, None, "qp"),
+        _dev(kp, ps, qp.dtype, "kp"), float(scale), float(thr), sta_c,
+        _dev(kv_count, lead, torch.int32, "kv_count"),
+        _dev(kv_index, lead + (nb,), torch.int32, "kv_index"), bp, _stream(qp))
+    _check("cabf_build_block_mask_noalloc", st)
 
 
 def cabf_build_block_mask_pooled(geom: Geom, scale: float, thr: float, k: int, sta, kv_count,

@@ -17,8 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcabf.so")
 
-SOURCES = ["api.cpp", "permute.hip", "mask.hip", "attention.hip", "attention_simple.hip",
-           "attention_mfma.hip", "attention_bwd.hip", "kmeans.hip", "svg.hip", "probe.hip"]
+SOURCES = ["api.cpp", "permute.hip", "mask.hip", "mask_noalloc.hip", "attention.hip",
+           "attention_simple.hip", "attention_mfma.hip", "attention_bwd.hip", "kmeans.hip", "svg.hip",
+           "probe.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

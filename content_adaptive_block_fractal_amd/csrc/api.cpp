@@ -59,6 +59,37 @@ int launched() {
   return e == hipSuccess ? CABF_OK : CABF_EHIP;
 }
 
+// Arguments of the mask entry points, validated (CABF_OK or the status).
+struct MaskCall {
+  Geo geo;
+  bool sta_on = false;
+  int dt = 0, dy = 0, dx = 0;
+};
+
+int check_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void* kp, bool pooled,
+               float scale, float thr, const cabf_sta* sta, const int32_t* kv_count,
+               const int32_t* kv_index, const float* block_prob, MaskCall* c) {
+  const int st = make_geo(g, &c->geo);
+  if (st != CABF_OK) return st;
+  if (!pooled && (elem_bytes(dtype) == 0 || qp == nullptr || kp == nullptr)) return CABF_EINVAL;
+  if (kv_count == nullptr || kv_index == nullptr) return CABF_EINVAL;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
+  if (!(thr >= 0.0f && thr <= 1.0f)) return CABF_EINVAL;
+  if (reinterpret_cast<uintptr_t>(qp) % 16 || reinterpret_cast<uintptr_t>(kp) % 16 ||
+      reinterpret_cast<uintptr_t>(kv_count) % 4 || reinterpret_cast<uintptr_t>(kv_index) % 4 ||
+      reinterpret_cast<uintptr_t>(block_prob) % 4)
+    return CABF_EINVAL;
+  if (sta != nullptr && sta->enabled) {
+    if (sta->dt < 0 || sta->dy < 0 || sta->dx < 0) return CABF_EINVAL;
+    c->sta_on = true;
+    c->dt = sta->dt;
+    c->dy = sta->dy;
+    c->dx = sta->dx;
+  }
+  if (c->geo.nb > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
+  return CABF_OK;
+}
+
 // Shared by the CDF (topk = 0) and the top-k entry points.
 // pooled: the block means are already in the workspace (cabf_permute_pool),
 // qp, kp and dtype are unused
@@ -66,34 +97,19 @@ int build_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, const void*
                float scale, float thr, int topk, const cabf_sta* sta, int32_t* kv_count,
                int32_t* kv_index, float* block_prob, void* workspace, size_t workspace_bytes,
                hipStream_t stream) {
-  Geo geo;
-  const int st = make_geo(g, &geo);
+  MaskCall c;
+  const int st = check_mask(g, dtype, qp, kp, pooled, scale, thr, sta, kv_count, kv_index,
+                            block_prob, &c);
   if (st != CABF_OK) return st;
-  if (!pooled && (elem_bytes(dtype) == 0 || qp == nullptr || kp == nullptr)) return CABF_EINVAL;
-  if (kv_count == nullptr || kv_index == nullptr || workspace == nullptr) return CABF_EINVAL;
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return CABF_EINVAL;
-  if (!(thr >= 0.0f && thr <= 1.0f)) return CABF_EINVAL;
-  if (reinterpret_cast<uintptr_t>(qp) % 16 || reinterpret_cast<uintptr_t>(kp) % 16 ||
-      reinterpret_cast<uintptr_t>(workspace) % 256 || reinterpret_cast<uintptr_t>(kv_count) % 4 ||
-      reinterpret_cast<uintptr_t>(kv_index) % 4 || reinterpret_cast<uintptr_t>(block_prob) % 4)
-    return CABF_EINVAL;
-  bool sta_on = false;
-  int dt = 0, dy = 0, dx = 0;
-  if (sta != nullptr && sta->enabled) {
-    if (sta->dt < 0 || sta->dy < 0 || sta->dx < 0) return CABF_EINVAL;
-    sta_on = true;
-    dt = sta->dt;
-    dy = sta->dy;
-    dx = sta->dx;
-  }
-  if (geo.nb > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
-  if (workspace_bytes < cabf::mask_workspace_layout(geo).total) return CABF_EWORKSPACE;
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 256) return CABF_EINVAL;
+  if (workspace_bytes < cabf::mask_workspace_layout(c.geo).total) return CABF_EWORKSPACE;
   if (pooled)
-    cabf::launch_mask_from_pooled(geo, scale, thr, topk, sta_on, dt, dy, dx, kv_count, kv_index,
-                                  block_prob, workspace, stream);
+    cabf::launch_mask_from_pooled(c.geo, scale, thr, topk, c.sta_on, c.dt, c.dy, c.dx, kv_count,
+                                  kv_index, block_prob, workspace, stream);
   else
-    cabf::launch_build_block_mask(geo, dtype == CABF_BF16, qp, kp, scale, thr, topk, sta_on, dt,
-                                  dy, dx, kv_count, kv_index, block_prob, workspace, stream);
+    cabf::launch_build_block_mask(c.geo, dtype == CABF_BF16, qp, kp, scale, thr, topk, c.sta_on,
+                                  c.dt, c.dy, c.dx, kv_count, kv_index, block_prob, workspace,
+                                  stream);
   return launched();
 }
 
@@ -205,6 +221,22 @@ int cabf_build_block_mask(const cabf_geom* g, cabf_dtype dtype, const void* qp, 
                           size_t workspace_bytes, hipStream_t stream) {
   return build_mask(g, dtype, qp, kp, false, scale, thr, 0, sta, kv_count, kv_index, block_prob,
                     workspace, workspace_bytes, stream);
+}
+
+int cabf_build_block_mask_noalloc(const cabf_geom* g, cabf_dtype dtype, const void* qp,
+                                  const void* kp, float scale, float thr, const cabf_sta* sta,
+                                  int32_t* kv_count, int32_t* kv_index, float* block_prob,
+                                  hipStream_t stream) {
+  MaskCall c;
+  const int st = check_mask(g, dtype, qp, kp, false, scale, thr, sta, kv_count, kv_index,
+                            block_prob, &c);
+  if (st != CABF_OK) return st;
+  if (cabf::noalloc_pairs_per_pass(c.geo) < 1) return CABF_EWORKSPACE;
+  const int ls = cabf::launch_build_block_mask_noalloc(c.geo, elem_bytes(dtype), qp, kp, scale,
+                                                       thr, c.sta_on, c.dt, c.dy, c.dx, kv_count,
+                                                       kv_index, block_prob, stream);
+  if (ls != CABF_OK) return ls;
+  return launched();
 }
 
 int cabf_build_block_mask_topk(const cabf_geom* g, cabf_dtype dtype, const void* qp,

@@ -30,6 +30,16 @@ void launch_build_block_mask(const Geo& g, bool bf16, const void* qp, const void
                              int32_t* kv_count, int32_t* kv_index, float* block_prob,
                              void* workspace, hipStream_t stream);
 
+// The CDF mask (no top-k) with the workspace in a fixed device array instead
+// of a caller buffer (mask_noalloc.hip): noalloc_pairs_per_pass is the number
+// of (batch, head) pairs one pass of the array holds (0: a single pair does
+// not fit); the launcher returns a cabf_status.
+int64_t noalloc_pairs_per_pass(const Geo& g);
+int launch_build_block_mask_noalloc(const Geo& g, int elem_bytes, const void* qp, const void* kp,
+                                    float scale, float thr, bool sta_on, int dt, int dy, int dx,
+                                    int32_t* kv_count, int32_t* kv_index, float* block_prob,
+                                    hipStream_t stream);
+
 // logits, selection and compaction from pooled means already in the workspace
 void launch_mask_from_pooled(const Geo& g, float scale, float thr, int topk, bool sta_on, int dt,
                              int dy, int dx, int32_t* kv_count, int32_t* kv_index,

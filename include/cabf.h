@@ -165,6 +165,27 @@ int cabf_build_block_mask_topk(const cabf_geom* g, cabf_dtype dtype,
                                float* block_prob, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Device bytes cabf_build_block_mask_noalloc keeps in a static array on
+ * every GPU it runs on, for the life of the process. */
+#define CABF_NOALLOC_SCRATCH_BYTES ((size_t)96 * 1024 * 1024)
+
+/* cabf_build_block_mask without a workspace argument, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): it allocates nothing. Its
+ * workspace is a static device array of CABF_NOALLOC_SCRATCH_BYTES on the
+ * stream's GPU, through which the (batch, head) pairs pass a few at a time;
+ * the results are the same as cabf_build_block_mask's, bit for bit. All
+ * calls on one GPU share that array: calls that overlap on a GPU (two
+ * streams or two threads at once) race and must be serialised by the
+ * caller. A geometry whose single (batch, head) pair needs more than the
+ * array (2 nb head_dim + nb * ceil64(nb) floats; nb above about 4,600 at
+ * head_dim 128) returns CABF_EWORKSPACE before any launch. Other arguments,
+ * outputs, errors and limits as for cabf_build_block_mask. */
+int cabf_build_block_mask_noalloc(const cabf_geom* g, cabf_dtype dtype,
+                                  const void* qp, const void* kp, float scale, float thr,
+                                  const cabf_sta* sta, int32_t* kv_count, int32_t* kv_index,
+                                  float* block_prob, hipStream_t stream);
+
 /* Steps 2-5 of cabf_build_block_mask (k = 0: the CDF cut at thr) or of
  * cabf_build_block_mask_topk (k >= 1), from the block means that
  * cabf_permute_pool left in `workspace` (the same buffer, same geometry).

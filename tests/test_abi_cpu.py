@@ -135,6 +135,29 @@ def test_mask_argument_checks():
 
 
 @no_gpu
+def test_noalloc_mask_argument_checks():
+    """The no-allocation mask rejects bad arguments, and a geometry whose one
+    (batch, head) pair needs more than the static scratch, before any launch."""
+    def call(g=None, **kw):
+        a = dict(qp=DUMMY, scale=0.125, thr=0.2, cnt=DUMMY2, dt=0)
+        a.update(kw)
+        return L.cabf_build_block_mask_noalloc(geom() if g is None else g, a["dt"], a["qp"], DUMMY,
+                                               a["scale"], a["thr"], None, a["cnt"], DUMMY2,
+                                               None, NULL)
+    assert call(qp=NULL) == cabf.CABF_EINVAL
+    assert call(cnt=NULL) == cabf.CABF_EINVAL
+    assert call(scale=0.0) == cabf.CABF_EINVAL
+    assert call(thr=2.0) == cabf.CABF_EINVAL
+    assert call(dt=3) == cabf.CABF_EINVAL
+    assert call(geom(P=4)) == cabf.CABF_EUNSUPPORTED
+    # nb = 125 * 5 * 8 = 5000 blocks at head_dim 128: 2*5000*128 + 5000*5056 floats > 96 MiB
+    big = geom(head_dim=128, T=125, H=40, W=64)
+    assert (2 * 5000 * 128 + 5000 * 5056) * 4 > cabf.NOALLOC_SCRATCH_BYTES
+    assert call(big) == cabf.CABF_EWORKSPACE
+    assert call(geom(head_dim=128, T=9000, H=8, W=8)) == cabf.CABF_EUNSUPPORTED   # nb > 8192
+
+
+@no_gpu
 def test_topk_and_sta_mask_argument_checks():
     g = geom()
     need = L.cabf_mask_workspace_bytes(g)
