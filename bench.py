@@ -52,9 +52,6 @@ def parse():
                     help="also time the semantic-permutation (k-means + top-p) variant (0 to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle CPU-baseline sample (0 to skip)")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="run one plain device copy of this many MiB before the steps "
-                         "(reference dispatch for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -156,6 +153,34 @@ def profiled_traffic(workload: str):
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def roofline(attn_tflops: float, attn_ms: float, traffic):
+    """The attention kernel against the bf16 matrix-core roofline (its algorithmic bound: a dense
+    64x64xd contraction per kept tile), with the measured bytes it moves beyond L2 per launch
+    (rocprofv3 counters, scaled by the bytes the permute kernel of the same profiled run is known
+    to move) and the rate they imply, which names the resource that actually limits it."""
+    r = {
+        "bound": "mfma",
+        "kernel": "bsa_fwd_mfma (cabf_bsa_forward)",
+        "achieved": attn_tflops,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": attn_tflops / PEAK_BF16_TFLOPS,
+        "traffic": traffic,
+        "traffic_unit": ("bytes per launch beyond L2 (MALL/HBM): FETCH_SIZE and WRITE_SIZE, each "
+                         "scaled by the bytes reorder_pool_blocks is known to read and write in the "
+                         "same profiled run"),
+        "algorithmic_unit": "4*64*64*head_dim flops per kept 64x64 tile",
+        "avg_launch_ms": attn_ms,
+    }
+    if traffic is not None:
+        rate = traffic / (attn_ms * 1e-3) / 1e9
+        r["traffic_GBps"] = rate
+        r["traffic_frac_of_hbm_peak"] = rate / PEAK_HBM_GBS
+        r["limiter"] = ("beyond-L2 traffic" if rate / PEAK_HBM_GBS > r["frac"]
+                        else "matrix cores")
+    return r
 
 
 def measure_subset(cabf, geom, bufs, thr, sta, flags, steps: int, frac: float = 0.25):
@@ -435,30 +460,76 @@ def _oracle_head_sample(job):
                 t_mask=t_mask, t_attn=t_attn, t_equiv=t_attn + t_mask * done / g.nb)
 
 
+def _cpu_worker(job_path: str, out_path: str):
+    """Entry of one CPU-baseline worker process (``bench.py --cpu-worker JOB OUT``): reads its
+    head from an .npz file, runs _oracle_head_sample, writes the result as JSON."""
+    import numpy as np
+    with np.load(job_path, allow_pickle=False) as z:
+        sta = tuple(int(x) for x in z["sta"]) if z["sta"].size else None
+        job = (z["q"], z["k"], z["v"], tuple(int(x) for x in z["grid"]), int(z["head_dim"]),
+               float(z["thr"]), sta, float(z["budget_s"]))
+    with open(out_path, "w") as fh:
+        json.dump(_oracle_head_sample(job), fh)
+
+
+def host_cpu_model() -> str:
+    """The CPU model name as lscpu reports it (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(q, k, v, w, thr, sta, budget_s):
     """The CPU oracle on a bounded sample of the same layer, heads sharded over worker processes
     (one per host core, up to 16 and up to the head count): each worker runs head h's permute and
     block mask (all rows) plus attention for the first query blocks that fit the time budget, on
-    one thread. value = the sum of the workers' throughputs (each measured while all run)."""
+    one thread. value = the sum of the workers' throughputs (each measured while all run).
+    Workers are plain child processes (this script with --cpu-worker), each given its head in an
+    .npz file and waited for, so none outlives the benchmark."""
+    import subprocess
+    import tempfile
+
+    import numpy as np
     cores = len(os.sched_getaffinity(0))
     workers = max(1, min(cores, 16, w.heads))
     f = lambda t, hd: t[0, hd].float().cpu().numpy()
-    jobs = [(f(q, hd), f(k, hd), f(v, hd), (w.T, w.H, w.W, w.P), w.head_dim, thr, sta, budget_s)
-            for hd in range(workers)]
     results = None
-    if workers > 1:
+    with tempfile.TemporaryDirectory(prefix="cabf_cpu_") as tmp:
+        procs = []
         try:
-            import multiprocessing as mp
-            from concurrent.futures import ProcessPoolExecutor
-            with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
-                results = list(ex.map(_oracle_head_sample, jobs))
+            for hd in range(workers):
+                job = os.path.join(tmp, f"job{hd}.npz")
+                np.savez(job, q=f(q, hd), k=f(k, hd), v=f(v, hd),
+                         grid=np.array([w.T, w.H, w.W, w.P]), head_dim=w.head_dim, thr=thr,
+                         sta=np.array(sta if sta else [], dtype=np.int64), budget_s=budget_s)
+                out = os.path.join(tmp, f"out{hd}.json")
+                env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1",
+                           MKL_NUM_THREADS="1")
+                procs.append((subprocess.Popen([sys.executable, os.path.abspath(__file__),
+                                                "--cpu-worker", job, out], env=env), out))
+            results = []
+            for p, out in procs:
+                if p.wait() != 0:
+                    raise RuntimeError(f"worker exited with {p.returncode}")
+                with open(out) as fh:
+                    results.append(json.load(fh))
         except Exception as exc:       # a host without working worker processes: one core
-            print(f"cpu baseline: worker processes unavailable ({exc!r}); using one core",
+            for p, _ in procs:
+                if p.poll() is None:
+                    p.kill()
+                    p.wait()
+            print(f"cpu baseline: worker processes failed ({exc!r}); using one core",
                   file=sys.stderr)
             results = None
     if results is None:
         workers = 1
-        results = [_oracle_head_sample(jobs[0])]
+        results = [_oracle_head_sample((f(q, 0), f(k, 0), f(v, 0), (w.T, w.H, w.W, w.P),
+                                        w.head_dim, thr, sta, budget_s))]
     value = sum(r["flops"] / r["t_equiv"] for r in results) / 1e12
     r0 = results[0]
     per_layer_s = (r0["t_mask"] + r0["t_attn"] / r0["done"] * r0["nb"]) * w.heads * w.batch
@@ -475,12 +546,15 @@ def cpu_baseline(q, k, v, w, thr, sta, budget_s):
                    f"({done} query blocks, {tiles} kept tiles in all, ~{budget_s:.0f} s per worker); "
                    f"fp64 numpy"),
         "extrapolated_s_per_layer_one_core": per_layer_s,
-        "host_cpu": platform.processor() or platform.machine(),
+        "host_cpu": host_cpu_model(),
         "host_cores_available": cores,
     }
 
 
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--cpu-worker":
+        _cpu_worker(sys.argv[2], sys.argv[3])
+        return
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -532,13 +606,6 @@ def main():
                     wall_ms=wall_ms, stage_ms_median=med, stage_ms_mean=mean,
                     stage_ms_min={kk: min(vv) for kk, vv in stages.items()})
 
-    if args.copy_mib > 0:
-        n = args.copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     sta = (1, 1, 1) if args.sta else None
     flags = cabf.BSA_DETERMINISTIC if args.deterministic else 0
     main_run = measure(args.sparsity, sta, args.steps, args.warmup, flags, fused=not args.unfused)
@@ -579,19 +646,7 @@ def main():
                        else "reorder fused with block pooling (cabf_permute_pool, "
                             "cabf_build_block_mask_pooled)",
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "bsa_fwd_mfma (cabf_bsa_forward)",
-            "achieved": attn_tflops,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": profiled_traffic(w.name),
-            "traffic_unit": ("bytes per launch beyond L2: FETCH_SIZE and WRITE_SIZE, each scaled by "
-                             "what it reads for a 1 GiB copy in the same profiled run"),
-            "algorithmic_unit": "4*64*64*head_dim flops per kept 64x64 tile",
-            "avg_launch_ms": attn_ms,
-        },
+        "roofline": roofline(attn_tflops, attn_ms, profiled_traffic(w.name)),
         "stages_ms": main_run["stage_ms_mean"],
         "stages_ms_median": main_run["stage_ms_median"],
         "stages_ms_min": main_run["stage_ms_min"],
