@@ -94,7 +94,16 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 __device__ inline void store_elem(float* p, float v) { *p = v; }
 __device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
+// Longest block row the paired forward (attention_pair.hip) merges in LDS,
+// and its sweep period per kept entry of a list (ticks of the 100 MHz clock).
+constexpr int kPairMaxBlocks = 8192;
+constexpr uint32_t kPairSweepTicks = 130;
+
 void launch_bsa_forward_simple(const AttnArgs& a, bool bf16, int D, hipStream_t stream);
+// The bf16 forward over pairs of query blocks (frames 2t, 2t+1 of a patch) and
+// the union of their lists; nb <= kPairMaxBlocks. T = frames.
+void launch_bsa_forward_pair(const AttnArgs& a, int D, int T, bool phased, hipStream_t stream);
+int pairs_per_head(int T, int Ty, int Tx);
 void launch_bsa_forward_mfma(const AttnArgs& a, int D, bool phased, hipStream_t stream);
 // The bf16 forward over a list of n global query block ids only.
 void launch_bsa_forward_subset_mfma(const AttnArgs& a, int D, bool phased,

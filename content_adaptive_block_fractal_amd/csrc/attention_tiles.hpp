@@ -121,12 +121,14 @@ __device__ inline void hold_back_to_sweep(int jb, int nb, uint32_t period, int l
   }
 }
 
-template <int D>
+// Tile copies by a workgroup of NT threads (NT / 64 waves).
+template <int D, int NT = kThreads>
 struct Stage {
   static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
-  static constexpr int kIters = kBlock * kChunks / kThreads;   // chunks per thread per tensor
+  static constexpr int kIters = kBlock * kChunks / NT;         // chunks per thread per tensor
   static constexpr int kTile = kBlock * kChunks;               // 16-byte chunks per K (or V) tile
-  static constexpr int kRowsPerIter = kThreads / kChunks;      // rows one pass of the workgroup fills
+  static constexpr int kRowsPerIter = NT / kChunks;            // rows one pass of the workgroup fills
+  static constexpr int kWavesPerGroup = NT / 64;
 };
 
 // Direct-to-LDS copy of one K or V tile into a ring slot: each wave
@@ -136,9 +138,9 @@ struct Stage {
 // swizzle's period in the row, so a lane's source offset in pass i is its
 // offset in pass 0 plus a constant (added to the scalar base). The offsets are
 // the same for every tile.
-template <int D, bool IS_V>
+template <int D, bool IS_V, int NT = kThreads>
 __device__ inline uint32_t tile_load_offset(int wave, int lane) {
-  using S = Stage<D>;
+  using S = Stage<D, NT>;
   static_assert(S::kRowsPerIter % 16 == 0, "swizzle period");
   const int phys = wave * 64 + lane;
   const int row = phys / S::kChunks;
@@ -152,9 +154,9 @@ __device__ inline uint32_t tile_load_offset(int wave, int lane) {
 // s_waitcnt immediate: vmcnt = the loads of one tile copy (Stage::kIters),
 // expcnt and lgkmcnt not waited on (gfx9 encoding: vmcnt[3:0] and [15:14],
 // expcnt[6:4], lgkmcnt[11:8])
-template <int D>
+template <int D, int NT = kThreads>
 constexpr int kWaitAllButOneTile() {
-  constexpr int n = Stage<D>::kIters;
+  constexpr int n = Stage<D, NT>::kIters;
   static_assert(n < 64, "vmcnt range");
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
@@ -167,11 +169,12 @@ constexpr int kWaitAllButOneTile() {
 // which keeps the number of loads per copy, and so the vmcnt bookkeeping,
 // unchanged. A wave's share is 4 rows at d = 128 (half a patch row) and 8 at
 // d = 64 (a whole patch row).
-template <int D>
+template <int D, int NT = kThreads>
 __device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4* slot,
                                                 uint32_t off, int wave, int real_rows = kBlock,
                                                 int real_cols = kP) {
-  using S = Stage<D>;
+  using S = Stage<D, NT>;
+  constexpr int kW = S::kWavesPerGroup;
   // An empty asm makes each load's scalar base (tile and pass) and lane
   // offset opaque, so the compiler cannot fold (base + lane offset) once and
   // rebuild every other address with 64-bit vector adds: the base stays in
@@ -181,12 +184,12 @@ __device__ __forceinline__ void issue_tile_load(const uint16_t* tile_src, u32x4*
 #pragma unroll
   for (int i = 0; i < S::kIters; ++i) {
     // rows of this wave's instruction: first_row .. first_row + kRowsPerIter / kWaves - 1
-    const int first_row = i * S::kRowsPerIter + wave * (S::kRowsPerIter / kWaves);
+    const int first_row = i * S::kRowsPerIter + wave * (S::kRowsPerIter / kW);
     const bool used = first_row < real_rows && (first_row & (kP - 1)) < real_cols;
     const uint16_t* src = used ? tile_src + i * S::kRowsPerIter * D : tile_src;
     const char* base = reinterpret_cast<const char*>(src);
     asm volatile("" : "+s"(base));
-    __builtin_amdgcn_global_load_lds(base + o, slot + (i * kWaves + wave) * 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + o, slot + (i * kW + wave) * 64, 16, 0, 0);
   }
 }
 

@@ -21,7 +21,7 @@ _spec = _iu.spec_from_file_location(
 build = _iu.module_from_spec(_spec)
 _spec.loader.exec_module(build)
 
-FILES = ["attention_mfma.hip", "attention_bwd.hip"]
+FILES = ["attention_mfma.hip", "attention_pair.hip", "attention_bwd.hip"]
 
 
 def _have_hipcc() -> bool:

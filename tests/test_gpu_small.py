@@ -191,10 +191,14 @@ ATTN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("deterministic", [False, True])
 @pytest.mark.parametrize("name,thr,sta", ATTN_CASES)
-def test_attention_on_oracle_lists(name, thr, sta):
-    """bsa_forward fed the oracle's own block lists equals the oracle's attention."""
-    say(f"attention {name} thr={thr} sta={sta}")
+def test_attention_on_oracle_lists(name, thr, sta, deterministic):
+    """bsa_forward fed the oracle's own block lists equals the oracle's attention,
+    in the default order (one query block per workgroup) and in list order (bf16:
+    pairs of blocks over the union of their lists; odd frame and patch counts
+    leave single blocks)."""
+    say(f"attention {name} thr={thr} sta={sta} deterministic={deterministic}")
     g, og, q, k, v = make(name)
     s = cabf.default_scale(g)
     qp, kp, vp = cabf.permute(q, k, v, g)
@@ -203,7 +207,8 @@ def test_attention_on_oracle_lists(name, thr, sta):
     info = oracle.build_block_mask(qn, kn, og, s, thr, sta)
     cnt = torch.from_numpy(info["kv_count"]).to(DEV)
     idx = torch.from_numpy(info["kv_index"]).to(DEV)
-    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True,
+                               deterministic=deterministic)
     torch.cuda.synchronize()
     ref_o, ref_lse = oracle.bsa_forward(qn, kn, vn, info["kv_count"], info["kv_index"], og, s)
     compare_attention(op, ref_o, q.dtype == torch.bfloat16, lse, ref_lse, label=name)
@@ -309,7 +314,10 @@ def test_attention_ignores_finite_pad_values(name):
         assert torch.equal(l1[:, :, ~pad], l2[:, :, ~pad])
 
 
-def test_attention_rows_with_no_blocks_and_arbitrary_lists():
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_attention_rows_with_no_blocks_and_arbitrary_lists(deterministic):
+    """Random lists (no structure) with an empty row: in list order the empty
+    block shares its workgroup with a block that keeps tiles."""
     g, og, q, k, v = make("ragged-bf16-d128")
     nb = og.nb
     qp, kp, vp = cabf.permute(q, k, v, g)
@@ -319,11 +327,12 @@ def test_attention_rows_with_no_blocks_and_arbitrary_lists():
     mask[0, 1, :5] = False
     cnt_np, idx_np = oracle.mask_to_lists(mask)
     op, lse = cabf.bsa_forward(qp, kp, vp, torch.from_numpy(cnt_np).to(DEV),
-                               torch.from_numpy(idx_np).to(DEV), g, return_lse=True)
+                               torch.from_numpy(idx_np).to(DEV), g, return_lse=True,
+                               deterministic=deterministic)
     torch.cuda.synchronize()
     ref_o, ref_lse = oracle.bsa_forward(to_np(qp), to_np(kp), to_np(vp), cnt_np, idx_np, og,
                                         cabf.default_scale(g))
-    compare_attention(op, ref_o, True, lse, ref_lse, label="arbitrary lists")
+    compare_attention(op, ref_o, True, lse, ref_lse, label=f"arbitrary lists det={deterministic}")
     assert torch.all(op[0, 0, 3 * 64:4 * 64] == 0)
     assert torch.all(torch.isneginf(lse[0, 0, 3 * 64:4 * 64]))
 
