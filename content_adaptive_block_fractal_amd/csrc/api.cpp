@@ -355,7 +355,7 @@ int cabf_bsa_backward(const cabf_geom* g, cabf_dtype dtype, const void* qp, cons
 size_t cabf_kmeans_workspace_bytes(const cabf_seq* s, int32_t clusters) {
   int64_t BH = 0;
   if (check_seq(s, &BH) != CABF_OK || clusters < 1 || clusters > s->n ||
-      clusters > cabf::kMaxBlocks || !cabf::kmeans_keys_fit(BH, clusters))
+      clusters > cabf::kMaxBlocks)
     return 0;
   return cabf::kmeans_workspace_layout(BH, s->n, clusters, s->head_dim).total;
 }
@@ -373,7 +373,7 @@ int cabf_kmeans(const cabf_seq* s, cabf_dtype dtype, const void* x, int32_t clus
       labels == nullptr || perm == nullptr || offsets == nullptr || workspace == nullptr)
     return CABF_EINVAL;
   if (clusters < 1 || clusters > s->n || iters < 0) return CABF_EINVAL;
-  if (clusters > cabf::kMaxBlocks || !cabf::kmeans_keys_fit(BH, clusters)) return CABF_EUNSUPPORTED;
+  if (clusters > cabf::kMaxBlocks) return CABF_EUNSUPPORTED;
   if (misaligned(x, 16) || misaligned(init, 4) || misaligned(centroids, 16) ||
       misaligned(counts, 4) || misaligned(labels, 4) || misaligned(perm, 4) ||
       misaligned(offsets, 4) || misaligned(workspace, 256))

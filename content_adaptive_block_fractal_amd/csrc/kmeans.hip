@@ -12,17 +12,22 @@
 //               on the matrix cores (x is exact in bf16), fp32 accumulation,
 //               so the dot product is close to fp32 accuracy. Ties go to the
 //               lowest index.
-//   sort        stable radix sort of the keys (bh << bits) | label over all
-//               heads at once (token index as payload): the permutation of
-//               every head, clusters contiguous, original order inside a
-//               cluster
-//   km_offsets  offsets[c] = first sorted position of the head with label >= c
-//   km_update   mean of the members, summed in sorted (token) order, so the
-//               result is deterministic; an empty cluster keeps its centroid
+//   counting sort of every head's labels, stable (original order inside a
+//   cluster), in three passes over chunks of 1024 tokens:
+//     km_hist     per-chunk label histogram (LDS)
+//     km_scan     per head: cluster sizes and offsets (offsets[c] = first
+//                 position of cluster c), and each chunk's first position
+//                 inside every cluster
+//     km_scatter  per chunk, in token order 64 at a time: a token's position
+//                 is its chunk's next free position in its cluster plus the
+//                 number of lanes before it with the same label (found with
+//                 one ballot per label bit); perm[position] = token
+//   km_update   mean of the members, summed in permutation (token) order, so
+//               the result is deterministic; an empty cluster keeps its
+//               centroid
 // After the last update a final assignment and sort make labels, counts and
 // the permutation consistent with the returned centroids.
 #include <hip/hip_runtime.h>
-#include <hipcub/hipcub.hpp>
 
 #include <cmath>
 #include <cstdint>
@@ -104,7 +109,6 @@ __global__ __launch_bounds__(256) void km_assign(const uint16_t* __restrict__ x,
                                                  const uint16_t* __restrict__ terms,
                                                  const float* __restrict__ norm,
                                                  int32_t* __restrict__ label,
-                                                 uint32_t* __restrict__ sort_key, int key_bits,
                                                  int n, int Cp, int64_t rows_padded,
                                                  int tiles_per_bh) {
   constexpr int kKS = D / 16;
@@ -214,36 +218,116 @@ __global__ __launch_bounds__(256) void km_assign(const uint16_t* __restrict__ x,
       best[g] = ob;
       best_c[g] = oc;
     }
-    if (h == 0 && tok[g] < n) {
-      label[bh * n + tok[g]] = best_c[g];
-      sort_key[bh * n + tok[g]] = (static_cast<uint32_t>(bh) << key_bits) | best_c[g];
-    }
+    if (h == 0 && tok[g] < n) label[bh * n + tok[g]] = best_c[g];
   }
 }
 
-// offsets[bh, c] = first position of head bh's sorted keys with label >= c,
-// c <= C (all keys of a head share its high bits); counts on request
-__global__ __launch_bounds__(256) void km_offsets(const uint32_t* __restrict__ sorted_key,
-                                                  int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ counts, int n, int C,
-                                                  int key_bits, int64_t total /* BH * (C + 1) */) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int64_t bh = e / (C + 1);
-  const int c = static_cast<int>(e - bh * (C + 1));
-  const uint32_t* s = sorted_key + bh * n;
-  const uint32_t head = static_cast<uint32_t>(bh) << key_bits;
-  auto lower = [&](uint32_t key) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s[mid] < key) lo = mid + 1; else hi = mid;
+constexpr int kSortChunk = 1024;   // tokens per chunk of the counting sort (one wave each)
+
+// hist[bh, chunk, c] = tokens of the chunk with label c (one wave per chunk;
+// LDS histogram of C bins)
+__global__ __launch_bounds__(64) void km_hist(const int32_t* __restrict__ label,
+                                              int32_t* __restrict__ hist, int n, int C,
+                                              int chunks) {
+  extern __shared__ int32_t bins[];
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x / chunks;
+  const int ch = static_cast<int>(blockIdx.x - bh * chunks);
+  for (int c = lane; c < C; c += 64) bins[c] = 0;
+  __syncthreads();
+  const int t0 = ch * kSortChunk, t1 = min(t0 + kSortChunk, n);
+  const int32_t* lb = label + bh * n;
+  for (int t = t0 + lane; t < t1; t += 64) atomicAdd(&bins[lb[t]], 1);
+  __syncthreads();
+  int32_t* out = hist + (bh * chunks + ch) * static_cast<int64_t>(C);
+  for (int c = lane; c < C; c += 64) out[c] = bins[c];
+}
+
+// Per head (one workgroup of 256): hist[bh, chunk, c] becomes the number of
+// tokens of cluster c in the chunks before `chunk`; counts[c] (if requested)
+// and offsets[c] = sum of the sizes of clusters below c, offsets[C] = n.
+__global__ __launch_bounds__(256) void km_scan(int32_t* __restrict__ hist,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ counts, int C, int chunks) {
+  extern __shared__ int32_t size[];   // [C], then 256 partial sums
+  int32_t* const part = size + C;
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  int32_t* hb = hist + bh * chunks * static_cast<int64_t>(C);
+  for (int c = tid; c < C; c += 256) {
+    int run = 0;
+    for (int ch = 0; ch < chunks; ++ch) {
+      const int v = hb[static_cast<int64_t>(ch) * C + c];
+      hb[static_cast<int64_t>(ch) * C + c] = run;
+      run += v;
     }
-    return lo;
-  };
-  const int at = lower(head | static_cast<uint32_t>(c));
-  offsets[e] = at;
-  if (c > 0 && counts != nullptr) counts[bh * C + c - 1] = at - lower(head | static_cast<uint32_t>(c - 1));
+    size[c] = run;
+    if (counts != nullptr) counts[bh * C + c] = run;
+  }
+  __syncthreads();
+  // exclusive scan of size[0 .. C): thread tid takes a contiguous range
+  const int per = (C + 255) / 256;
+  const int c0 = min(tid * per, C), c1 = min(c0 + per, C);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += size[c];
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int run = part[tid];
+  int32_t* ob = offsets + bh * (C + 1);
+  for (int c = c0; c < c1; ++c) {
+    ob[c] = run;
+    run += size[c];
+  }
+  if (tid == 255) ob[C] = run;
+}
+
+// perm[bh, position] = token, one wave per chunk walking its tokens in order,
+// 64 at a time. next[c] (LDS) = the position the chunk's next token of
+// cluster c takes; lanes with equal labels are found with one ballot per
+// label bit, so a token's position is next[c] plus the number of lanes before
+// it with the same label (the sort is stable).
+__global__ __launch_bounds__(64) void km_scatter(const int32_t* __restrict__ label,
+                                                 const int32_t* __restrict__ hist,
+                                                 const int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ perm, int n, int C,
+                                                 int chunks, int bits) {
+  extern __shared__ int32_t next[];
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x / chunks;
+  const int ch = static_cast<int>(blockIdx.x - bh * chunks);
+  const int32_t* hrow = hist + (bh * chunks + ch) * static_cast<int64_t>(C);
+  const int32_t* ob = offsets + bh * (C + 1);
+  for (int c = lane; c < C; c += 64) next[c] = ob[c] + hrow[c];
+  __syncthreads();
+  const int t0 = ch * kSortChunk, t1 = min(t0 + kSortChunk, n);
+  const int32_t* lb = label + bh * n;
+  int32_t* pb = perm + bh * n;
+  const uint64_t below = (uint64_t{1} << lane) - 1u;
+  for (int base = t0; base < t1; base += 64) {
+    const int t = base + lane;
+    const bool in = t < t1;
+    const int c = in ? lb[t] : 0;
+    uint64_t same = __ballot(in);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (c >> b) & 1;
+      const uint64_t ones = __ballot(in && bit);
+      same &= bit ? ones : ~ones;
+    }
+    const int before = __popcll(same & below);
+    if (in) pb[next[c] + before] = t;
+    __syncthreads();                       // every lane has read next[] for this batch
+    if (in && before == 0) next[c] += __popcll(same);
+    __syncthreads();
+  }
 }
 
 // One workgroup per cluster: wave w sums members b + w*q .. (a contiguous
@@ -309,32 +393,17 @@ __global__ __launch_bounds__(256) void km_update(const uint16_t* __restrict__ x,
   }
 }
 
-__global__ __launch_bounds__(256) void km_iota(int32_t* __restrict__ v, int n, int64_t total) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e < total) v[e] = static_cast<int32_t>(e % n);
-}
-
 int bits_for(int64_t values) {
   int b = 1;
   while ((int64_t{1} << b) < values) ++b;
   return b;
 }
 
-// One device-wide stable radix sort over the combined keys of all heads.
-size_t sort_temp_bytes(int64_t BH, int n, int C) {
-  size_t bytes = 0;
-  const hipError_t e = hipcub::DeviceRadixSort::SortPairs(
-      nullptr, bytes, static_cast<const uint32_t*>(nullptr), static_cast<uint32_t*>(nullptr),
-      static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr),
-      static_cast<int>(BH * n), 0, bits_for(C) + bits_for(BH), nullptr);
-  return e == hipSuccess ? bytes : 0;   // 0: the sort itself reports the failure at launch
-}
+int sort_chunks(int n) { return (n + kSortChunk - 1) / kSortChunk; }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
 }  // namespace
-
-bool kmeans_keys_fit(int64_t BH, int C) { return bits_for(C) + bits_for(BH) <= 32; }
 
 KmeansWorkspace kmeans_workspace_layout(int64_t BH, int n, int C, int D) {
   KmeansWorkspace w{};
@@ -342,12 +411,7 @@ KmeansWorkspace kmeans_workspace_layout(int64_t BH, int n, int C, int D) {
   size_t o = 0;
   w.terms = o;   o += align256(3 * static_cast<size_t>(BH) * Cp * D * sizeof(uint16_t));
   w.norm = o;    o += align256(static_cast<size_t>(BH) * Cp * sizeof(float));
-  w.keys = o;    o += align256(static_cast<size_t>(BH) * n * sizeof(uint32_t));
-  w.sorted = o;  o += align256(static_cast<size_t>(BH) * n * sizeof(uint32_t));
-  w.iota = o;    o += align256(static_cast<size_t>(BH) * n * sizeof(int32_t));
-  w.sort_tmp = o;
-  w.sort_tmp_bytes = sort_temp_bytes(BH, n, C);
-  o += align256(w.sort_tmp_bytes);
+  w.hist = o;    o += align256(static_cast<size_t>(BH) * sort_chunks(n) * C * sizeof(int32_t));
   w.total = o;
   return w;
 }
@@ -359,17 +423,12 @@ int launch_kmeans(int64_t BH, int n, int D, int C, int iters, const void* x, con
   char* ws = static_cast<char*>(workspace);
   uint16_t* terms = reinterpret_cast<uint16_t*>(ws + w.terms);
   float* norm = reinterpret_cast<float*>(ws + w.norm);
-  uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
-  uint32_t* sorted = reinterpret_cast<uint32_t*>(ws + w.sorted);
-  int32_t* iota = reinterpret_cast<int32_t*>(ws + w.iota);
-  void* tmp = ws + w.sort_tmp;
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + w.hist);
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   const int Cp = (C + 31) / 32 * 32;
   const int64_t rows_padded = BH * Cp;
-  const int64_t items = BH * n;
   auto blocks = [](int64_t work, int per) { return dim3(static_cast<unsigned>((work + per - 1) / per)); };
 
-  hipLaunchKernelGGL(km_iota, blocks(items, 256), dim3(256), 0, stream, iota, n, items);
   if (D == 64)
     hipLaunchKernelGGL((km_init<64>), blocks(BH * C * 64, 256), dim3(256), 0, stream, xs, init,
                        cent, n, C, BH * C);
@@ -377,27 +436,30 @@ int launch_kmeans(int64_t BH, int n, int D, int C, int iters, const void* x, con
     hipLaunchKernelGGL((km_init<128>), blocks(BH * C * 128, 256), dim3(256), 0, stream, xs, init,
                        cent, n, C, BH * C);
   const int tiles = (n + 255) / 256;
-  const int bits = bits_for(C);               // label bits of a sort key
-  const int end_bit = bits + bits_for(BH);
+  const int bits = bits_for(C);               // label bits
+  const int chunks = sort_chunks(n);
+  const unsigned sort_grid = static_cast<unsigned>(BH * chunks);
+  const size_t bins_bytes = static_cast<size_t>(C) * sizeof(int32_t);
   for (int it = 0; it <= iters; ++it) {
     if (D == 64) {
       hipLaunchKernelGGL((km_prep<64>), blocks(rows_padded, 4), dim3(256), 0, stream, cent, terms,
                          norm, C, Cp, rows_padded);
       hipLaunchKernelGGL((km_assign<64>), dim3(static_cast<unsigned>(BH * tiles)), dim3(256), 0,
-                         stream, xs, terms, norm, label, keys, bits, n, Cp, rows_padded, tiles);
+                         stream, xs, terms, norm, label, n, Cp, rows_padded, tiles);
     } else {
       hipLaunchKernelGGL((km_prep<128>), blocks(rows_padded, 4), dim3(256), 0, stream, cent, terms,
                          norm, C, Cp, rows_padded);
       hipLaunchKernelGGL((km_assign<128>), dim3(static_cast<unsigned>(BH * tiles)), dim3(256), 0,
-                         stream, xs, terms, norm, label, keys, bits, n, Cp, rows_padded, tiles);
+                         stream, xs, terms, norm, label, n, Cp, rows_padded, tiles);
     }
-    size_t tmp_bytes = w.sort_tmp_bytes;
-    const hipError_t e = hipcub::DeviceRadixSort::SortPairs(
-        tmp, tmp_bytes, keys, sorted, iota, perm, static_cast<int>(items), 0, end_bit, stream);
-    if (e != hipSuccess) return -1;
     const bool last = it == iters;
-    hipLaunchKernelGGL(km_offsets, blocks(BH * (C + 1), 256), dim3(256), 0, stream, sorted,
-                       offsets, last ? counts : nullptr, n, C, bits, BH * (C + 1));
+    hipLaunchKernelGGL(km_hist, dim3(sort_grid), dim3(64), bins_bytes, stream, label, hist, n, C,
+                       chunks);
+    hipLaunchKernelGGL(km_scan, dim3(static_cast<unsigned>(BH)), dim3(256),
+                       bins_bytes + 256 * sizeof(int32_t), stream, hist, offsets,
+                       last ? counts : nullptr, C, chunks);
+    hipLaunchKernelGGL(km_scatter, dim3(sort_grid), dim3(64), bins_bytes, stream, label, hist,
+                       offsets, perm, n, C, chunks, bits);
     if (last) break;
     if (D == 64)
       hipLaunchKernelGGL((km_update<64>), dim3(static_cast<unsigned>(BH * C)), dim3(256), 0, stream,

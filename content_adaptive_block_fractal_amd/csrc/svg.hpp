@@ -13,13 +13,11 @@ namespace cabf {
 
 // Byte offsets inside the k-means workspace.
 struct KmeansWorkspace {
-  size_t terms, norm, keys, sorted, iota, sort_tmp, sort_tmp_bytes, total;
+  size_t terms, norm, hist, total;
 };
 KmeansWorkspace kmeans_workspace_layout(int64_t BH, int n, int C, int D);
-// whether the sort keys (head << label bits | label) fit in 32 bits
-bool kmeans_keys_fit(int64_t BH, int C);
 
-// Returns 0, or -1 if the sort could not be launched.
+// Always returns 0.
 int launch_kmeans(int64_t BH, int n, int D, int C, int iters, const void* x, const int32_t* init,
                   float* cent, int32_t* counts, int32_t* label, int32_t* perm, int32_t* offsets,
                   void* workspace, hipStream_t stream);

@@ -53,7 +53,7 @@ def check_permutation(labels, perm, offsets, counts, C):
     assert np.array_equal(counts, np.diff(want_off))
 
 
-@pytest.mark.parametrize("d,C", [(128, 40), (64, 17), (128, 1)])
+@pytest.mark.parametrize("d,C", [(128, 40), (64, 17), (128, 1), (128, 1500), (64, 2900)])
 def test_kmeans_steps_match_oracle(d, C):
     n, heads = 3000, 2
     q, _, _ = mixture(n, heads, d, seed=4)
