@@ -214,15 +214,17 @@ def measure_subset(cabf, geom, bufs, thr, sta, flags, steps: int, frac: float = 
 
 
 def measured_peaks(cabf, dev):
-    """What this GPU sustains: a dense bf16 matrix-core loop (cabf_mfma_peak_probe)
-    and a plain 2 GiB device copy, timed with HIP events."""
+    """What this GPU sustains: a dense bf16 matrix-core loop (the measurement aid
+    libcabf_probe.so) and a plain 2 GiB device copy, timed with HIP events."""
     import torch
+
+    from content_adaptive_block_fractal_amd import peak_probe
     wgs, iters = 2048, 20000
     out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
-    cabf.cabf_mfma_peak_probe(wgs, 200, out)
+    peak_probe.mfma_peak(wgs, 200, out)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    cabf.cabf_mfma_peak_probe(wgs, iters, out)
+    peak_probe.mfma_peak(wgs, iters, out)
     e1.record()
     torch.cuda.synchronize()
     flops = wgs * 4 * iters * 8 * 2.0 * 32 * 32 * 16

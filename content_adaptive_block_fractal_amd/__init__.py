@@ -33,7 +33,7 @@ EXPORTED = ("cabf_geom_sizes", "cabf_permute", "cabf_permute_pool", "cabf_unperm
             "cabf_kmeans_workspace_bytes", "cabf_kmeans", "cabf_gather_rows",
             "cabf_scatter_rows", "cabf_cluster_select_workspace_bytes", "cabf_cluster_select",
             "cabf_cluster_attention_workspace_bytes", "cabf_cluster_attention",
-            "cabf_mfma_peak_probe", "cabf_status_string")
+            "cabf_status_string")
 
 SEQ_PAD_ROWS = 64      # extra zero rows of permuted tensors for cabf_cluster_attention
 
@@ -103,7 +103,6 @@ def _load():
         "cabf_cluster_attention_workspace_bytes": (SZ, [Q, I32, I32]),
         "cabf_cluster_attention": (ctypes.c_int, [Q, ctypes.c_int, I32, I32, P, P, P, P, P, P, P,
                                                   F32, P, P, P, SZ, P]),
-        "cabf_mfma_peak_probe": (ctypes.c_int, [I32, I32, P, P]),
         "cabf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -582,14 +581,6 @@ def cabf_cluster_attention(seq: Seq, cq: int, ck: int, qp, kp, vp, q_offsets, k_
         _dev(kv_index, lead + (cq, ck), torch.int32, "kv_index"), float(scale),
         _dev(op, shape, qp.dtype, "op"), lp, ptr, nbytes, _stream(qp))
     _check("cabf_cluster_attention", st)
-
-
-def cabf_mfma_peak_probe(workgroups: int, iters: int, out):
-    """Dense bf16 matrix-core loop (measurement aid); out: float32 [workgroups * 256]."""
-    st = _lib.cabf_mfma_peak_probe(int(workgroups), int(iters),
-                                   _dev(out, (int(workgroups) * 256,), torch.float32, "out"),
-                                   _stream(out))
-    _check("cabf_mfma_peak_probe", st)
 
 
 def kmeans(x, clusters: int, init, iters: int):

@@ -480,12 +480,6 @@ int cabf_cluster_attention(const cabf_seq* s, cabf_dtype dtype, int32_t cq, int3
   return launched();
 }
 
-int cabf_mfma_peak_probe(int32_t workgroups, int32_t iters, float* out, hipStream_t stream) {
-  if (workgroups < 1 || iters < 1 || out == nullptr || misaligned(out, 4)) return CABF_EINVAL;
-  cabf::launch_mfma_peak(workgroups, iters, out, stream);
-  return launched();
-}
-
 const char* cabf_status_string(int status) {
   switch (status) {
     case CABF_OK: return "ok";

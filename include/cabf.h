@@ -52,7 +52,11 @@ typedef enum {
 
 typedef enum {
   CABF_BF16 = 0,           /* bfloat16 tensors, fp32 accumulation and softmax   */
-  CABF_F32 = 1             /* float32 tensors                                   */
+  CABF_F32 = 1,            /* float32 tensors                                   */
+  /* Not dtypes: they make every 32-bit int a value of the type, so that any
+   * int a caller passes can be read and rejected (CABF_EINVAL). */
+  CABF_DTYPE_RANGE_LOW_ = -2147483647 - 1,
+  CABF_DTYPE_RANGE_HIGH_ = 2147483647
 } cabf_dtype;
 
 /* Flags of cabf_bsa_forward. */
@@ -378,14 +382,6 @@ int cabf_cluster_attention(const cabf_seq* s, cabf_dtype dtype, int32_t cq, int3
                            const int32_t* kv_count, const int32_t* kv_index, float scale,
                            void* op, float* lse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
-
-/* Measurement aid, not part of the method: a dense bf16 matrix-core loop
- * (each wave runs iters x 8 independent 32x32x16 products, 262144 * iters
- * flops per wave) whose time gives the matrix-core rate the chip sustains
- * under load, to set beside the published peak. workgroups of 256 threads
- * (4 waves); out: workgroups * 256 floats (device, output, values without
- * meaning). workgroups, iters >= 1, else CABF_EINVAL. */
-int cabf_mfma_peak_probe(int32_t workgroups, int32_t iters, float* out, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* cabf_status_string(int status);

@@ -304,8 +304,12 @@ def test_fused_entry_argument_checks():
 
 
 @no_gpu
-def test_probe_argument_checks():
-    assert L.cabf_mfma_peak_probe(0, 10, DUMMY2, NULL) == cabf.CABF_EINVAL
-    assert L.cabf_mfma_peak_probe(4, 0, DUMMY2, NULL) == cabf.CABF_EINVAL
-    assert L.cabf_mfma_peak_probe(4, 10, NULL, NULL) == cabf.CABF_EINVAL
-    assert L.cabf_mfma_peak_probe(4, 10, ctypes.c_void_p(0x200002), NULL) == cabf.CABF_EINVAL
+def test_probe_library_is_separate_and_checks_arguments():
+    """The benchmark's matrix-core probe lives in its own library, outside the C ABI."""
+    from content_adaptive_block_fractal_amd import peak_probe
+    lib = peak_probe._load()
+    assert not hasattr(L, "cabf_mfma_peak_probe")
+    assert lib.probe_mfma_peak(0, 10, DUMMY2, NULL) == -1
+    assert lib.probe_mfma_peak(4, 0, DUMMY2, NULL) == -1
+    assert lib.probe_mfma_peak(4, 10, NULL, NULL) == -1
+    assert lib.probe_mfma_peak(4, 10, ctypes.c_void_p(0x200002), NULL) == -1

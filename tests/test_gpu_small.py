@@ -364,9 +364,10 @@ def test_layer_end_to_end(name, thr, sta):
 
 
 def test_mfma_peak_probe_runs():
-    """The measurement aid: every lane writes the sum of its accumulators,
-    finite and positive (the products of positive inputs)."""
+    """The benchmark's measurement aid (its own library): every lane writes the
+    sum of its accumulators, finite and positive (products of positive inputs)."""
+    from content_adaptive_block_fractal_amd import peak_probe
     out = torch.full((8 * 256,), -1.0, device=DEV)
-    cabf.cabf_mfma_peak_probe(8, 3, out)
+    peak_probe.mfma_peak(8, 3, out)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all() and (out > 0).all()
