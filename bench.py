@@ -159,7 +159,7 @@ def roofline(attn_tflops: float, attn_ms: float, traffic):
     """The attention kernel against the bf16 matrix-core roofline (its algorithmic bound: a dense
     64x64xd contraction per kept tile), with the measured bytes it moves beyond L2 per launch
     (rocprofv3 counters, scaled by the bytes the permute kernel of the same profiled run is known
-    to move) and the rate they imply, which names the resource that actually limits it."""
+    to move) and the rate they imply, with the roof the kernel comes closest to."""
     r = {
         "bound": "mfma",
         "kernel": "bsa_fwd_mfma (cabf_bsa_forward)",
@@ -178,8 +178,9 @@ def roofline(attn_tflops: float, attn_ms: float, traffic):
         rate = traffic / (attn_ms * 1e-3) / 1e9
         r["traffic_GBps"] = rate
         r["traffic_frac_of_hbm_peak"] = rate / PEAK_HBM_GBS
-        r["limiter"] = ("beyond-L2 traffic" if rate / PEAK_HBM_GBS > r["frac"]
-                        else "matrix cores")
+        # the roof the kernel comes closest to (not necessarily what holds it there)
+        r["nearest_roof"] = ("beyond-L2 traffic vs the HBM peak" if rate / PEAK_HBM_GBS > r["frac"]
+                             else "matrix cores")
     return r
 
 
