@@ -32,7 +32,23 @@ struct AttnArgs {
   // agree to rounding but may differ bitwise between runs. 0 walks every list
   // from its first entry (bit-reproducible).
   uint32_t sweep_ticks;
+  // First work item of this launch: a pass in list order runs as a series of
+  // launches of as many workgroups as the device holds at once (see
+  // resident_workgroups), each over the next items.
+  int64_t item0;
 };
+
+// Workgroups of `kernel` (launched with `threads` threads and no dynamic LDS)
+// that the device of `stream` runs at once; 0 when the runtime cannot say.
+int64_t resident_workgroups(const void* kernel, int threads, hipStream_t stream);
+
+// Launches of a pass in list order: `launch(first, n)` for consecutive runs
+// of `per` items (all of them in one launch when per <= 0).
+template <typename F>
+void launch_in_generations(int64_t items, int64_t per, F&& launch) {
+  if (per <= 0) per = items;
+  for (int64_t first = 0; first < items; first += per) launch(first, items - first < per ? items - first : per);
+}
 
 // Real rows / columns of block b's 8x8 patch (pads sit at the bottom/right
 // edge of the padded frame).
@@ -94,15 +110,17 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 __device__ inline void store_elem(float* p, float v) { *p = v; }
 __device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
-// Longest block row the paired forward (attention_pair.hip) merges in LDS,
-// and its sweep period per kept entry of a list (ticks of the 100 MHz clock).
+// Longest block row the paired forward (attention_pair.hip) merges in LDS.
 constexpr int kPairMaxBlocks = 8192;
-constexpr uint32_t kPairSweepTicks = 130;
+// Rows of at least this many blocks count as long (see launch_bsa_forward).
+constexpr int kLongRowBlocks = 2048;
+// Launches of a list-order pass hold this many device-fulls of workgroups.
+constexpr int64_t kGenerationsPerLaunch = 1;
 
 void launch_bsa_forward_simple(const AttnArgs& a, bool bf16, int D, hipStream_t stream);
 // The bf16 forward over pairs of query blocks (frames 2t, 2t+1 of a patch) and
-// the union of their lists; nb <= kPairMaxBlocks. T = frames.
-void launch_bsa_forward_pair(const AttnArgs& a, int D, int T, bool phased, hipStream_t stream);
+// the union of their lists, in list order; nb <= kPairMaxBlocks. T = frames.
+void launch_bsa_forward_pair(const AttnArgs& a, int D, int T, hipStream_t stream);
 int pairs_per_head(int T, int Ty, int Tx);
 void launch_bsa_forward_mfma(const AttnArgs& a, int D, bool phased, hipStream_t stream);
 // The bf16 forward over a list of n global query block ids only.

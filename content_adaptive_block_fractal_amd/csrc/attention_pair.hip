@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bsa_fwd_pair(AttnArgs a, int 
   __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile];
   __shared__ uint32_t ulist[kPairMaxBlocks];              // union entries, ascending
   __shared__ uint32_t bits[2 * (kPairMaxBlocks / 32)];    // kept bits of A, then of B
-  __shared__ int scan[kPairWaves + 2];   // wave totals, union length, start
+  __shared__ int scan[kPairWaves + 1];   // wave totals, union length
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bsa_fwd_pair(AttnArgs a, int 
   const int li = lane & 31;
   const int h = lane >> 5;
 
-  const int64_t item = xcd_order(blockIdx.x, n_items);
+  const int64_t item = a.item0 + xcd_order(blockIdx.x, n_items);
   const int64_t bh = item / pairs_per_head;
   const int F = a.Ty * a.Tx;
   int blk_a, blk_b;
@@ -172,32 +172,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void bsa_fwd_pair(AttnArgs a, int 
   const float inv_c = 1.0f / cs;
   const int key0 = 32 * wk;
 
-  // Clock-phased start: the first union entry at or after the block the
-  // sweep has reached (see clock_phased_start), counted from the bitmaps by
-  // wave 0 and shared, so that every wave agrees on it.
-  if (wave == 0) {
-    int below = 0;
-    if (a.sweep_ticks != 0 && cnt > 1) {
-      const int swept = swept_block(sweep_period(counts, nb, a.sweep_ticks, lane), nb);
-      for (int w = lane; w < words; w += 64) {
-        const uint32_t u = bits[w] | bits[words + w];
-        const int lo = w * 32;
-        if (lo + 32 <= swept) below += __builtin_popcount(u);
-        else if (lo < swept) below += __builtin_popcount(u & ((1u << (swept - lo)) - 1u));
-      }
-#pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) below += __shfl_xor(below, sh);
-    }
-    if (lane == 0) scan[kPairWaves + 1] = below >= cnt ? 0 : below;
-  }
-  __syncthreads();
-  const int start = __builtin_amdgcn_readfirstlane(scan[kPairWaves + 1]);
-
   // union entries of the pass, 64 at a time, one per lane (from LDS)
   auto load_batch = [&](int b) {
-    int pos = min(b * 64 + lane, cnt - 1) + start;
-    pos -= pos >= cnt ? cnt : 0;
-    return ulist[pos];
+    return ulist[min(b * 64 + lane, cnt - 1)];
   };
   uint32_t batch_cur = 0, batch_nxt = 0;
   auto entry = [&](int t) {
@@ -410,16 +387,22 @@ int pairs_per_head(int T, int Ty, int Tx) {
   return (T / 2) * F + (T % 2 ? (F + 1) / 2 : 0);
 }
 
-void launch_bsa_forward_pair(const AttnArgs& args, int D, int T, bool phased, hipStream_t stream) {
+void launch_bsa_forward_pair(const AttnArgs& args, int D, int T, hipStream_t stream) {
   const int pph = pairs_per_head(T, args.Ty, args.Tx);
   const int64_t n = args.BH * pph;
   AttnArgs a = args;
-  a.sweep_ticks = phased ? kPairSweepTicks : 0u;
-  const unsigned grid = static_cast<unsigned>(n);
-  if (D == 64)
-    hipLaunchKernelGGL((bsa_fwd_pair<64>), dim3(grid), dim3(kPairThreads), 0, stream, a, pph, n);
-  else
-    hipLaunchKernelGGL((bsa_fwd_pair<128>), dim3(grid), dim3(kPairThreads), 0, stream, a, pph, n);
+  a.sweep_ticks = 0u;
+  const void* kernel = D == 64 ? reinterpret_cast<const void*>(&bsa_fwd_pair<64>)
+                               : reinterpret_cast<const void*>(&bsa_fwd_pair<128>);
+  const int64_t per = kGenerationsPerLaunch * resident_workgroups(kernel, kPairThreads, stream);
+  launch_in_generations(n, per, [&](int64_t first, int64_t count) {
+    a.item0 = first;
+    const unsigned grid = static_cast<unsigned>(count);
+    if (D == 64)
+      hipLaunchKernelGGL((bsa_fwd_pair<64>), dim3(grid), dim3(kPairThreads), 0, stream, a, pph, count);
+    else
+      hipLaunchKernelGGL((bsa_fwd_pair<128>), dim3(grid), dim3(kPairThreads), 0, stream, a, pph, count);
+  });
 }
 
 }  // namespace cabf

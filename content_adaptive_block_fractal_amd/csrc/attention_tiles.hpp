@@ -106,21 +106,6 @@ __device__ inline int clock_phased_start(const int32_t* head_counts, const int32
   return before >= cnt ? 0 : before;
 }
 
-// Pacing of a clock-phased pass: while key block jb (the next one the pass
-// reads) lies more than `lead` blocks ahead of the sweep (and less than half
-// the range, which would mean behind it), the calling wave sleeps about 1000
-// cycles at a time, at most 32 times; its workgroup then waits for it at the
-// next barrier. A workgroup that has run ahead of the others of its head
-// would fetch tiles that no other one needs yet.
-__device__ inline void hold_back_to_sweep(int jb, int nb, uint32_t period, int lead) {
-  for (int i = 0; i < 32; ++i) {
-    int ahead = jb - swept_block(period, nb);
-    ahead += ahead < 0 ? nb : 0;
-    if (ahead <= lead || 2 * ahead >= nb) break;
-    __builtin_amdgcn_s_sleep(16);
-  }
-}
-
 // Tile copies by a workgroup of NT threads (NT / 64 waves).
 template <int D, int NT = kThreads>
 struct Stage {

@@ -231,7 +231,9 @@ int cabf_build_sta_mask(const cabf_geom* g, const cabf_sta* sta,
  *   then stay in L2) and wraps around; the result is the same softmax sum in
  *   another order, so it may differ from run to run in the last bits.
  *   CABF_BSA_DETERMINISTIC walks every list from its first entry and gives
- *   bit-identical results on every run. fp32 is always deterministic. */
+ *   bit-identical results on every run. fp32, and bf16 rows of 2048 blocks
+ *   or more (long lists, which run fastest in list order), are always
+ *   deterministic. */
 int cabf_bsa_forward(const cabf_geom* g, cabf_dtype dtype,
                      const void* qp, const void* kp, const void* vp,
                      const int32_t* kv_count, const int32_t* kv_index, float scale,

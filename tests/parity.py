@@ -141,6 +141,15 @@ def compare_attention(op_gpu, ref_op, bf16: bool, lse_gpu=None, ref_lse=None, ro
         assert lerr <= LSE_ABS, lerr
 
 
+def sample_blocks(og, n):
+    """Query blocks to check: first, last, padded patches and a spread."""
+    bt, bty, btx = oracle.block_coords(og)
+    padded = np.nonzero((bty == og.Ty - 1) | (btx == og.Tx - 1))[0]
+    pick = {0, og.nb - 1, int(padded[0]), int(padded[-1]), int(padded[len(padded) // 2])}
+    pick |= set(np.linspace(0, og.nb - 1, n).astype(int).tolist())
+    return sorted(pick)
+
+
 def sample_rows(blocks, block=64):
     return np.concatenate([np.arange(b * block, (b + 1) * block) for b in blocks])
 

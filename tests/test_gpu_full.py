@@ -29,7 +29,7 @@ import content_adaptive_block_fractal_amd as cabf
 import oracle
 from synth import WORKLOADS, fourier_video_qkv, gaussian_video_qkv
 from tests.parity import (assert_inputs_discriminate, attention_on_gpu_lists, compare_attention,
-                          compare_masks, rescale_rows, sample_rows, say, to_np)
+                          compare_masks, rescale_rows, sample_blocks, sample_rows, say, to_np)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -50,15 +50,6 @@ def calibrate(build, g, target):
         else:
             hi = mid
     return hi
-
-
-def sample_blocks(og, n):
-    """Query blocks to check: first, last, padded patches and a spread."""
-    bt, bty, btx = oracle.block_coords(og)
-    padded = np.nonzero((bty == og.Ty - 1) | (btx == og.Tx - 1))[0]
-    pick = {0, og.nb - 1, int(padded[0]), int(padded[-1]), int(padded[len(padded) // 2])}
-    pick |= set(np.linspace(0, og.nb - 1, n).astype(int).tolist())
-    return sorted(pick)
 
 
 def geometry(name):
@@ -144,9 +135,10 @@ def test_full_size_timed_path(name, target, sta, scale):
 @pytest.mark.parametrize("name,target", [("wan14b-720p", 0.80), ("hunyuan-241f-768p", 0.85)])
 def test_full_size_sharp_attention(name, target):
     """Token-independent inputs at scale 3.5/sqrt(d) on the full geometry
-    (partial patches; 252-entry lists at 720p, ~600 at 768p, where the passes
-    are paced): the data can fail a wrong kernel, and the GPU stays within the
-    tolerance of the oracle over its own lists."""
+    (partial patches; 252-entry lists at 720p; ~600 at 768p, whose rows of
+    4026 blocks run the paired kernel in list order): the data can fail a
+    wrong kernel, and the GPU stays within the tolerance of the oracle over
+    its own lists."""
     w, g, og = geometry(name)
     s = SHARP_SCALE / math.sqrt(w.head_dim)
     say(f"full-size sharp attention {name} sparsity {target}")
@@ -155,7 +147,7 @@ def test_full_size_sharp_attention(name, target):
     mean_len = r["cnt"].float().mean().item()
     say(f"thr={r['thr']:.6f} mean list length {mean_len:.1f}")
     if name.startswith("hunyuan"):
-        assert mean_len >= 512       # the paced long-list passes run
+        assert mean_len >= 512       # long lists
     blocks = sample_blocks(og, 4)
     for hd in (0, w.heads - 1):
         qh, kh, vh, cnt_h, idx_h, ref_o, _ = check_head(r, g, og, hd, s, None, blocks, f"{name} sharp")

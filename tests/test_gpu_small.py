@@ -195,9 +195,7 @@ ATTN_CASES = [
 @pytest.mark.parametrize("name,thr,sta", ATTN_CASES)
 def test_attention_on_oracle_lists(name, thr, sta, deterministic):
     """bsa_forward fed the oracle's own block lists equals the oracle's attention,
-    in the default order (one query block per workgroup) and in list order (bf16:
-    pairs of blocks over the union of their lists; odd frame and patch counts
-    leave single blocks)."""
+    in the default order (bf16: clock-phased start) and in list order."""
     say(f"attention {name} thr={thr} sta={sta} deterministic={deterministic}")
     g, og, q, k, v = make(name)
     s = cabf.default_scale(g)
