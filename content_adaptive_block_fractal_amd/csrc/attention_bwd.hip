@@ -17,12 +17,13 @@
 //                  query blocks that keep it, ascending (through a bitmap)
 //   bwd_dkv        one workgroup of two four-wave groups per key block over
 //                  those query blocks, both groups on the same Q and dO
-//                  tiles: the dV group forms S = Q K^T, then dV^T += dO^T P;
-//                  the dK group S and dP = dO V^T, then dK^T += Q^T dS (Q, dO
-//                  rows from LDS; K, V in registers; dO^T, Q^T from
-//                  transposing LDS reads). Holding K, V and both accumulators
-//                  in every lane would take over 256 registers; split over
-//                  the groups, each wave stays within 256.
+//                  tiles: the dV group forms S = Q K^T and P, adds dV^T +=
+//                  dO^T P and hands P to the dK group through LDS; the dK
+//                  group forms dP = dO V^T, then dS = P (dP - D) and dK^T +=
+//                  Q^T dS (Q, dO rows from LDS; K or V in registers; dO^T,
+//                  Q^T from transposing LDS reads). Holding K, V and both
+//                  accumulators in every lane would take over 256 registers;
+//                  split over the groups, each wave stays within 256.
 // Every gradient kernel splits the 64 x 64 tile over 4 waves (two halves of
 // each side) and adds the two partial sums of a row once at the end, so with
 // list-order walks (the deterministic flag) every result is reproducible.
@@ -348,14 +349,21 @@ __global__ __launch_bounds__(256) void bwd_transpose(const uint32_t* __restrict_
 // dK and dV in one pass: one workgroup of eight waves per key block over the
 // query blocks that keep it. Waves 0-3 form the dV group, waves 4-7 the dK
 // group; in each group wave (wk, wq) takes key half wk and query half wq of
-// every tile, lane li holding key li of its half. Both groups read the same
-// Q and dO tiles, so a kept tile crosses the memory system once for both
-// gradients: the dV group copies Q, the dK
-// group dO. Per tile the dV group forms S and P and adds dV^T += dO^T P; the
-// dK group forms S, dP = dO V^T and dS = P (dP - D) and adds dK^T += Q^T dS.
-// A SIMD holds one wave of each group. Q, dO, lse and D of tile e+1 arrive
-// during tile e (two-slot rings; a third slot, with copies two tiles ahead,
-// was slower).
+// every tile, lane li holding key li of its half, so waves w and w + 4 hold
+// the same elements of a tile and share a SIMD. Both groups read the same Q
+// and dO tiles, so a kept tile crosses the memory system once for both
+// gradients (the dV group copies Q, the dK group dO).
+// The softmax weights are formed once: per tile e the dV group forms S = Q
+// K^T and P, adds dV^T += dO^T P, and leaves P (fp32) in LDS; the dK group
+// forms dP = dO V^T and keeps dP - D, and in the next tile, once the barrier
+// has made P visible, forms dS = P (dP - D) of tile e and adds dK^T += Q^T dS
+// with tile e's Q, still in its ring. The products of dS therefore run one
+// tile behind, and the dK group's dS work overlaps its own dP products of the
+// next tile. Rings: Q in four slots, copied two tiles ahead (kept one tile
+// after use); dO, P, lse and D in two, copied one tile ahead (dO two tiles
+// ahead as well was slower: 77 against 67 ms at 720p / 80%). Computing P once
+// instead of in both groups, and the deeper Q ring, took the pass from 74 to
+// 67 ms there.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uint16_t* __restrict__ dop,
@@ -368,9 +376,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   using S = Stage<D>;
   constexpr int kKS = D / 16;
   constexpr int kDT = D / 32;
-  __shared__ u32x4 q_slot0[S::kTile], q_slot1[S::kTile];
-  __shared__ u32x4 d_slot0[S::kTile], d_slot1[S::kTile];
+  __shared__ u32x4 q_slot[4][S::kTile];
+  __shared__ u32x4 d_slot[2][S::kTile];
   __shared__ f32x4 vec_slot[2][2][kBlock / 4];   // [slot][lse2, D][4 rows]
+  __shared__ f32x4 p_slot[2][4][4][64];          // [slot][wave of the group][r / 4][lane]: P, fp32
   __shared__ int start_sh;
 
   const int tid = threadIdx.x;
@@ -387,12 +396,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   const float* __restrict__ lse_h = lse2 + bh * a.N;
   const float* __restrict__ dl_h = delta + bh * a.N;
   const int64_t krow = item * kBlock + wk * 32 + li;        // global key row of this lane
-  const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(a.kp);
-  const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(a.vp);
-  bf16x8 kf[kKS];
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks)
-    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kg + krow * D + 16 * ks + 8 * h));
   const float c = a.scale_log2;
   f32x16 acc[kDT];
 #pragma unroll
@@ -440,46 +443,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
     }
     return r;
   };
-  // pad query rows (partial patches only: a uniform branch) get S = -inf,
-  // hence P = dS = 0
-  auto mask = [&](uint32_t pe, f32x16& s) {
-    const BlockExtent ext = packed_extent(pe);
-    if (!ext.full()) {
-      const uint32_t bits = real_accumulator_bits(ext, wq, h);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
-    }
-  };
-  // P of the tile in bf16 (dV group)
-  auto probs = [&](uint32_t pe, f32x16 s, const f32x4 (&vec)[2][kBlock / 4], bf16x8 (&wb)[2]) {
-    mask(pe, s);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 lv = vec[0][(row0 >> 2) + 2 * g + h];     // rows row0 + 8 g + 4 h .. + 3
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 4 * g + x;
-        wb[r >> 3][r & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x])));
-      }
-    }
-  };
-  // dS of the tile in bf16, from S and dP (dK group)
-  auto weights = [&](uint32_t pe, f32x16 s, const f32x16& dp, const f32x4 (&vec)[2][kBlock / 4],
-                     bf16x8 (&wb)[2]) {
-    mask(pe, s);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int m4 = (row0 >> 2) + 2 * g + h;              // rows row0 + 8 g + 4 h .. + 3
-      const f32x4 lv = vec[0][m4];
-      const f32x4 dv4 = vec[1][m4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 4 * g + x;
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x]));
-        wb[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dv4[x]));
-      }
-    }
-  };
   // acc^T += X^T W with X^T from transposing reads of the tile `xs` (dO for
   // the dV group, Q for the dK group)
   auto accumulate = [&](const u32x4* xs, const bf16x8 (&wb)[2]) {
@@ -504,8 +467,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
     }
   };
   const uint32_t off = tile_load_offset<D, false>(w, lane);
-  // The two groups run the same tile loop, instantiated once per group so
-  // that the dV group holds no V fragments; both pass the same barriers.
+  // The two groups run the same tile loop, instantiated once per group, and
+  // pass the same barriers.
   auto run = [&](auto group) {
     constexpr int kDk = decltype(group)::value;
     // this group's share of the copies of query block pe: Q (dV group) or
@@ -517,71 +480,125 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
       else
         issue_tile_load<D>(Q + r0, qs, off, w, rows(pe), cols(pe));
     };
-    bf16x8 vf[kKS];
-    if constexpr (kDk) {
+    // K (dV group) or V (dK group) rows of this lane's key
+    bf16x8 xf[kKS];
+    {
+      const uint16_t* src = static_cast<const uint16_t*>(kDk ? a.vp : a.kp) + krow * D + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
-        vf[ks] = __builtin_bit_cast(bf16x8,
-                                    *reinterpret_cast<const uint4*>(Vg + krow * D + 16 * ks + 8 * h));
+        xf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + 16 * ks));
     }
+    f32x16 dpm;   // dK group: dP - D of the tile before
     if (cnt == 0) return;
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
-    uint32_t ib_cur = entry(0);
+    uint32_t ib_cur = entry(0), ib_n1 = entry(1);
     copy_vecs(ib_cur, vec_slot[0]);
-    copy_tile(ib_cur, q_slot0, d_slot0);
+    copy_tile(ib_cur, q_slot[0], d_slot[0]);
+    if (!kDk && cnt > 1) copy_tile(ib_n1, q_slot[1], nullptr);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // tile e in slot e % 2; the copies of e+1 go to the other slot
-    auto body = [&](int e, auto parity) {
-      constexpr int kOdd = decltype(parity)::value;
-      u32x4* const qc = kOdd ? q_slot1 : q_slot0;
-      u32x4* const dc = kOdd ? d_slot1 : d_slot0;
-      u32x4* const qn = kOdd ? q_slot0 : q_slot1;
-      u32x4* const dn = kOdd ? d_slot0 : d_slot1;
-      if (((e + 1) & 63) == 0 && e + 1 < cnt) {   // entry e + 1 opens the next batch
-        batch_cur = batch_nxt;
-        batch_nxt = load_batch(((e + 1) >> 6) + 1);
-      }
-      const uint32_t ib_next = entry(e + 1);
-      if (e + 1 < cnt) {
-        copy_vecs(ib_next, vec_slot[kOdd ^ 1]);
-        copy_tile(ib_next, qn, dn);
-      }
-      const f32x16 sv = rows_times(qc, kf);
+    // dS = P (dP - D) of the tile before (P from the dV wave of the same
+    // elements) in bf16, and dK^T += Q^T dS with that tile's Q
+    auto dk_step = [&](const f32x4 (&pt)[4][64], const u32x4* qprev) {
       bf16x8 wb[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 pr = pt[g][lane];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * g + x;
+          wb[r >> 3][r & 7] = static_cast<__bf16>(pr[x] * dpm[r]);
+        }
+      }
+      accumulate(qprev, wb);
+    };
+    // tile e: Q in slot e % 4, dO, P, lse and D in slot e % 2; the copies of
+    // Q of e + 2 and of the rest of e + 1 go to the slots after
+    auto body = [&](int e, auto pslot) {
+      constexpr int PS = decltype(pslot)::value;
+      constexpr int PN = PS ^ 1;
+      const int QS = e & 3, QB = (e - 1) & 3, Q2 = (e + 2) & 3;
+      if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
+        batch_cur = batch_nxt;
+        batch_nxt = load_batch(((e + 2) >> 6) + 1);
+      }
+      const uint32_t ib_next = ib_n1;
+      const uint32_t ib_n2 = entry(e + 2);
+      if (e + 1 < cnt) {
+        copy_vecs(ib_next, vec_slot[PN]);
+        if constexpr (kDk) copy_tile(ib_next, nullptr, d_slot[PN]);
+      }
+      if constexpr (!kDk) {
+        if (e + 2 < cnt) copy_tile(ib_n2, q_slot[Q2], nullptr);
+      }
+      ib_n1 = ib_n2;
       if constexpr (kDk) {
-        const f32x16 dp = rows_times(dc, vf);
-        weights(ib_cur, sv, dp, vec_slot[kOdd], wb);
-        accumulate(qc, wb);
+        const f32x16 dp = rows_times(d_slot[PS], xf);
+        if (e > 0) dk_step(p_slot[PN][w], q_slot[QB]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 dv4 = vec_slot[PS][1][(row0 >> 2) + 2 * g + h];   // rows row0 + 8 g + 4 h ..
+#pragma unroll
+          for (int x = 0; x < 4; ++x) dpm[4 * g + x] = dp[4 * g + x] - dv4[x];
+        }
       } else {
-        probs(ib_cur, sv, vec_slot[kOdd], wb);
-        accumulate(dc, wb);
+        f32x16 s = rows_times(q_slot[QS], xf);
+        // pad query rows (partial patches only: a uniform branch) get S =
+        // -inf, hence P = dS = 0
+        const BlockExtent ext = packed_extent(ib_cur);
+        if (!ext.full()) {
+          const uint32_t bits = real_accumulator_bits(ext, wq, h);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
+        }
+        bf16x8 wb[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lv = vec_slot[PS][0][(row0 >> 2) + 2 * g + h];    // rows row0 + 8 g + 4 h ..
+          f32x4 pr;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            pr[x] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + x], c, -lv[x]));
+            wb[(4 * g + x) >> 3][(4 * g + x) & 7] = static_cast<__bf16>(pr[x]);
+          }
+          p_slot[PS][w][g][lane] = pr;
+        }
+        accumulate(d_slot[PS], wb);
       }
       ib_cur = ib_next;
-      // Every copy has landed, so Q, dO, lse and D of e+1 are in LDS for
-      // every wave after the barrier. The scheduling barrier keeps the wait
-      // after this tile's work; the empty asm statements keep the compiler
-      // from moving LDS accesses across the barrier.
+      // Every copy and P store has landed, so Q, dO, lse and D of e + 1 and
+      // P of e are in LDS for every wave after the barrier. The scheduling
+      // barrier keeps the wait after this tile's work; the empty asm
+      // statements keep the compiler from moving LDS accesses across the
+      // barrier.
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0);
+      if (!kDk && e + 2 < cnt)
+        __builtin_amdgcn_s_waitcnt(kWaitAllButOneTile<D>());   // Q of e + 2 may stay in flight
+      else
+        __builtin_amdgcn_s_waitcnt(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    for (int e = 0; e < cnt; e += 2) {
+    // unrolled by two (the slots other than Q's)
+    for (int e = 0;;) {
       body(e, std::integral_constant<int, 0>{});
-      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
+      if (++e >= cnt) break;
+      body(e, std::integral_constant<int, 1>{});
+      if (++e >= cnt) break;
     }
+    // the dS products of the last tile (its P is visible after the last barrier)
+    if constexpr (kDk) dk_step(p_slot[(cnt - 1) & 1][w], q_slot[(cnt - 1) & 3]);
   };
   if (grp == 0)
     run(std::integral_constant<int, 0>{});
   else
     run(std::integral_constant<int, 1>{});
+  __syncthreads();   // the last dS products have read their Q slot
 
   // ---- add the two query halves of each group, store (pad keys: 0) --------
-  float* const part = reinterpret_cast<float*>(grp == 0 ? (wk ? q_slot1 : q_slot0)
-                                                        : (wk ? d_slot1 : d_slot0));
+  float* const part = reinterpret_cast<float*>(grp == 0 ? q_slot[wk] : d_slot[wk]);
   static_assert(S::kTile * 16 >= kDT * 16 * 64 * 4, "merge area");
   if (wq == 1) {
 #pragma unroll
