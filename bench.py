@@ -155,14 +155,14 @@ def profiled_traffic(workload: str):
         return None
 
 
-def roofline(attn_tflops: float, attn_ms: float, traffic):
+def roofline(attn_tflops: float, attn_ms: float, traffic, kernel: str):
     """The attention kernel against the bf16 matrix-core roofline (its algorithmic bound: a dense
     64x64xd contraction per kept tile), with the measured bytes it moves beyond L2 per launch
     (rocprofv3 counters, scaled by the bytes the permute kernel of the same profiled run is known
     to move) and the rate they imply, with the roof the kernel comes closest to."""
     r = {
         "bound": "mfma",
-        "kernel": "bsa_fwd_mfma (cabf_bsa_forward)",
+        "kernel": kernel,
         "achieved": attn_tflops,
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -643,13 +643,20 @@ def main():
             "thr": main_run["thr"], "sta_window": list(sta) if sta else None,
             "block_logit_row_std": logit_std,
             "parallelism": "single GPU",
-            "attention_order": "list order (deterministic)" if args.deterministic
-                               else "clock-phased start (default)",
+            "attention_order": ("list order, paired kernel in device-sized launches (rows of "
+                                ">= 2048 blocks, either flag)" if nb >= 2048 else
+                                "list order in device-sized launches (deterministic)"
+                                if args.deterministic else "clock-phased start (default)"),
             "reorder": "separate reorder and block pooling" if args.unfused
                        else "reorder fused with block pooling (cabf_permute_pool, "
                             "cabf_build_block_mask_pooled)",
         },
-        "roofline": roofline(attn_tflops, attn_ms, profiled_traffic(w.name)),
+        # the committed counter profile is of the default order
+        "roofline": roofline(attn_tflops, attn_ms,
+                             None if args.deterministic else profiled_traffic(w.name),
+                             "bsa_fwd_pair (cabf_bsa_forward, rows of >= 2048 blocks; one pass = "
+                             "device-sized launches, timed together)" if nb >= 2048 else
+                             "bsa_fwd_mfma (cabf_bsa_forward)"),
         "stages_ms": main_run["stage_ms_mean"],
         "stages_ms_median": main_run["stage_ms_median"],
         "stages_ms_min": main_run["stage_ms_min"],
