@@ -17,6 +17,7 @@ import argparse
 import json
 import math
 import os
+import re
 import platform
 import statistics
 import sys
@@ -125,13 +126,20 @@ def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0, select="cdf", topk=
     return stage
 
 
-def kernel_source_digest() -> str:
-    """sha256 of the attention kernel's sources (ties a counter profile to a kernel version)."""
+def kernel_source_digest(read=None) -> str:
+    """sha256 of the attention kernel's sources with comments and blank lines removed (ties a
+    counter profile to a kernel version; comment edits do not change it). read(name) -> text
+    reads another version of the sources."""
     import hashlib
+    if read is None:
+        def read(name):
+            with open(os.path.join(ROOT, "content_adaptive_block_fractal_amd", "csrc", name)) as fh:
+                return fh.read()
     h = hashlib.sha256()
     for f in ("attention_mfma.hip", "attention_common.hpp", "attention_tiles.hpp", "geometry.hpp"):
-        with open(os.path.join(ROOT, "content_adaptive_block_fractal_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        text = re.sub(r"/\*.*?\*/", "", read(f), flags=re.S)
+        code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in code if ln.strip()).encode())
     return h.hexdigest()
 
 
@@ -147,7 +155,8 @@ def profiled_traffic(workload: str):
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].strip().split(": ", 1)
                 fields[k.strip("`")] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    m = re.search(r"[0-9a-f]{64}", fields.get("kernel_code_sha256", ""))
+    if m is None or m.group(0) != kernel_source_digest():
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])

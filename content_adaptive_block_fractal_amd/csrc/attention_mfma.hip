@@ -13,7 +13,8 @@
 //   ascending list where a clock-driven sweep of the key range stands, so
 //   that the workgroups of a head sweep the key range together and read the
 //   same K/V tiles at about the same time (in deterministic mode the list is
-//   walked from its first entry).
+//   walked from its first entry, in launches of as many workgroups as the
+//   device holds, which start together and walk the key range in step).
 //
 // Per kept tile, per wave, with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T    A = K (LDS, row-major, 16-byte chunks XOR-swizzled by row)

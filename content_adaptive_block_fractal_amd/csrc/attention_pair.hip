@@ -2,12 +2,16 @@
 // of their kept lists (NABLA summary, Methodology item 2, expansion bullet:
 // attention runs on the kept (query block, key block) tiles only).
 //
-// Why pairs: the kernel is limited by the K/V tile traffic from beyond L2,
-// not by its arithmetic. The same patch in consecutive frames keeps largely
+// Why pairs: on long rows (2048 blocks or more; 241 frames at 768p has
+// 4026) a head's key range no longer fits L2 and the tile fetches from
+// beyond it set the pace. The same patch in consecutive frames keeps largely
 // the same key blocks, so a workgroup serving both blocks streams each K/V
 // tile of the union of their lists into LDS once where two workgroups would
 // fetch it twice (1.38 kept tiles per union tile at 720p / 80% on the seeded
-// smooth-field workload).
+// smooth-field workload). Lists are walked in order, in launches of as many
+// workgroups as the device holds (each launch's workgroups start together
+// and walk the key range in step). On shorter rows the one-block kernel is
+// faster: a tile kept by one block only leaves the other group idle.
 //
 // Work decomposition
 //   One workgroup of 8 waves per pair (A, B): waves 0-3 serve block A and
