@@ -77,11 +77,12 @@ __global__ __launch_bounds__(256) void bwd_rowdot(const uint16_t* __restrict__ o
   }
 }
 
-// Element offsets (within a 64-row K-swizzled tile) of the transposing reads
-// that give a lane its fragments of X^T (d x rows) for rows
-// rbase + 4 (vgrp / 2) + vsl / 4 + 16 st + 8 half and columns 32 dt + vcol:
-// off[dt][half] for st = 0; the K swizzle repeats every 16 rows, so st = 1
-// is 16 D elements further (kept out of the array, one register each less).
+// Element offsets (within a 64-row tile in the two-way layout, b_chunk_slot)
+// of the transposing reads that give a lane its fragments of X^T (d x rows)
+// for rows rbase + 4 (vgrp / 2) + vsl / 4 + 16 st + 8 half and columns
+// 32 dt + vcol: off[dt][half] for st = 0; the swizzle repeats every 16 rows,
+// so st = 1 is 16 D elements further (kept out of the array, one register
+// each less).
 template <int D>
 __device__ inline void transposed_offsets(int (&off)[D / 32][2], int rbase, int lane) {
   const int vgrp = lane >> 4, vsl = lane & 15;
@@ -93,7 +94,7 @@ __device__ inline void transposed_offsets(int (&off)[D / 32][2], int rbase, int 
     for (int hf = 0; hf < 2; ++hf) {
       const int row = vrow + 8 * hf;
       const int col = 32 * dt + vcol;
-      off[dt][hf] = k_chunk_slot<D>(row, col >> 3) * 8 + (col & 7);
+      off[dt][hf] = b_chunk_slot<D>(row, col >> 3) * 8 + (col & 7);
     }
 }
 
@@ -105,7 +106,8 @@ __device__ inline bf16x8 transposed_fragment(const uint16_t* tile, int off_lo, i
 }
 
 // Loads the D-wide rows of one 64-row tile of `a` and `b` (K/V, or Q/dO) into
-// a K-swizzled LDS slot each.
+// an LDS slot each, in the two-way layout (read by rows and transposed
+// without bank conflicts).
 template <int D>
 __device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, u32x4* sa, u32x4* sb,
                                           uint32_t off, int wave, int real_rows = kBlock,
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     for (int i = 0; i < 16; ++i) r[i] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const u32x4 u = tile[k_chunk_slot<D>(key0 + li, 2 * ks + h)];
+      const u32x4 u = tile[b_chunk_slot<D>(key0 + li, 2 * ks + h)];
       r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), f[ks], r, 0, 0, 0);
     }
     return r;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   };
 
   if (cnt > 0) {
-    const uint32_t off = tile_load_offset<D, false>(wave, lane);
+    const uint32_t off = tile_load_offset<D, Swz::B>(wave, lane);
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
     uint32_t jb_cur = tile_of(0);
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
     for (int i = 0; i < 16; ++i) r[i] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const u32x4 u = tile[k_chunk_slot<D>(row0 + li, 2 * ks + h)];
+      const u32x4 u = tile[b_chunk_slot<D>(row0 + li, 2 * ks + h)];
       r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), f[ks], r, 0, 0, 0);
     }
     return r;
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
       __builtin_amdgcn_global_load_lds(dl_h + r0 + lane, reinterpret_cast<float*>(vec[1]), 4, 0, 0);
     }
   };
-  const uint32_t off = tile_load_offset<D, false>(w, lane);
+  const uint32_t off = tile_load_offset<D, Swz::B>(w, lane);
   // The two groups run the same tile loop, instantiated once per group, and
   // pass the same barriers.
   auto run = [&](auto group) {

@@ -335,8 +335,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     };
 
     // ---- prologue: K of tiles 0-2 and V of tile 0 in LDS, S^T of tile 0 ----
-    const uint32_t koff = tile_load_offset<D, false>(wave, lane);
-    const uint32_t voff = tile_load_offset<D, true>(wave, lane);
+    const uint32_t koff = tile_load_offset<D, Swz::K>(wave, lane);
+    const uint32_t voff = tile_load_offset<D, Swz::V>(wave, lane);
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
     const TileRef t0 = tile(0);

@@ -264,8 +264,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void bsa_fwd_pair(AttnArgs a, int 
   };
 
   if (cnt > 0) {
-    const uint32_t koff = tile_load_offset<D, false, kPairThreads>(wave, lane);
-    const uint32_t voff = tile_load_offset<D, true, kPairThreads>(wave, lane);
+    const uint32_t koff = tile_load_offset<D, Swz::K, kPairThreads>(wave, lane);
+    const uint32_t voff = tile_load_offset<D, Swz::V, kPairThreads>(wave, lane);
     batch_cur = load_batch(0);
     batch_nxt = load_batch(1);
     uint32_t e_cur = entry(0);

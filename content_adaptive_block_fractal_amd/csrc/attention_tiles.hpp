@@ -52,6 +52,26 @@ __device__ inline int v_chunk_slot(int key, int chunk) {
   return key * kChunks + (chunk ^ swz);
 }
 
+// A tile read both ways (the backward's Q, dO and K tiles): by rows, 16
+// bytes per lane and 16 consecutive rows per 16-lane group, as K; and
+// transposed, 4 consecutive rows x 64 bytes per 32-lane half, as V. The
+// chunk index is XOR-ed with f(row), a permutation over 16 consecutive rows
+// (D = 64: over the 8 rows of a bank half) whose bits 2-3 differ between
+// the 4 rows of a transposing read (D = 64: between its two rows in a bank
+// half), so both kinds of read hit 64 distinct banks. K's rotation by row
+// leaves a transposing read four chunks in four banks' worth of space (a
+// 4-way conflict); V's leaves row reads 4-way conflicted.
+template <int D>
+__device__ inline int b_chunk_slot(int row, int chunk) {
+  constexpr int kChunks = D / 8;
+  const int swz = (D == 128) ? 4 * (row & 3) + ((row >> 2) & 3)
+                             : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  return row * kChunks + (chunk ^ swz);
+}
+
+// Which swizzle a tile copy lays out.
+enum class Swz { K, V, B };
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // max of v over lanes l and l ^ 32 (v_permlane32_swap exchanges the upper
@@ -123,16 +143,17 @@ struct Stage {
 // swizzle's period in the row, so a lane's source offset in pass i is its
 // offset in pass 0 plus a constant (added to the scalar base). The offsets are
 // the same for every tile.
-template <int D, bool IS_V, int NT = kThreads>
+template <int D, Swz L, int NT = kThreads>
 __device__ inline uint32_t tile_load_offset(int wave, int lane) {
   using S = Stage<D, NT>;
   static_assert(S::kRowsPerIter % 16 == 0, "swizzle period");
   const int phys = wave * 64 + lane;
   const int row = phys / S::kChunks;
   const int pc = phys % S::kChunks;
-  // the swizzle is an XOR with a function of the row: its own inverse
-  const int chunk = IS_V ? (v_chunk_slot<D>(row, pc) - row * S::kChunks)
-                         : (k_chunk_slot<D>(row, pc) - row * S::kChunks);
+  // every swizzle is an XOR with a function of the row: its own inverse
+  const int slot = L == Swz::V ? v_chunk_slot<D>(row, pc)
+                               : (L == Swz::B ? b_chunk_slot<D>(row, pc) : k_chunk_slot<D>(row, pc));
+  const int chunk = slot - row * S::kChunks;
   return static_cast<uint32_t>((row * D + chunk * 8) * 2);
 }
 
