@@ -6,18 +6,21 @@ rounded to bf16, fp32 accumulation), so their errors scale with the
 gradient's own magnitude: max |err| <= 2e-2 * max |ref| and mean |err| <=
 1e-2 * mean |ref| over the compared rows, per tensor.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
 
 import content_adaptive_block_fractal_amd as cabf
 import oracle
-from synth import WORKLOADS, fourier_video_qkv
+from synth import WORKLOADS, fourier_video_qkv, gaussian_video_qkv
 from tests.parity import say, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 REL_MAX, REL_MEAN = 2e-2, 1e-2
+SHARP_SCALE = 3.5        # kernel scale of the sharp cases, times 1/sqrt(d)
 
 
 def compare_grad(got, ref, rows, label):
@@ -74,6 +77,56 @@ def test_backward_matches_oracle(name, shape, thr, sta):
         for nm, got, r in (("dq", pq, ref[0]), ("dk", pk, ref[1]), ("dv", pv, ref[2])):
             compare_grad(got[0, hd], r, valid, f"{name} head {hd} {nm} (clock-phased)")
             assert torch.all(got[0, hd][torch.from_numpy(~valid).to(DEV)] == 0)
+
+
+@pytest.mark.parametrize("name,shape,thr", [("ragged-d128", (3, 21, 35, 2, 128), 0.4),
+                                            ("ragged-d64", (5, 9, 17, 2, 64), 0.5)])
+def test_backward_sharp_inputs(name, shape, thr):
+    """Token-independent Q, K, V at scale 3.5/sqrt(d), where each query's
+    weights sit on a few keys, on ragged grids with partial patches: two
+    plausible mistakes, planted in the oracle's inputs on the CPU (uniform
+    weights; dO rows of neighbouring queries exchanged, as a wrong row order in
+    the transposed dO or in dP would do), move every gradient by more than ten
+    times the tolerance, and the GPU's gradients, in both visit orders, stay
+    within it."""
+    T, H, W, heads, d = shape
+    say(f"sharp backward {name} thr={thr}")
+    g = cabf.Geom(1, heads, d, T, H, W, 8)
+    og = oracle.Grid(T, H, W, 8)
+    s = SHARP_SCALE / math.sqrt(d)
+    q, k, v = gaussian_video_qkv(T, H, W, heads, d, seed=11, device=DEV)
+    qp, kp, vp = cabf.permute(q, k, v, g)
+    cnt, idx = cabf.build_block_mask(qp, kp, g, thr, None, s)
+    op, lse = cabf.bsa_forward(qp, kp, vp, cnt, idx, g, s, return_lse=True, deterministic=True)
+    gen = torch.Generator(device=DEV).manual_seed(12)
+    dop = torch.randn(qp.shape, generator=gen, device=DEV).to(torch.bfloat16)
+    dq, dk, dv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s, deterministic=True)
+    pq, pk, pv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)     # clock-phased
+    torch.cuda.synchronize()
+    valid = oracle.valid_slots(og)
+    for hd in range(heads):
+        qn, kn, vn, don = (to_np(t[0, hd]) for t in (qp, kp, vp, dop))
+        cnt_h, idx_h = cnt[0, hd].cpu().numpy(), idx[0, hd].cpu().numpy()
+        ref = oracle.bsa_backward(qn, kn, vn, don, cnt_h, idx_h, og, s)
+        if hd == 0:
+            swapped = don.reshape(-1, 2, d)[:, ::-1].reshape(don.shape)
+            mistakes = {"uniform weights": oracle.bsa_backward(qn, kn, vn, don, cnt_h, idx_h, og, 0.0),
+                        "dO rows exchanged": oracle.bsa_backward(qn, kn, vn, swapped, cnt_h, idx_h, og, s)}
+            for label, wrong in mistakes.items():
+                for nm, a, b in zip(("dq", "dk", "dv"), wrong, ref):
+                    if label == "uniform weights" and nm != "dv":
+                        continue      # scale 0 zeroes dq and dk outright
+                    err = np.abs(np.asarray(a)[valid] - np.asarray(b)[valid])
+                    ref_v = np.abs(np.asarray(b)[valid])
+                    say(f"planted mistake ({label}) {nm}: max_err {err.max():.3e} "
+                        f"(tolerance {REL_MAX * ref_v.max():.3e}), mean_err {err.mean():.3e} "
+                        f"(tolerance {REL_MEAN * ref_v.mean():.3e})")
+                    assert (err.max() > 10 * REL_MAX * ref_v.max()
+                            or err.mean() > 10 * REL_MEAN * ref_v.mean()), (label, nm)
+        for nm, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+            compare_grad(got[0, hd], r, valid, f"sharp {name} head {hd} {nm}")
+        for nm, got, r in (("dq", pq, ref[0]), ("dk", pk, ref[1]), ("dv", pv, ref[2])):
+            compare_grad(got[0, hd], r, valid, f"sharp {name} head {hd} {nm} (clock-phased)")
 
 
 def test_backward_rows_without_blocks_and_unused_keys():
