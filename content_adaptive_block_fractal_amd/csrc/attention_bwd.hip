@@ -15,6 +15,10 @@
 //                  dQ^T += K^T dS^T with K^T from transposing LDS reads
 //   bwd_transpose  the kept lists turned around: for every key block, the
 //                  query blocks that keep it, ascending (through a bitmap)
+//   bwd_order      the key blocks of each head by the length of those lists,
+//                  longest first (counting sort): the dK/dV pass runs them in
+//                  that order, so workgroups side by side walk lists of about
+//                  the same length
 //   bwd_dkv        one workgroup of two four-wave groups per key block over
 //                  those query blocks, both groups on the same Q and dO
 //                  tiles: the dV group forms S = Q K^T and P, adds dV^T +=
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave & 1, wk = wave >> 1;
   const int li = lane & 31, h = lane >> 5;
-  const int64_t item = xcd_order(blockIdx.x, n_items);
+  const int64_t item = a.item0 + xcd_order(blockIdx.x, n_items);
   const int64_t bh = item / a.nb;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.kp) + bh * a.N * D;
@@ -347,6 +351,60 @@ __global__ __launch_bounds__(256) void bwd_transpose(const uint32_t* __restrict_
   if (lane == 0) q_count[row] = count;
 }
 
+// Key blocks of each (batch, head) ordered by the length of their transposed
+// lists, longest first, equal lengths by index: k_order[bh * nb + r] is the
+// r-th. A stable counting sort in one workgroup per (batch, head), nb <=
+// kMaxBlocks (the histogram lives in LDS).
+__global__ __launch_bounds__(256) void bwd_order(const int32_t* __restrict__ q_count,
+                                                 int32_t* __restrict__ k_order, int nb) {
+  __shared__ int hist[kMaxBlocks + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * nb;
+  auto key_of = [&](int j) { return nb - min(max(q_count[base + j], 0), nb); };   // 0: longest
+  for (int i = tid; i <= nb; i += 256) hist[i] = 0;
+  __syncthreads();
+  for (int j = tid; j < nb; j += 256) atomicAdd(&hist[key_of(j)], 1);
+  __syncthreads();
+  if (tid < 64) {
+    // exclusive scan of hist[0 .. nb]: each lane sums a run of bins, the
+    // wave scans the run totals, each lane then writes its run's offsets
+    const int per = (nb + 1 + 63) / 64;
+    const int lo = min(lane * per, nb + 1), hi = min(lo + per, nb + 1);
+    int run = 0;
+    for (int i = lo; i < hi; ++i) run += hist[i];
+    int incl = run;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int o = __shfl_up(incl, sh);
+      incl += lane >= sh ? o : 0;
+    }
+    int off = incl - run;
+    for (int i = lo; i < hi; ++i) {
+      const int c = hist[i];
+      hist[i] = off;
+      off += c;
+    }
+    // stable scatter, 64 key blocks at a time in index order: a lane's place
+    // is its key's next free slot plus the lanes before it with the same key
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+      const int j = j0 + lane;
+      const bool on = j < nb;
+      const int key = on ? key_of(j) : -1;
+      uint64_t same = __ballot(on);
+      for (int bit = 0; (1 << bit) <= nb; ++bit) {
+        const uint64_t b = __ballot(on && ((key >> bit) & 1));
+        same &= ((key >> bit) & 1) ? b : ~b;
+      }
+      const int rank = __popcll(same & lt);
+      const int pos = on ? hist[key] + rank : 0;
+      if (on) k_order[base + pos] = j;
+      if (on && rank == __popcll(same) - 1) hist[key] = pos + 1;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK and dV in one pass: one workgroup of eight waves per key block over the
 // query blocks that keep it. Waves 0-3 form the dV group, waves 4-7 the dK
@@ -373,6 +431,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
                                                            const float* __restrict__ lse2,
                                                            const int32_t* __restrict__ q_count,
                                                            const int32_t* __restrict__ q_index,
+                                                           const int32_t* __restrict__ k_order,
                                                            uint16_t* __restrict__ dkp,
                                                            uint16_t* __restrict__ dvp, int64_t n_items) {
   using S = Stage<D>;
@@ -391,8 +450,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   const int w = wave & 3;                                   // wave within the group
   const int wk = w & 1, wq = w >> 1;
   const int li = lane & 31, h = lane >> 5;
-  const int64_t item = xcd_order(blockIdx.x, n_items);     // bh * nb + key block j
-  const int64_t bh = item / a.nb;
+  // bh * nb + key block j; with k_order, slot r of a head runs its r-th
+  // longest transposed list
+  const int64_t slot = a.item0 + xcd_order(blockIdx.x, n_items);
+  const int64_t bh = slot / a.nb;
+  const int64_t item =
+      k_order != nullptr ? bh * a.nb + min(max(k_order[slot], 0), a.nb - 1) : slot;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp) + bh * a.N * D;
   const uint16_t* __restrict__ dO = dop + bh * a.N * D;
   const float* __restrict__ lse_h = lse2 + bh * a.N;
@@ -650,6 +713,7 @@ BwdWorkspace bwd_workspace_layout(const Geo& g) {
   w.bitmap = o;   o += align256(static_cast<size_t>(g.BH) * g.nb * w.words * sizeof(uint32_t));
   w.q_count = o;  o += align256(static_cast<size_t>(g.BH) * g.nb * sizeof(int32_t));
   w.q_index = o;  o += align256(static_cast<size_t>(g.BH) * g.nb * g.nb * sizeof(int32_t));
+  w.k_order = o;  o += align256(static_cast<size_t>(g.BH) * g.nb * sizeof(int32_t));
   w.total = o;
   return w;
 }
@@ -681,6 +745,15 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
                      bitmap, g.nb, w.words, entries);
   hipLaunchKernelGGL(bwd_transpose, grid_for(g.BH * g.nb, 4), dim3(256), 0, stream, bitmap, q_count,
                      q_index, g.nb, w.words, g.BH * g.nb);
+  // Key blocks by transposed-list length, longest first: the dK/dV pass
+  // then runs lists of about the same length side by side (a key block is
+  // kept by 57 to 427 query blocks at 720p / 80%), so concurrent workgroups
+  // walk the query range at about the same rate, and the longest start first.
+  int32_t* k_order = reinterpret_cast<int32_t*>(ws + w.k_order);
+  const bool sorted = g.nb <= kMaxBlocks;
+  if (sorted)
+    hipLaunchKernelGGL(bwd_order, dim3(static_cast<unsigned>(g.BH)), dim3(256), 0, stream, q_count,
+                       k_order, g.nb);
 
   AttnArgs a{};
   a.qp = qp;
@@ -698,28 +771,44 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   a.N = g.N;
   a.BH = g.BH;
   const int64_t items = g.BH * g.nb;
-  const unsigned grid = static_cast<unsigned>(items);
   uint16_t* dq16 = static_cast<uint16_t*>(dqp);
   uint16_t* dk16 = static_cast<uint16_t*>(dkp);
   uint16_t* dv16 = static_cast<uint16_t*>(dvp);
-  // clock-phased periods: ticks of the 100 MHz clock per tile of each pass
-  // (d = 128 at 720p; d = 64 tiles take about half as long)
+  // Clock-phased (default): both passes as one launch each, every list
+  // started where a sweep of the 100 MHz clock stands (ticks per tile of each
+  // pass at d = 128, 720p; d = 64 tiles take about half as long). In list
+  // order (bit-reproducible): the dQ pass in launches of a device-full of
+  // workgroups, which start together and walk the key range in step (as the
+  // forward; uniform list lengths), the dK/dV pass in one launch in the
+  // length-sorted order. 720p / 80%, one box: 100.2 ms clock-phased (103.3
+  // unsorted), list order ~101 ms (106.9 with both passes as one unsorted
+  // launch; generations of the dK/dV pass were slower, 111.7 ms).
   const uint32_t t_dq = phased ? (g.D == 64 ? 95u : 185u) : 0u;
   const uint32_t t_dkv = phased ? (g.D == 64 ? 110u : 220u) : 0u;
   AttnArgs a_dq = a, a_dkv = a;
   a_dq.sweep_ticks = t_dq;
   a_dkv.sweep_ticks = t_dkv;
-  if (g.D == 64) {
-    hipLaunchKernelGGL((bwd_dq<64>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta,
-                       lse2, dq16, items);
-    hipLaunchKernelGGL((bwd_dkv<64>), dim3(grid), dim3(2 * kThreads), 0, stream, a_dkv, do16,
-                       delta, lse2, q_count, q_index, dk16, dv16, items);
-  } else {
-    hipLaunchKernelGGL((bwd_dq<128>), dim3(grid), dim3(kThreads), 0, stream, a_dq, do16, delta,
-                       lse2, dq16, items);
-    hipLaunchKernelGGL((bwd_dkv<128>), dim3(grid), dim3(2 * kThreads), 0, stream, a_dkv, do16,
-                       delta, lse2, q_count, q_index, dk16, dv16, items);
-  }
+  const void* kdq = g.D == 64 ? reinterpret_cast<const void*>(&bwd_dq<64>)
+                              : reinterpret_cast<const void*>(&bwd_dq<128>);
+  const int64_t per_dq = phased ? items : kGenerationsPerLaunch * resident_workgroups(kdq, kThreads, stream);
+  launch_in_generations(items, per_dq, [&](int64_t first, int64_t count) {
+    a_dq.item0 = first;
+    const unsigned gr = static_cast<unsigned>(count);
+    if (g.D == 64)
+      hipLaunchKernelGGL((bwd_dq<64>), dim3(gr), dim3(kThreads), 0, stream, a_dq, do16, delta, lse2,
+                         dq16, count);
+    else
+      hipLaunchKernelGGL((bwd_dq<128>), dim3(gr), dim3(kThreads), 0, stream, a_dq, do16, delta, lse2,
+                         dq16, count);
+  });
+  const int32_t* order = sorted ? k_order : nullptr;
+  const unsigned grid = static_cast<unsigned>(items);
+  if (g.D == 64)
+    hipLaunchKernelGGL((bwd_dkv<64>), dim3(grid), dim3(2 * kThreads), 0, stream, a_dkv, do16, delta,
+                       lse2, q_count, q_index, order, dk16, dv16, items);
+  else
+    hipLaunchKernelGGL((bwd_dkv<128>), dim3(grid), dim3(2 * kThreads), 0, stream, a_dkv, do16, delta,
+                       lse2, q_count, q_index, order, dk16, dv16, items);
 }
 
 }  // namespace cabf

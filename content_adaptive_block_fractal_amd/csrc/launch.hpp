@@ -49,10 +49,11 @@ void launch_build_sta_mask(const Geo& g, int dt, int dy, int dx, int32_t* kv_cou
                            int32_t* kv_index, hipStream_t stream);
 
 // Backward workspace: D = rowsum(dO * O), the kept-list bitmap and the
-// transposed lists (query blocks of every key block).
+// transposed lists (query blocks of every key block), the key blocks of
+// each head ordered by transposed-list length.
 struct BwdWorkspace {
   int words;
-  size_t delta, lse2, bitmap, q_count, q_index, total;
+  size_t delta, lse2, bitmap, q_count, q_index, k_order, total;
 };
 BwdWorkspace bwd_workspace_layout(const Geo& g);
 void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const void* vp,

@@ -258,8 +258,9 @@ int cabf_bsa_forward_subset(const cabf_geom* g, cabf_dtype dtype,
                             void* op, float* lse, unsigned flags, hipStream_t stream);
 
 /* Bytes of workspace cabf_bsa_backward needs (0 if the geometry is
- * unsupported): fp32 D and base-2 lse per row, a kept-list bitmap and the
- * transposed lists (about B*heads*nb*nb*4 bytes). */
+ * unsupported): fp32 D and base-2 lse per row, a kept-list bitmap, the
+ * transposed lists (about B*heads*nb*nb*4 bytes) and the key blocks of each
+ * head ordered by the length of their transposed lists. */
 size_t cabf_bsa_backward_workspace_bytes(const cabf_geom* g);
 
 /* Gradients of cabf_bsa_forward (NABLA summary, closing remarks: the sparse

@@ -176,9 +176,14 @@ def test_backward_nonfinite_lse_rows_contribute_nothing():
     assert torch.equal(dq_a.float(), dq_b.float())
 
 def test_backward_full_size_sampled():
-    """Wan-14B 720p at 80% sparsity: the gradients of two key blocks (every
-    query block that keeps them is included, so those rows are exact) and the
-    dq of those query blocks, head 0."""
+    """Wan-14B 720p at 80% sparsity, in both visit orders (clock-phased; list
+    order, whose dQ pass runs in several device-sized launches and whose dK/dV
+    pass runs the key blocks longest transposed list first): the gradients of
+    two key blocks (every query block that keeps them is included, so those
+    rows are exact) and the dq of those query blocks, head 0, against the
+    oracle; the list-order gradients repeat bit for bit; and the two orders
+    agree over the whole of dq, dk and dv (the same sums in another order),
+    so no key block or query block is left out by either."""
     w = WORKLOADS["wan14b-720p"]
     g = cabf.Geom(w.batch, w.heads, w.head_dim, w.T, w.H, w.W, w.P)
     og = oracle.Grid(w.T, w.H, w.W, w.P)
@@ -191,7 +196,15 @@ def test_backward_full_size_sampled():
     dop = torch.randn(qp.shape, generator=torch.Generator(device=DEV).manual_seed(9),
                       device=DEV).to(torch.bfloat16)
     dq, dk, dv = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
+    det = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s, deterministic=True)
+    det2 = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s, deterministic=True)
     torch.cuda.synchronize()
+    for nm, a, b, c in zip(("dq", "dk", "dv"), (dq, dk, dv), det, det2):
+        assert torch.equal(b.view(torch.int16), c.view(torch.int16)), nm
+        diff = float((a.float() - b.float()).abs().max())
+        big = float(a.float().abs().max())
+        say(f"full-size {nm}: clock-phased vs list order max diff {diff:.3e} (max {big:.3e})")
+        assert diff <= 1e-2 * big, nm
     hd = 0
     c0, i0 = cnt[0, hd].cpu().numpy(), idx[0, hd].cpu().numpy()
     key_blocks = [0, og.nb - 1]
@@ -205,6 +218,7 @@ def test_backward_full_size_sampled():
     krows = krows[valid[krows]]
     qrows = np.concatenate([np.arange(b * 64, (b + 1) * 64) for b in np.nonzero(keeps)[0][:40]])
     qrows = qrows[valid[qrows]]
-    compare_grad(dk[0, hd], ref[1], krows, "full-size dk")
-    compare_grad(dv[0, hd], ref[2], krows, "full-size dv")
-    compare_grad(dq[0, hd], ref[0], qrows, "full-size dq")
+    for tag, (gq, gk, gv) in (("clock-phased", (dq, dk, dv)), ("list order", det)):
+        compare_grad(gk[0, hd], ref[1], krows, f"full-size dk ({tag})")
+        compare_grad(gv[0, hd], ref[2], krows, f"full-size dv ({tag})")
+        compare_grad(gq[0, hd], ref[0], qrows, f"full-size dq ({tag})")
