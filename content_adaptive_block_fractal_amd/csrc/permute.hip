@@ -7,13 +7,14 @@
 // (one 8x8 patch of one frame): the reordered side is a contiguous 64-row run
 // and the raster side is 8 runs of 8 consecutive tokens, so every wave reads
 // and writes whole rows. Block coordinates are decoded once per workgroup in
-// scalar registers.
+// scalar registers. Loads and stores are non-temporal (nothing is reused).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "geometry.hpp"
 #include "launch.hpp"
+#include "streaming.hpp"
 
 namespace cabf {
 namespace {
@@ -72,12 +73,12 @@ __global__ __launch_bounds__(kThreads) void reorder_blocks(CopySet set, int64_t 
         const int c = it * kThreads + static_cast<int>(threadIdx.x);
         const int row = c / CH;
         const int64_t r = raster_of(row);
-        vals[it] = r >= 0 ? src[r * CH + (c - row * CH)] : make_uint4(0u, 0u, 0u, 0u);
+        vals[it] = r >= 0 ? load_stream(src + r * CH + (c - row * CH)) : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
         const int c = it * kThreads + static_cast<int>(threadIdx.x);
-        dst[fractal_base * CH + c] = vals[it];
+        store_stream(dst + fractal_base * CH + c, vals[it]);
       }
     } else {
 #pragma unroll
@@ -85,8 +86,8 @@ __global__ __launch_bounds__(kThreads) void reorder_blocks(CopySet set, int64_t 
         const int c = it * kThreads + static_cast<int>(threadIdx.x);
         const int row = c / CH;
         const int64_t r = raster_of(row);
-        const uint4 val = src[fractal_base * CH + c];
-        if (r >= 0) dst[r * CH + (c - row * CH)] = val;
+        const uint4 val = load_stream(src + fractal_base * CH + c);
+        if (r >= 0) store_stream(dst + r * CH + (c - row * CH), val);
       }
     }
   }
@@ -134,10 +135,10 @@ __global__ __launch_bounds__(kThreads) void reorder_pool_blocks(CopySet set, Poo
       const int x = bp.tx * kP + (row & 7);
       const bool real = y < H && x < W;
       const int64_t r = raster_base + (static_cast<int64_t>(bp.t) * H + y) * W + x;
-      vals[it] = real ? src[r * CH + col] : make_uint4(0u, 0u, 0u, 0u);
+      vals[it] = real ? load_stream(src + r * CH + col) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) dst[fractal_base * CH + it * kThreads + tid] = vals[it];
+    for (int it = 0; it < kIters; ++it) store_stream(dst + fractal_base * CH + it * kThreads + tid, vals[it]);
     if (pdst != nullptr) {
       float acc[kEPC];
 #pragma unroll

@@ -15,6 +15,7 @@
 #include <cstdint>
 
 #include "attention_common.hpp"
+#include "streaming.hpp"
 #include "svg.hpp"
 
 namespace cabf {
@@ -36,9 +37,9 @@ __global__ __launch_bounds__(256) void gather_rows(const uint4* __restrict__ x,
   uint4 v = make_uint4(0, 0, 0, 0);
   if (i < n) {
     const int src = min(max(perm[bh * n + i], 0), n - 1);
-    v = x[(bh * n + src) * chunks_per_row + ch];
+    v = load_stream(x + (bh * n + src) * chunks_per_row + ch);
   }
-  xp[e] = v;
+  store_stream(xp + e, v);
 }
 
 __global__ __launch_bounds__(256) void scatter_rows(const uint4* __restrict__ xp,
@@ -52,7 +53,8 @@ __global__ __launch_bounds__(256) void scatter_rows(const uint4* __restrict__ xp
   const int64_t bh = row / n;
   const int i = static_cast<int>(row - bh * n);
   const int dst = min(max(perm[row], 0), n - 1);
-  x[(bh * n + dst) * chunks_per_row + ch] = xp[(bh * rows_in + i) * chunks_per_row + ch];
+  store_stream(x + (bh * n + dst) * chunks_per_row + ch,
+               load_stream(xp + (bh * rows_in + i) * chunks_per_row + ch));
 }
 
 // one thread per (bh, a, b); padding columns b >= ck are never read
