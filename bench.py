@@ -126,6 +126,11 @@ def run_steps(cabf, geom, bufs, thr, sta, n, timed, flags=0, select="cdf", topk=
     return stage
 
 
+def progress(msg: str):
+    """One line on stderr per finished stage (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def kernel_source_digest(read=None) -> str:
     """sha256 of the attention kernel's sources with comments and blank lines removed (ties a
     counter profile to a kernel version; comment edits do not change it). read(name) -> text
@@ -273,7 +278,7 @@ def hbm_fractions(geom, sizes, stages, kept, elem_bytes, fused):
         work = {"permute": 3 * (raster + padded) + pooled, "mask": pooled + lists}
     else:
         work = {"permute": 3 * (raster + padded), "mask": 2 * padded + 2 * pooled + lists}
-    work["unpermute"] = raster + padded
+    work["unpermute"] = 2 * raster      # real rows read from the reordered tensor, written back
     out = {}
     for k, b in work.items():
         gbs = b / (stages[k] * 1e-3) / 1e9
@@ -622,6 +627,7 @@ def main():
     flags = cabf.BSA_DETERMINISTIC if args.deterministic else 0
     main_run = measure(args.sparsity, sta, args.steps, args.warmup, flags, fused=not args.unfused)
     ms = main_run["wall_ms"]
+    progress(f"main step {ms:.2f} ms (thr {main_run['thr']:.6f})")
     # spread of the block logits (scaled, base e): mean over rows of the row std of log p
     _, _, probs = cabf.build_block_mask(qp, kp, geom, main_run["thr"], sta, return_probs=True)
     logit_std = float(torch.log(probs.clamp_min(1e-30)).std(dim=-1).mean().item())
@@ -677,6 +683,7 @@ def main():
     }
     peaks = measured_peaks(cabf, dev)
     line["measured_peaks"] = peaks
+    progress("measured peaks")
     line["roofline"]["frac_of_measured_peak"] = attn_tflops / peaks["mfma_bf16_tflops"]
     if args.variants:
         var = {}
@@ -695,6 +702,7 @@ def main():
                 attention_ms=a, mask_ms=r["stage_ms_mean"]["mask"],
                 attention_tflops=r["flops"] / (a * 1e-3) / 1e12,
                 step_tflops=r["flops"] / (r["wall_ms"] * 1e-3) / 1e12)
+            progress(f"variant {name}: attention {a:.2f} ms")
         # the other selection rules at the same shape: a static keep ratio of
         # 20% (top-k per row) and the sliding-tile window alone
         k20 = cabf.topk_for_ratio(geom, 0.20)
@@ -719,11 +727,14 @@ def main():
         line["variants"] = var
         line["active_query_subset"] = measure_subset(cabf, geom, bufs, main_run["thr"], sta,
                                                      flags, max(3, args.steps // 4))
+        progress("selection variants, reorder variant, active-query subset")
     if args.backward:
         line["backward"] = measure_backward(cabf, geom, bufs, main_run["thr"], sta,
                                             max(3, args.steps // 4))
+        progress(f"backward {line['backward']['ms']:.2f} ms")
     if args.semantic:
         line["semantic_variant"] = measure_semantic(cabf, max(3, args.steps // 4), 2, args.seed)
+        progress(f"semantic-permutation layer {line['semantic_variant']['ms_per_layer']:.2f} ms")
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_run["thr"], sta, args.cpu_seconds)
     print(json.dumps(line), flush=True)
