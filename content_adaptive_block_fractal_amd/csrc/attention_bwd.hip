@@ -181,13 +181,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   // use, and read out with readlane (as in the forward): no list load is
   // waited on per tile. Entry t of the pass is list entry start + t
   // (wrapped); t is clamped to the last one.
-  // Entries are packed with their extents (pack_block_entry).
+  // Entries are packed with their extents (pack_block_entry) when their
+  // batch comes into use, not right after the load (which would wait for
+  // it, and with it for every tile copy issued before it).
   auto load_batch = [&](int b) {
     int pos = min(b * 64 + lane, cnt - 1) + start;
     pos -= pos >= cnt ? cnt : 0;
-    return pack_block_entry(a, list[pos]);
+    return list[pos];
   };
-  uint32_t batch_cur = 0, batch_nxt = 0;   // entries 64 B .. and 64 (B + 1) .. of the pass
+  uint32_t batch_cur = 0;    // entries 64 B .. of the pass, packed
+  int32_t batch_nxt = 0;     // entries 64 (B + 1) .., as loaded
   auto tile_of = [&](int t) {
     const int p = t < cnt ? t : cnt - 1;
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(batch_cur, p & 63));
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
 
   if (cnt > 0) {
     const uint32_t off = tile_load_offset<D, Swz::B>(wave, lane);
-    batch_cur = load_batch(0);
+    batch_cur = pack_block_entry(a, load_batch(0));
     batch_nxt = load_batch(1);
     uint32_t jb_cur = tile_of(0);
     load_pair<D>(K + tile_off(jb_cur), V + tile_off(jb_cur), k_slot0, v_slot0, off, wave,
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
       u32x4* const kn = kOdd ? k_slot0 : k_slot1;
       u32x4* const vn = kOdd ? v_slot0 : v_slot1;
       if (((e + 1) & 63) == 0 && e + 1 < cnt) {   // entry e + 1 opens the next batch
-        batch_cur = batch_nxt;
+        batch_cur = pack_block_entry(a, batch_nxt);
         batch_nxt = load_batch(((e + 1) >> 6) + 1);
       }
       const uint32_t jb_next = tile_of(e + 1);
@@ -439,7 +442,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   constexpr int kDT = D / 32;
   __shared__ u32x4 q_slot[4][S::kTile];
   __shared__ u32x4 d_slot[2][S::kTile];
-  __shared__ f32x4 vec_slot[2][2][kBlock / 4];   // [slot][lse2, D][4 rows]
+  // lse2 and D of a query block, [lse2, D][4 rows], in two slots that are separate LDS objects:
+  // reads of one slot then need not wait for the copies still landing in the other (or in the
+  // Q and dO rings)
+  __shared__ f32x4 vec_slot0[2][kBlock / 4], vec_slot1[2][kBlock / 4];
   __shared__ f32x4 p_slot[2][4][4][64];          // [slot][wave of the group][r / 4][lane]: P, fp32
   __shared__ int start_sh;
 
@@ -480,15 +486,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   }
   __syncthreads();
   const int start = __builtin_amdgcn_readfirstlane(start_sh);
-  // list entries, packed with their extents, 64 at a time a batch ahead (as
-  // in the forward); entry t of the pass is list entry start + t (wrapped),
-  // t clamped to the last one
+  // list entries, 64 at a time a batch ahead (as in the forward), packed
+  // with their extents when their batch comes into use; entry t of the pass
+  // is list entry start + t (wrapped), t clamped to the last one
   auto load_batch = [&](int b) {
     int pos = min(b * 64 + lane, cnt - 1) + start;
     pos -= pos >= cnt ? cnt : 0;
-    return pack_block_entry(a, list[pos]);
+    return list[pos];
   };
-  uint32_t batch_cur = 0, batch_nxt = 0;
+  uint32_t batch_cur = 0;    // packed
+  int32_t batch_nxt = 0;     // as loaded
   auto entry = [&](int t) {
     const int p = t < cnt ? t : cnt - 1;
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(batch_cur, p & 63));
@@ -555,10 +562,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
     }
     f32x16 dpm;   // dK group: dP - D of the tile before
     if (cnt == 0) return;
-    batch_cur = load_batch(0);
+    batch_cur = pack_block_entry(a, load_batch(0));
     batch_nxt = load_batch(1);
     uint32_t ib_cur = entry(0), ib_n1 = entry(1);
-    copy_vecs(ib_cur, vec_slot[0]);
+    copy_vecs(ib_cur, vec_slot0);
     copy_tile(ib_cur, q_slot[0], d_slot[0]);
     if (!kDk && cnt > 1) copy_tile(ib_n1, q_slot[1], nullptr);
     __builtin_amdgcn_s_waitcnt(0);
@@ -583,15 +590,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
     auto body = [&](int e, auto pslot) {
       constexpr int PS = decltype(pslot)::value;
       constexpr int PN = PS ^ 1;
+      f32x4 (&vec_here)[2][kBlock / 4] = PS ? vec_slot1 : vec_slot0;
       const int QS = e & 3, QB = (e - 1) & 3, Q2 = (e + 2) & 3;
       if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
-        batch_cur = batch_nxt;
+        batch_cur = pack_block_entry(a, batch_nxt);
         batch_nxt = load_batch(((e + 2) >> 6) + 1);
       }
       const uint32_t ib_next = ib_n1;
       const uint32_t ib_n2 = entry(e + 2);
       if (e + 1 < cnt) {
-        copy_vecs(ib_next, vec_slot[PN]);
+        copy_vecs(ib_next, PN ? vec_slot1 : vec_slot0);
         if constexpr (kDk) copy_tile(ib_next, nullptr, d_slot[PN]);
       }
       if constexpr (!kDk) {
@@ -603,12 +611,15 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
         if (e > 0) dk_step(p_slot[PN][w], q_slot[QB]);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 dv4 = vec_slot[PS][1][(row0 >> 2) + 2 * g + h];   // rows row0 + 8 g + 4 h ..
+          const f32x4 dv4 = vec_here[1][(row0 >> 2) + 2 * g + h];   // rows row0 + 8 g + 4 h ..
 #pragma unroll
           for (int x = 0; x < 4; ++x) dpm[4 * g + x] = dp[4 * g + x] - dv4[x];
         }
       } else {
         f32x16 s = rows_times(q_slot[QS], xf);
+        f32x4 lv[4];   // lse2 of this wave's rows, read before the branch below
+#pragma unroll
+        for (int g = 0; g < 4; ++g) lv[g] = vec_here[0][(row0 >> 2) + 2 * g + h];   // rows row0 + 8 g + 4 h ..
         // pad query rows (partial patches only: a uniform branch) get S =
         // -inf, hence P = dS = 0
         const BlockExtent ext = packed_extent(ib_cur);
@@ -620,11 +631,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
         bf16x8 wb[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 lv = vec_slot[PS][0][(row0 >> 2) + 2 * g + h];    // rows row0 + 8 g + 4 h ..
           f32x4 pr;
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            pr[x] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + x], c, -lv[x]));
+            pr[x] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + x], c, -lv[g][x]));
             wb[(4 * g + x) >> 3][(4 * g + x) & 7] = static_cast<__bf16>(pr[x]);
           }
           p_slot[PS][w][g][lane] = pr;

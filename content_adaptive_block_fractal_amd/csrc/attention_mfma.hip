@@ -249,12 +249,16 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   // Entry t of the pass is list entry start + t (wrapped); t is clamped to the
   // last one (loads past the end are redundant but in bounds, and their
   // results are never used).
+  // The next batch is kept as loaded and prepared (lay.prep) only when it
+  // comes into use: preparing it right after the load would wait for the
+  // load, and with it for every tile copy issued before it.
   auto load_batch = [&](int b) {
     int pos = min(b * 64 + lane, cnt - 1) + start;
     pos -= pos >= cnt ? cnt : 0;
-    return lay.prep(a, list[pos]);
+    return list[pos];
   };
-  uint32_t batch_cur = 0, batch_nxt = 0;   // entries 64 B .. and 64 (B + 1) .. of the pass
+  uint32_t batch_cur = 0;    // entries 64 B .. of the pass, prepared
+  int32_t batch_nxt = 0;     // entries 64 (B + 1) .., as loaded
   auto tile = [&](int t) {
     const int p = t < cnt ? t : cnt - 1;
     return lay.template decode<D>(a, __builtin_amdgcn_readlane(batch_cur, p & 63));
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
     // ---- prologue: K of tiles 0-2 and V of tile 0 in LDS, S^T of tile 0 ----
     const uint32_t koff = tile_load_offset<D, Swz::K>(wave, lane);
     const uint32_t voff = tile_load_offset<D, Swz::V>(wave, lane);
-    batch_cur = load_batch(0);
+    batch_cur = lay.prep(a, load_batch(0));
     batch_nxt = load_batch(1);
     const TileRef t0 = tile(0);
     TileRef t_next = tile(1);
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
       u32x4* const v_here = kOdd ? v_slot1 : v_slot0;    // slot e % 2
       u32x4* const v_fill = kOdd ? v_slot0 : v_slot1;    // slot (e + 1) % 2
       if (((e + 3) & 63) == 0 && e + 3 < cnt) {   // entry e + 3 opens the next batch
-        batch_cur = batch_nxt;
+        batch_cur = lay.prep(a, batch_nxt);
         batch_nxt = load_batch(((e + 3) >> 6) + 1);
       }
       const TileRef t3 = tile(e + 3);

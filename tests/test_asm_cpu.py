@@ -5,6 +5,13 @@ the builtin as a pointer to a float vector, the compiler emitted the null LDS
 address (M0 = -1) and then dropped every read of the slot as never written;
 these tests compile the kernels to assembly and check that every such copy
 gets a real base and that no tile kernel spills to scratch memory.
+
+The tile pipelines keep copies in flight across tiles and wait for them only
+at each tile's barrier. An LDS read that the compiler cannot tell apart from
+a slot a copy is still filling (two ring slots in one LDS object) makes it
+insert a full wait for every copy in flight in the middle of the tile, which
+silently takes the prefetch away; the last test checks that every wait on
+the copies after a copy is issued is the tile barrier's own.
 """
 import os
 import re
@@ -79,3 +86,49 @@ def test_tile_kernels_do_not_spill(assembly, f):
     text = assembly[f]
     for m in re.finditer(r"^\s*\.amdhsa_private_segment_fixed_size\s+(\d+)", text, flags=re.M):
         assert int(m.group(1)) == 0, f"{f}: a kernel uses {m.group(1)} bytes of scratch per lane"
+
+
+_SCALAR_GLUE = re.compile(r"^(s_waitcnt|s_mov|s_cbranch|s_branch|s_nop|s_and|s_or|s_andn2|s_cselect|s_cmp)")
+
+
+def _waits_before_barrier(body):
+    """Full waits on the memory counter (vmcnt(0)) that follow a tile copy
+    (global_load_lds) before the next s_barrier and are not part of that
+    barrier's own wait (the barrier within a few scalar instructions, labels
+    and branches of the wait)."""
+    lines = [ln.strip() for ln in body.splitlines()]
+    lines = [t for t in lines if t and not t.startswith(";") and not t.startswith(".") or
+             re.match(r"^\.LBB", t)]
+    bad, copy_seen = [], False
+    for i, t in enumerate(lines):
+        if t.startswith("s_barrier"):
+            copy_seen = False
+        elif t.startswith("global_load_lds"):
+            copy_seen = True
+        elif copy_seen and t.startswith("s_waitcnt") and "vmcnt(0)" in t:
+            ok = False
+            for u in lines[i + 1:i + 12]:
+                if u.startswith("s_barrier"):
+                    ok = True
+                    break
+                if re.match(r"^\.LBB\w+:", u) or _SCALAR_GLUE.match(u):
+                    continue
+                break
+            if not ok:
+                bad.append((i, t, lines[i + 1] if i + 1 < len(lines) else ""))
+    return bad
+
+
+TILE_KERNELS = ("bsa_fwd_mfma", "bwd_dq", "bwd_dkv")
+
+
+@pytest.mark.parametrize("f", ["attention_mfma.hip", "attention_bwd.hip"])
+def test_tile_loops_wait_for_copies_only_at_barriers(assembly, f):
+    checked = 0
+    for name, body in _kernels(assembly[f]):
+        if not any(k in name for k in TILE_KERNELS):
+            continue
+        checked += 1
+        bad = _waits_before_barrier(body)
+        assert not bad, f"{name}: waits on the copies in flight inside a tile: {bad[:3]}"
+    assert checked > 0
