@@ -34,10 +34,10 @@ def compare_grad(got, ref, rows, label):
     assert err.mean() <= REL_MEAN * scale_mean + 1e-7
 
 
-def setup(T, H, W, heads, d, thr, sta, seed=0, amp=0.7):
-    g = cabf.Geom(1, heads, d, T, H, W, 8)
+def setup(T, H, W, heads, d, thr, sta, seed=0, amp=0.7, batch=1):
+    g = cabf.Geom(batch, heads, d, T, H, W, 8)
     og = oracle.Grid(T, H, W, 8)
-    q, k, v = fourier_video_qkv(T, H, W, heads, d, amp, seed=seed, dtype="bf16")
+    q, k, v = fourier_video_qkv(T, H, W, heads, d, amp, seed=seed, dtype="bf16", batch=batch)
     qp, kp, vp = cabf.permute(q.to(DEV), k.to(DEV), v.to(DEV), g)
     s = cabf.default_scale(g)
     cnt, idx = cabf.build_block_mask(qp, kp, g, thr, sta, s)
@@ -77,6 +77,29 @@ def test_backward_matches_oracle(name, shape, thr, sta):
         for nm, got, r in (("dq", pq, ref[0]), ("dk", pk, ref[1]), ("dv", pv, ref[2])):
             compare_grad(got[0, hd], r, valid, f"{name} head {hd} {nm} (clock-phased)")
             assert torch.all(got[0, hd][torch.from_numpy(~valid).to(DEV)] == 0)
+
+
+def test_backward_batch_of_two():
+    """Two batch entries of two heads (the key-block order and every pass index
+    (batch, head) pairs as one flat axis): both orders against the oracle for
+    each (batch, head), and the list order repeats bit for bit."""
+    g, og, s, qp, kp, vp, cnt, idx, op, lse, dop = setup(3, 21, 35, 2, 128, 0.5, None, seed=13,
+                                                         batch=2)
+    det = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s, deterministic=True)
+    det2 = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s, deterministic=True)
+    pha = cabf.bsa_backward(qp, kp, vp, op, lse, dop, cnt, idx, g, s)
+    torch.cuda.synchronize()
+    for a, b in zip(det, det2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    valid = oracle.valid_slots(og)
+    for b in range(2):
+        for hd in range(g.heads):
+            ref = oracle.bsa_backward(to_np(qp[b, hd]), to_np(kp[b, hd]), to_np(vp[b, hd]),
+                                      to_np(dop[b, hd]), cnt[b, hd].cpu().numpy(),
+                                      idx[b, hd].cpu().numpy(), og, s)
+            for tag, grads in (("list order", det), ("clock-phased", pha)):
+                for nm, got, r in zip(("dq", "dk", "dv"), grads, ref):
+                    compare_grad(got[b, hd], r, valid, f"batch {b} head {hd} {nm} ({tag})")
 
 
 @pytest.mark.parametrize("name,shape,thr", [("ragged-d128", (3, 21, 35, 2, 128), 0.4),
