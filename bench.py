@@ -19,7 +19,9 @@ import math
 import os
 import re
 import platform
+import shutil
 import statistics
+import subprocess
 import sys
 import time
 
@@ -226,6 +228,62 @@ def measure_subset(cabf, geom, bufs, thr, sta, flags, steps: int, frac: float = 
     ms = statistics.fmean(a.elapsed_time(b) for a, b in times)
     return dict(active_blocks=int(ids.size), of_blocks=total, kept_tiles=kept, attention_ms=ms,
                 attention_tflops=flops / (ms * 1e-3) / 1e12)
+
+
+def _smi_sample(exe):
+    """(socket power W, mean gfx clock MHz over the XCDs) from one amd-smi reading, or None."""
+    try:
+        r = subprocess.run([exe, "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                           timeout=10)
+        gpu = json.loads(r.stdout)["gpu_data"][0]
+        watts = float(gpu["power"]["socket_power"]["value"])
+        clks = [float(v["clk"]["value"]) for k, v in gpu["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        return watts, (sum(clks) / len(clks) if clks else None)
+    except Exception:
+        return None
+
+
+def package_power(run, seconds=2.0):
+    """Median socket power (W) and gfx clock (MHz) that amd-smi reports while run() (which
+    enqueues GPU work) is repeated for about `seconds`, outside every timed region; None where
+    amd-smi is not available. Tells whether a kernel runs at the package power limit, where
+    the firmware lowers the clock."""
+    import threading
+
+    import torch
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            smp = _smi_sample(exe)
+            if smp is not None:
+                samples.append(smp)
+            stop.wait(0.2)
+
+    run()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        run()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    use = samples[1:] or samples          # the first reading can precede the load
+    if not use:
+        return None
+    watts = statistics.median(w for w, _ in use)
+    clks = [c for _, c in use if c is not None]
+    return {"socket_w": watts, "gfx_mhz": statistics.median(clks) if clks else None,
+            "samples": len(use)}
 
 
 def measured_peaks(cabf, dev):
@@ -684,6 +742,19 @@ def main():
     peaks = measured_peaks(cabf, dev)
     line["measured_peaks"] = peaks
     progress("measured peaks")
+    # package power and clock under each load (amd-smi; outside the timed regions): the
+    # attention runs at the package power limit, where the firmware lowers the clock
+    scale = cabf.default_scale(geom)
+    q0, k0, v0, qp0, kp0, vp0, op0, o0, cnt0, idx0, ws0 = bufs
+    pw_attn = package_power(lambda: cabf.cabf_bsa_forward(geom, qp0, kp0, vp0, cnt0, idx0, scale,
+                                                           op0, None, flags))
+    from content_adaptive_block_fractal_amd import peak_probe
+    probe_out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    pw_mfma = package_power(lambda: peak_probe.mfma_peak(2048, 2000, probe_out))
+    line["package_power"] = {
+        "attention": pw_attn, "mfma_probe": pw_mfma, "tool": "amd-smi metric -p -c",
+        "note": "median socket power and XCD gfx clock over ~2 s of back-to-back launches"}
+    progress(f"package power: attention {pw_attn}, matrix-core loop {pw_mfma}")
     line["roofline"]["frac_of_measured_peak"] = attn_tflops / peaks["mfma_bf16_tflops"]
     if args.variants:
         var = {}
