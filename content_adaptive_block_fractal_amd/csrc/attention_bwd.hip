@@ -116,8 +116,8 @@ template <int D>
 __device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, u32x4* sa, u32x4* sb,
                                           uint32_t off, int wave, int real_rows = kBlock,
                                           int real_cols = kP) {
-  issue_tile_load<D>(a, sa, off, wave, real_rows, real_cols);
-  issue_tile_load<D>(b, sb, off, wave, real_rows, real_cols);
+  issue_tile_load<D, kThreads, Copy::Asm>(a, sa, off, wave, real_rows, real_cols);
+  issue_tile_load<D, kThreads, Copy::Asm>(b, sb, off, wave, real_rows, real_cols);
 }
 
 // ---------------------------------------------------------------------------
@@ -442,9 +442,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   constexpr int kDT = D / 32;
   __shared__ u32x4 q_slot[4][S::kTile];
   __shared__ u32x4 d_slot[2][S::kTile];
-  // lse2 and D of a query block, [lse2, D][4 rows], in two slots that are separate LDS objects:
-  // reads of one slot then need not wait for the copies still landing in the other (or in the
-  // Q and dO rings)
+  // lse2 and D of a query block, [lse2, D][4 rows], in two slots
   __shared__ f32x4 vec_slot0[2][kBlock / 4], vec_slot1[2][kBlock / 4];
   __shared__ f32x4 p_slot[2][4][4][64];          // [slot][wave of the group][r / 4][lane]: P, fp32
   __shared__ int start_sh;
@@ -528,14 +526,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   };
   // lse2 and D of query block pe -> vec slot, copied straight into LDS by
   // wave 0 (one dword per lane) ahead of its Q copy, so the tile's wait
-  // covers them and no register waits on them. The LDS operand goes in as
-  // float*: passed as a vector pointer, the compiler turned it into the null
-  // LDS address.
+  // covers them and no register waits on them.
   auto copy_vecs = [&](uint32_t pe, f32x4 (&vec)[2][kBlock / 4]) {
     if (wave == 0) {
       const int64_t r0 = static_cast<int64_t>(packed_block(pe)) * kBlock;
-      __builtin_amdgcn_global_load_lds(lse_h + r0 + lane, reinterpret_cast<float*>(vec[0]), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(dl_h + r0 + lane, reinterpret_cast<float*>(vec[1]), 4, 0, 0);
+      lds_copy_x1_asm(lse_h + r0, 4 * lane, vec[0]);
+      lds_copy_x1_asm(dl_h + r0, 4 * lane, vec[1]);
     }
   };
   const uint32_t off = tile_load_offset<D, Swz::B>(w, lane);
@@ -548,9 +544,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
     auto copy_tile = [&](uint32_t pe, u32x4* qs, u32x4* ds) {
       const int64_t r0 = static_cast<int64_t>(packed_block(pe)) * kBlock * D;
       if constexpr (kDk)
-        issue_tile_load<D>(dO + r0, ds, off, w, rows(pe), cols(pe));
+        issue_tile_load<D, kThreads, Copy::Asm>(dO + r0, ds, off, w, rows(pe), cols(pe));
       else
-        issue_tile_load<D>(Q + r0, qs, off, w, rows(pe), cols(pe));
+        issue_tile_load<D, kThreads, Copy::Asm>(Q + r0, qs, off, w, rows(pe), cols(pe));
     };
     // K (dV group) or V (dK group) rows of this lane's key
     bf16x8 xf[kKS];
