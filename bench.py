@@ -53,6 +53,9 @@ def parse():
                     help="also time the block-sparse attention backward at the main sparsity (0 to skip)")
     ap.add_argument("--semantic", type=int, default=1,
                     help="also time the semantic-permutation (k-means + top-p) variant (0 to skip)")
+    ap.add_argument("--power", type=int, default=1,
+                    help="sample package power and clock with amd-smi (0: skip, e.g. under a "
+                         "profiler, which does not let a child process start another program)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle CPU-baseline sample (0 to skip)")
     return ap.parse_args()
@@ -746,11 +749,13 @@ def main():
     # attention runs at the package power limit, where the firmware lowers the clock
     scale = cabf.default_scale(geom)
     q0, k0, v0, qp0, kp0, vp0, op0, o0, cnt0, idx0, ws0 = bufs
-    pw_attn = package_power(lambda: cabf.cabf_bsa_forward(geom, qp0, kp0, vp0, cnt0, idx0, scale,
-                                                           op0, None, flags))
-    from content_adaptive_block_fractal_amd import peak_probe
-    probe_out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
-    pw_mfma = package_power(lambda: peak_probe.mfma_peak(2048, 2000, probe_out))
+    pw_attn = pw_mfma = None
+    if args.power:
+        pw_attn = package_power(lambda: cabf.cabf_bsa_forward(geom, qp0, kp0, vp0, cnt0, idx0,
+                                                               scale, op0, None, flags))
+        from content_adaptive_block_fractal_amd import peak_probe
+        probe_out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+        pw_mfma = package_power(lambda: peak_probe.mfma_peak(2048, 2000, probe_out))
     line["package_power"] = {
         "attention": pw_attn, "mfma_probe": pw_mfma, "tool": "amd-smi metric -p -c",
         "note": "median socket power and XCD gfx clock over ~2 s of back-to-back launches"}
