@@ -316,18 +316,21 @@ __global__ __launch_bounds__(256) void bwd_fill_zero(uint32_t* __restrict__ p, i
   if (e < words) p[e] = 0u;
 }
 
+// one wave per row (bh, query block i) over its list entries
 __global__ __launch_bounds__(256) void bwd_bitmap(const int32_t* __restrict__ kv_count,
                                                   const int32_t* __restrict__ kv_index,
                                                   uint32_t* __restrict__ bitmap, int nb, int words,
-                                                  int64_t total /* BH * nb * nb */) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int64_t row = e / nb;                     // bh * nb + i
-  const int t = static_cast<int>(e - row * nb);
-  if (t >= min(max(kv_count[row], 0), nb)) return;
-  const int j = kv_index[e];
-  if (static_cast<unsigned>(j) >= static_cast<unsigned>(nb)) return;
-  atomicOr(bitmap + row * words + (j >> 5), 1u << (j & 31));
+                                                  int64_t rows /* BH * nb */) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int cnt = min(max(kv_count[row], 0), nb);
+  const int32_t* lst = kv_index + row * nb;
+  uint32_t* bm = bitmap + row * words;
+  for (int t = lane; t < cnt; t += 64) {
+    const int j = lst[t];
+    if (static_cast<unsigned>(j) < static_cast<unsigned>(nb)) atomicOr(bm + (j >> 5), 1u << (j & 31));
+  }
 }
 
 // one wave per (bh, key block j): the query blocks i with bit (i, j), ascending
@@ -746,9 +749,8 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
                        delta, lse2, rows);
   const int64_t words = g.BH * g.nb * w.words;
   hipLaunchKernelGGL(bwd_fill_zero, grid_for(words, 256), dim3(256), 0, stream, bitmap, words);
-  const int64_t entries = g.BH * g.nb * g.nb;
-  hipLaunchKernelGGL(bwd_bitmap, grid_for(entries, 256), dim3(256), 0, stream, kv_count, kv_index,
-                     bitmap, g.nb, w.words, entries);
+  hipLaunchKernelGGL(bwd_bitmap, grid_for(g.BH * g.nb, 4), dim3(256), 0, stream, kv_count, kv_index,
+                     bitmap, g.nb, w.words, g.BH * g.nb);
   hipLaunchKernelGGL(bwd_transpose, grid_for(g.BH * g.nb, 4), dim3(256), 0, stream, bitmap, q_count,
                      q_index, g.nb, w.words, g.BH * g.nb);
   // Key blocks by transposed-list length, longest first: the dK/dV pass
