@@ -316,7 +316,10 @@ __global__ __launch_bounds__(256) void bwd_fill_zero(uint32_t* __restrict__ p, i
   if (e < words) p[e] = 0u;
 }
 
-// one wave per row (bh, query block i) over its list entries
+// One wave per row (bh, query block i) over its list, 64 entries at a time.
+// The list ascends, so entries in the same 32-bit word sit in consecutive
+// lanes: an OR scan within each such run leaves the run's word in its last
+// lane, which alone writes it (atomically: a word can span two batches).
 __global__ __launch_bounds__(256) void bwd_bitmap(const int32_t* __restrict__ kv_count,
                                                   const int32_t* __restrict__ kv_index,
                                                   uint32_t* __restrict__ bitmap, int nb, int words,
@@ -327,34 +330,56 @@ __global__ __launch_bounds__(256) void bwd_bitmap(const int32_t* __restrict__ kv
   const int cnt = min(max(kv_count[row], 0), nb);
   const int32_t* lst = kv_index + row * nb;
   uint32_t* bm = bitmap + row * words;
-  for (int t = lane; t < cnt; t += 64) {
-    const int j = lst[t];
-    if (static_cast<unsigned>(j) < static_cast<unsigned>(nb)) atomicOr(bm + (j >> 5), 1u << (j & 31));
+  for (int t0 = 0; t0 < cnt; t0 += 64) {
+    const int t = t0 + lane;
+    const int j = t < cnt ? lst[t] : -1;
+    const bool on = static_cast<unsigned>(j) < static_cast<unsigned>(nb);
+    const int wd = on ? (j >> 5) : -1 - lane;     // lanes without an entry form runs of their own
+    uint32_t bits = on ? 1u << (j & 31) : 0u;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const uint32_t b = __shfl_up(bits, sh);
+      const int w = __shfl_up(wd, sh);
+      bits |= (lane >= sh && w == wd) ? b : 0u;
+    }
+    const int next = __shfl_down(wd, 1);
+    if (on && (lane == 63 || next != wd)) atomicOr(bm + wd, bits);
   }
 }
 
-// one wave per (bh, key block j): the query blocks i with bit (i, j), ascending
+// One wave per (bh, word column c): key blocks j = 32 c .. 32 c + 31. Each
+// lane reads the word of query block i (64 at a time), which holds bits
+// (i, j) for all 32 of them, so every word is read once; per key block a
+// ballot over the lanes gives the kept query blocks of this batch in
+// ascending order, appended to j's list. Lane b keeps the count of key
+// block 32 c + b.
 __global__ __launch_bounds__(256) void bwd_transpose(const uint32_t* __restrict__ bitmap,
                                                      int32_t* __restrict__ q_count,
                                                      int32_t* __restrict__ q_index, int nb,
-                                                     int words, int64_t rows /* BH * nb */) {
+                                                     int words, int64_t cols /* BH * words */) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int64_t bh = row / nb;
-  const int j = static_cast<int>(row - bh * nb);
-  const uint32_t* bm = bitmap + bh * nb * static_cast<int64_t>(words) + (j >> 5);
-  int32_t* out = q_index + row * nb;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (col >= cols) return;
+  const int64_t bh = col / words;
+  const int c = static_cast<int>(col - bh * words);
+  const uint32_t* bm = bitmap + bh * nb * static_cast<int64_t>(words) + c;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int count = 0;
+  const int jn = min(32, nb - 32 * c);          // key blocks in this column
+  int count = 0;                                // lane b < jn: count of key block 32 c + b
   for (int base = 0; base < nb; base += 64) {
     const int i = base + lane;
-    const bool keep = i < nb && ((bm[static_cast<int64_t>(i) * words] >> (j & 31)) & 1u);
-    const uint64_t b = __ballot(keep);
-    if (keep) out[count + __popcll(b & lt)] = i;
-    count += __popcll(b);
+    const uint32_t wv = i < nb ? bm[static_cast<int64_t>(i) * words] : 0u;
+    for (int b = 0; b < jn; ++b) {
+      const bool keep = (wv >> b) & 1u;
+      const uint64_t m = __ballot(keep);
+      if (m == 0) continue;
+      const int before = __shfl(count, b);      // key block 32 c + b's count so far
+      const int64_t row = bh * nb + 32 * c + b;
+      if (keep) q_index[row * nb + before + __popcll(m & lt)] = i;
+      count += lane == b ? __popcll(m) : 0;
+    }
   }
-  if (lane == 0) q_count[row] = count;
+  if (lane < jn) q_count[bh * nb + 32 * c + lane] = count;
 }
 
 // Key blocks of each (batch, head) ordered by the length of their transposed
@@ -751,8 +776,8 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   hipLaunchKernelGGL(bwd_fill_zero, grid_for(words, 256), dim3(256), 0, stream, bitmap, words);
   hipLaunchKernelGGL(bwd_bitmap, grid_for(g.BH * g.nb, 4), dim3(256), 0, stream, kv_count, kv_index,
                      bitmap, g.nb, w.words, g.BH * g.nb);
-  hipLaunchKernelGGL(bwd_transpose, grid_for(g.BH * g.nb, 4), dim3(256), 0, stream, bitmap, q_count,
-                     q_index, g.nb, w.words, g.BH * g.nb);
+  hipLaunchKernelGGL(bwd_transpose, grid_for(g.BH * w.words, 4), dim3(256), 0, stream, bitmap,
+                     q_count, q_index, g.nb, w.words, g.BH * w.words);
   // Key blocks by transposed-list length, longest first: the dK/dV pass
   // then runs lists of about the same length side by side (a key block is
   // kept by 57 to 427 query blocks at 720p / 80%), so concurrent workgroups
