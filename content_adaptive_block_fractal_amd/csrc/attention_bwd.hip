@@ -123,6 +123,15 @@ __device__ __forceinline__ void load_pair(const uint16_t* a, const uint16_t* b, 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per query block. Wave (wq, wk): query half wq, key half
 // wk of every tile; lane holds query row li of its half (as in the forward).
+// Software-pipelined by one tile: in tile e the matrix cores run S^T and dP^T
+// of tile e + 1 and then dQ^T += K^T dS^T of tile e (dS of e formed in tile
+// e - 1), and the vector units form dS of e + 1 while the dQ products run.
+// K therefore stays in LDS for two tiles: three K slots, two V slots (80 KB
+// at d = 128, two workgroups per CU); K and V of e + 2 stream in during tile
+// e. Every product and dS value is the same as in a pass without the skew
+// (bit-identical gradients); at 720p / 80% the backward took 99.2-99.5 ms
+// against 100.5 ms without the skew in list order, and 100.0-100.4 against
+// 100.1-100.6 ms clock-phased (one box, interleaved runs).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t* __restrict__ dop,
@@ -132,8 +141,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   using S = Stage<D>;
   constexpr int kKS = D / 16;
   constexpr int kDT = D / 32;
-  __shared__ u32x4 k_slot0[S::kTile], k_slot1[S::kTile];
-  __shared__ u32x4 v_slot0[S::kTile], v_slot1[S::kTile];
+  // One LDS array for the ring (K slots 0-2, V slots 3-4): a slot is a
+  // constant offset from one base, which the reads take as their immediate
+  // offset, so one address register per lane offset serves every slot (with
+  // separate arrays the compiler kept an address per slot and spilled). The
+  // copies are asm statements the compiler does not see, so it does not wait
+  // for them where a read might alias a slot being filled.
+  __shared__ u32x4 ring[5][S::kTile];
+  u32x4* const k_slot0 = ring[0];
+  u32x4* const k_slot1 = ring[1];
+  u32x4* const k_slot2 = ring[2];
+  u32x4* const v_slot0 = ring[3];
+  u32x4* const v_slot1 = ring[4];
+  // the start position borrows K slot 2, which the first copy into it
+  // (tile 0) finds read
+  int* const start_shared = reinterpret_cast<int*>(k_slot2);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,14 +191,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   int toff[kDT][2];
   transposed_offsets<D>(toff, key0, lane);
   // first list entry of the pass (0, or clock-phased: see clock_phased_start)
-  __shared__ int start_sh;
   if (wave == 0) {
     const int st = clock_phased_start(a.kv_count + bh * a.nb, list, a.nb, cnt, a.sweep_ticks,
                                       lane);
-    if (lane == 0) start_sh = st;
+    if (lane == 0) *start_shared = st;
   }
   __syncthreads();
-  const int start = __builtin_amdgcn_readfirstlane(start_sh);
+  const int start = __builtin_amdgcn_readfirstlane(*start_shared);
   // List entries are fetched 64 at a time, one per lane, a batch ahead of
   // use, and read out with readlane (as in the forward): no list load is
   // waited on per tile. Entry t of the pass is list entry start + t
@@ -214,22 +235,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     }
     return r;
   };
-  // pad keys of a partial patch (a uniform branch) get S = -inf, hence P = dS = 0
-  auto step = [&](uint32_t pe, const u32x4* ks_, const u32x4* vs_) {
-    f32x16 s = rows_times(ks_, qf);
-    const f32x16 dp = rows_times(vs_, df);
+  // dS^T = P (dP - D) in bf16 of a tile whose S^T and dP^T are in s, dp;
+  // pad keys of a partial patch (a uniform branch) get S = -inf, hence P =
+  // dS = 0
+  auto form_ds = [&](f32x16 s, const f32x16& dp, uint32_t pe, bf16x8 (&dsb)[2]) {
     const BlockExtent ext = packed_extent(pe);
     if (!ext.full()) {
       const uint32_t bits = real_accumulator_bits(ext, wk, h);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = ((bits >> r) & 1u) ? s[r] : -INFINITY;
     }
-    bf16x8 dsb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
       dsb[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dlt));
     }
+  };
+  // dQ^T += K^T dS^T with K^T from transposing reads of the K tile `ks_`
+  auto dq_products = [&](const u32x4* ks_, const bf16x8 (&dsb)[2]) {
     const uint16_t* kt = reinterpret_cast<const uint16_t*>(ks_);
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -243,33 +266,68 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
     const uint32_t off = tile_load_offset<D, Swz::B>(wave, lane);
     batch_cur = pack_block_entry(a, load_batch(0));
     batch_nxt = load_batch(1);
-    uint32_t jb_cur = tile_of(0);
+    uint32_t jb_cur = tile_of(0);    // tile e
+    uint32_t jb_n1 = tile_of(1);     // tile e + 1
     load_pair<D>(K + tile_off(jb_cur), V + tile_off(jb_cur), k_slot0, v_slot0, off, wave,
                  tile_rows(jb_cur), tile_cols(jb_cur));
+    if (cnt > 1)
+      load_pair<D>(K + tile_off(jb_n1), V + tile_off(jb_n1), k_slot1, v_slot1, off, wave,
+                   tile_rows(jb_n1), tile_cols(jb_n1));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    auto body = [&](int e, auto parity) {
+    bf16x8 dsb[2];   // dS^T of tile e
+    form_ds(rows_times(k_slot0, qf), rows_times(v_slot0, df), jb_cur, dsb);
+    __syncthreads();   // V slot 0 is refilled in tile 0
+    // tile e: K of e in k_slot[e % 3], K and V of e + 1 in k_slot[(e + 1) % 3]
+    // and v_slot[(e + 1) % 2]; K and V of e + 2 stream into k_slot[(e + 2) %
+    // 3] and v_slot[e % 2], last read in tile e - 1.
+    auto body = [&](int e, auto parity, auto phase) {
       constexpr int kOdd = decltype(parity)::value;
-      u32x4* const kc = kOdd ? k_slot1 : k_slot0;
-      u32x4* const vc = kOdd ? v_slot1 : v_slot0;
-      u32x4* const kn = kOdd ? k_slot0 : k_slot1;
-      u32x4* const vn = kOdd ? v_slot0 : v_slot1;
-      if (((e + 1) & 63) == 0 && e + 1 < cnt) {   // entry e + 1 opens the next batch
+      constexpr int kPh = decltype(phase)::value;
+      u32x4* const k_here = kPh == 0 ? k_slot0 : (kPh == 1 ? k_slot1 : k_slot2);   // e % 3
+      u32x4* const k_next = kPh == 0 ? k_slot1 : (kPh == 1 ? k_slot2 : k_slot0);   // (e + 1) % 3
+      u32x4* const k_fill = kPh == 0 ? k_slot2 : (kPh == 1 ? k_slot0 : k_slot1);   // (e + 2) % 3
+      u32x4* const v_next = kOdd ? v_slot0 : v_slot1;    // (e + 1) % 2
+      u32x4* const v_fill = kOdd ? v_slot1 : v_slot0;    // e % 2
+      if (((e + 2) & 63) == 0 && e + 2 < cnt) {   // entry e + 2 opens the next batch
         batch_cur = pack_block_entry(a, batch_nxt);
-        batch_nxt = load_batch(((e + 1) >> 6) + 1);
+        batch_nxt = load_batch(((e + 2) >> 6) + 1);
       }
-      const uint32_t jb_next = tile_of(e + 1);
-      if (e + 1 < cnt)
-        load_pair<D>(K + tile_off(jb_next), V + tile_off(jb_next), kn, vn, off, wave,
-                     tile_rows(jb_next), tile_cols(jb_next));
-      step(jb_cur, kc, vc);
-      jb_cur = jb_next;
+      const uint32_t jb_n2 = tile_of(e + 2);
+      if (e + 2 < cnt)
+        load_pair<D>(K + tile_off(jb_n2), V + tile_off(jb_n2), k_fill, v_fill, off, wave,
+                     tile_rows(jb_n2), tile_cols(jb_n2));
+      __builtin_amdgcn_sched_barrier(0);
+      // past the end of the list the products of tile e + 1 read a stale
+      // slot; their results are not used
+      const f32x16 s = rows_times(k_next, qf);
+      const f32x16 dp = rows_times(v_next, df);
+      dq_products(k_here, dsb);
+      form_ds(s, dp, jb_n1, dsb);
+      jb_n1 = jb_n2;
+      // Every copy has landed: K and V of e + 2 are in LDS for every wave
+      // after the barrier. The scheduling barrier keeps the wait after this
+      // tile's work; the empty asm statements keep the compiler from moving
+      // LDS accesses across the barrier.
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     };
-    for (int e = 0; e < cnt; e += 2) {
-      body(e, std::integral_constant<int, 0>{});
-      if (e + 1 < cnt) body(e + 1, std::integral_constant<int, 1>{});
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // unrolled by six (three K slots, two V slots) with a guard per body (a
+    // chain of bodies joined by breaks moved the accumulators between
+    // register sets and spilled)
+    for (int e = 0; e < cnt; e += 6) {
+      body(e, I0{}, I0{});
+      if (e + 1 < cnt) body(e + 1, I1{}, I1{});
+      if (e + 2 < cnt) body(e + 2, I0{}, I2{});
+      if (e + 3 < cnt) body(e + 3, I1{}, I0{});
+      if (e + 4 < cnt) body(e + 4, I0{}, I1{});
+      if (e + 5 < cnt) body(e + 5, I1{}, I2{});
     }
   }
 
