@@ -879,6 +879,11 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   AttnArgs a_dq = a, a_dkv = a;
   a_dq.sweep_ticks = t_dq;
   a_dkv.sweep_ticks = t_dkv;
+  // Each XCD keeps a contiguous range of the items (xcd_order), unlike the
+  // forward's one launch (xcd_group_for): with two XCDs per head at 720p the
+  // dQ pass ran as fast as before (95.5 vs 95.6 ms, whole backward) and the
+  // dK/dV pass much slower (108 ms), its length-sorted key blocks splitting
+  // into the long lists of one XCD and the short ones of the other.
   const void* kdq = g.D == 64 ? reinterpret_cast<const void*>(&bwd_dq<64>)
                               : reinterpret_cast<const void*>(&bwd_dq<128>);
   const int64_t per_dq = phased ? items : kGenerationsPerLaunch * resident_workgroups(kdq, kThreads, stream);

@@ -36,7 +36,29 @@ struct AttnArgs {
   // launches of as many workgroups as the device holds at once (see
   // resident_workgroups), each over the next items.
   int64_t item0;
+  // XCDs that share a head in a pass over all BH * nb items in one launch
+  // (xcd_head_order; xcd_group_for picks it), or 0: every XCD takes a
+  // contiguous range of the items (xcd_order).
+  int xcd_group;
 };
+
+// XCDs per head for a pass over all BH * nb items of a head-major work space
+// in one launch: the smallest group (1, 2, 4 or 8 of the 8 XCDs) whose heads
+// in flight, 8 / group of them, keep their K and V (or Q and dO: 2 N D bf16
+// values per head) within three quarters of the 256 MB last-level cache
+// (MALL) beyond the L2s. With more heads in flight the tiles that miss L2
+// come from HBM instead (720p, 40 heads of 41 MB: two XCDs per head, four
+// heads in flight, gave the forward 1-4% over one head per XCD).
+inline int xcd_group_for(int64_t BH, int nb, int64_t N, int D) {
+  const int64_t head_bytes = 2 * N * D * 2;
+  const int64_t budget = int64_t{192} << 20;
+  for (int g = 1; g <= 8; g *= 2) {
+    const int64_t in_flight = 8 / g;
+    if (in_flight * head_bytes > budget || nb % g != 0 || BH % in_flight != 0) continue;
+    return g;
+  }
+  return 1;
+}
 
 // Workgroups of `kernel` (launched with `threads` threads and no dynamic LDS)
 // that the device of `stream` runs at once; 0 when the runtime cannot say.

@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   const int li = lane & 31;
   const int h = lane >> 5;
   WorkItem w;
-  if (!lay.work(a, a.item0 + xcd_order(blockIdx.x, n_items), w)) return;   // uniform per workgroup
+  if (!lay.work(a, a.item0 + xcd_head_order(blockIdx.x, n_items, a.nb, a.xcd_group), w))
+    return;   // uniform per workgroup
   const int64_t bh = w.bh;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.kp) + bh * a.N * D;
@@ -530,6 +531,9 @@ void launch_bsa_forward_mfma(const AttnArgs& args, int D, bool phased, hipStream
   // together; a launch as large as the device keeps them in step (see
   // launch_bsa_forward).
   const int64_t per = phased ? n : kGenerationsPerLaunch * resident_workgroups(kernel, kThreads, stream);
+  // one launch over every head: XCDs share heads so that the heads in flight
+  // fit the last-level cache
+  a.xcd_group = phased ? xcd_group_for(a.BH, a.nb, a.N, D) : 0;
   launch_in_generations(n, per, [&](int64_t first, int64_t count) {
     a.item0 = first;
     const unsigned grid = static_cast<unsigned>(count);
