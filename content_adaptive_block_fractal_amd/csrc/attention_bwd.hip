@@ -542,7 +542,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkv(AttnArgs a, const uin
   const int li = lane & 31, h = lane >> 5;
   // bh * nb + key block j; with k_order, slot r of a head runs its r-th
   // longest transposed list
-  const int64_t slot = a.item0 + xcd_order(blockIdx.x, n_items);
+  const int64_t slot = a.item0 + xcd_head_order(blockIdx.x, n_items, a.nb, a.xcd_group, true);
   const int64_t bh = slot / a.nb;
   const int64_t item =
       k_order != nullptr ? bh * a.nb + min(max(k_order[slot], 0), a.nb - 1) : slot;
@@ -879,11 +879,14 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   AttnArgs a_dq = a, a_dkv = a;
   a_dq.sweep_ticks = t_dq;
   a_dkv.sweep_ticks = t_dkv;
-  // Each XCD keeps a contiguous range of the items (xcd_order), unlike the
-  // forward's one launch (xcd_group_for): with two XCDs per head at 720p the
-  // dQ pass ran as fast as before (95.5 vs 95.6 ms, whole backward) and the
-  // dK/dV pass much slower (108 ms), its length-sorted key blocks splitting
-  // into the long lists of one XCD and the short ones of the other.
+  // The dK/dV pass (one launch in both orders) shares heads between XCDs as
+  // the forward does (xcd_group_for), each XCD of a group taking every
+  // group-th key block of the length-sorted order, so that both get the same
+  // mix of list lengths: 720p, whole backward 96.3 against 97.4 ms (contiguous
+  // halves, long lists on one XCD and short ones on the other: 108 ms). The
+  // dQ pass keeps a contiguous range of query blocks per XCD (xcd_order):
+  // two XCDs per head left it as fast as before (95.5 vs 95.6 ms).
+  a_dkv.xcd_group = xcd_group_for(g.BH, g.nb, g.N, g.D);
   const void* kdq = g.D == 64 ? reinterpret_cast<const void*>(&bwd_dq<64>)
                               : reinterpret_cast<const void*>(&bwd_dq<128>);
   const int64_t per_dq = phased ? items : kGenerationsPerLaunch * resident_workgroups(kdq, kThreads, stream);
