@@ -86,6 +86,10 @@ struct WorkItem {
 // padded patches are masked.
 struct BlockListLayout {
   static constexpr bool kPhased = true;   // clock-phased start (AttnArgs::sweep_ticks)
+  // work items per head, and whether the XCDs sharing a head (xcd_head_order)
+  // take contiguous parts of its items or interleave them
+  static constexpr bool kInterleave = false;
+  __device__ int64_t items_per_head(const AttnArgs& a) const { return a.nb; }
   __device__ bool work(const AttnArgs& a, int64_t item, WorkItem& w) const {
     w.bh = item / a.nb;
     w.qrow0 = item * kBlock;
@@ -138,6 +142,9 @@ struct SubsetLayout : BlockListLayout {
 // entries are key chunks (first key row << 6) | (keys - 1), 1 to 64 keys.
 struct ClusterLayout {
   static constexpr bool kPhased = false;
+  // the tiles of a head are ordered by cluster, unused entries last: XCDs
+  // sharing a head interleave them, so each gets the same mix
+  static constexpr bool kInterleave = true;
   const int32_t* tiles;         // [BH, max_tiles, 2]: query cluster (or -1), first row
   int max_tiles;
   const int32_t* q_off;         // [BH, cq + 1]
@@ -145,6 +152,7 @@ struct ClusterLayout {
   const int32_t* chunk_count;   // [BH, cq]
   const int32_t* chunks;        // [BH, cq, cap]
   int cap;
+  __device__ int64_t items_per_head(const AttnArgs&) const { return max_tiles; }
   __device__ bool work(const AttnArgs& a, int64_t item, WorkItem& w) const {
     const int qa = tiles[item * 2];
     if (qa < 0) return false;
@@ -205,7 +213,9 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_mfma(AttnArgs a, L lay, i
   const int li = lane & 31;
   const int h = lane >> 5;
   WorkItem w;
-  if (!lay.work(a, a.item0 + xcd_head_order(blockIdx.x, n_items, a.nb, a.xcd_group), w))
+  if (!lay.work(a, a.item0 + xcd_head_order(blockIdx.x, n_items, lay.items_per_head(a), a.xcd_group,
+                                             L::kInterleave),
+                w))
     return;   // uniform per workgroup
   const int64_t bh = w.bh;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp);
@@ -562,11 +572,15 @@ void launch_bsa_forward_subset_mfma(const AttnArgs& args, int D, bool phased,
                        lay, n);
 }
 
-void launch_cluster_attention_mfma(const AttnArgs& a, int D, const int32_t* tiles, int max_tiles,
+void launch_cluster_attention_mfma(const AttnArgs& args, int D, const int32_t* tiles, int max_tiles,
                                    const int32_t* q_off, int cq, const int32_t* chunk_count,
                                    const int32_t* chunks, int cap, hipStream_t stream) {
   ClusterLayout lay{tiles, max_tiles, q_off, cq, chunk_count, chunks, cap};
+  AttnArgs a = args;
   const int64_t n = a.BH * max_tiles;
+  // XCDs share heads so that the heads in flight keep their (gathered) K and
+  // V in the last-level cache, as in the block-list forward
+  a.xcd_group = xcd_group_for(a.BH, max_tiles, a.N, D);
   const unsigned grid = static_cast<unsigned>(n);
   if (D == 64)
     hipLaunchKernelGGL((bsa_fwd_mfma<64, ClusterLayout>), dim3(grid), dim3(kThreads), 0, stream, a,
