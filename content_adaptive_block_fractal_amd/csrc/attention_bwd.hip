@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(AttnArgs a, const uint16_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave & 1, wk = wave >> 1;
   const int li = lane & 31, h = lane >> 5;
-  const int64_t item = a.item0 + xcd_order(blockIdx.x, n_items);
+  const int64_t item = a.item0 + xcd_head_order(blockIdx.x, n_items, a.nb, a.xcd_group, true);
   const int64_t bh = item / a.nb;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.qp);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.kp) + bh * a.N * D;
@@ -879,14 +879,16 @@ void launch_bsa_backward(const Geo& g, const void* qp, const void* kp, const voi
   AttnArgs a_dq = a, a_dkv = a;
   a_dq.sweep_ticks = t_dq;
   a_dkv.sweep_ticks = t_dkv;
-  // The dK/dV pass (one launch in both orders) shares heads between XCDs as
-  // the forward does (xcd_group_for), each XCD of a group taking every
-  // group-th key block of the length-sorted order, so that both get the same
-  // mix of list lengths: 720p, whole backward 96.3 against 97.4 ms (contiguous
-  // halves, long lists on one XCD and short ones on the other: 108 ms). The
-  // dQ pass keeps a contiguous range of query blocks per XCD (xcd_order):
-  // two XCDs per head left it as fast as before (95.5 vs 95.6 ms).
+  // Both passes in one launch share heads between XCDs as the forward does
+  // (xcd_group_for), each XCD of a group taking every group-th item: in the
+  // dK/dV pass (one launch in both orders) the key blocks of the
+  // length-sorted order, so that both XCDs get the same mix of list lengths
+  // (720p, whole backward 96.3 against 97.4 ms; contiguous halves, long lists
+  // on one XCD and short ones on the other: 108 ms); in the clock-phased dQ
+  // pass the query blocks (94.5 against 94.9-95.3 ms; contiguous halves: no
+  // change).
   a_dkv.xcd_group = xcd_group_for(g.BH, g.nb, g.N, g.D);
+  a_dq.xcd_group = phased ? xcd_group_for(g.BH, g.nb, g.N, g.D) : 0;
   const void* kdq = g.D == 64 ? reinterpret_cast<const void*>(&bwd_dq<64>)
                               : reinterpret_cast<const void*>(&bwd_dq<128>);
   const int64_t per_dq = phased ? items : kGenerationsPerLaunch * resident_workgroups(kdq, kThreads, stream);
