@@ -42,7 +42,7 @@ struct AttnArgs {
   int xcd_group;
 };
 
-// XCDs per head for a pass over all BH * nb items of a head-major work space
+// XCDs per head for a pass over all BH * nb items (nb per head, head-major)
 // in one launch: the smallest group (1, 2, 4 or 8 of the 8 XCDs) whose heads
 // in flight, 8 / group of them, keep their K and V (or Q and dO: 2 N D bf16
 // values per head) within three quarters of the 256 MB last-level cache

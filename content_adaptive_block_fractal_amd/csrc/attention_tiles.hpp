@@ -29,24 +29,24 @@ __device__ inline int64_t xcd_order(int64_t wg, int64_t total) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
-// Workgroup id -> work item (h * nb + block) of a pass over all BH heads in
-// one launch, with `group` XCDs sharing a head: XCD x = group * p + q works
-// through heads p, p + 8 / group, p + 2 (8 / group), ... and takes the q-th
-// share of each head's nb blocks, so the XCDs of a group are on the same head
-// at about the same time and 8 / group heads are in flight. The share is the
-// q-th of `group` contiguous parts, or with `interleaved` every group-th
-// block from q (for work ordered by size, so that the XCDs of a group get
-// the same mix). The caller guarantees nb % group == 0 and BH % (8 / group)
-// == 0 (xcd_group_for); group <= 1 is xcd_order.
-__device__ inline int64_t xcd_head_order(int64_t wg, int64_t total, int nb, int group,
+// Workgroup id -> work item (h * per_head + i) of a pass over the items of
+// all BH heads in one launch, with `group` XCDs sharing a head: XCD x =
+// group * p + q works through heads p, p + 8 / group, p + 2 (8 / group), ...
+// and takes the q-th share of each head's items, so the XCDs of a group are
+// on the same head at about the same time and 8 / group heads are in flight.
+// The share is the q-th of `group` contiguous parts, or with `interleaved`
+// every group-th item from q (for items ordered by size, so that the XCDs of
+// a group get the same mix). The caller guarantees per_head % group == 0 and
+// BH % (8 / group) == 0 (xcd_group_for); group <= 1 is xcd_order.
+__device__ inline int64_t xcd_head_order(int64_t wg, int64_t total, int64_t per_head, int group,
                                          bool interleaved = false) {
   if (group <= 1) return xcd_order(wg, total);
   const int64_t xcd = wg % kXcds, local = wg / kXcds;
   const int64_t groups = kXcds / group;
-  const int64_t per = nb / group;
-  const int64_t j = local / per, blk = local - j * per;
+  const int64_t per = per_head / group;
+  const int64_t j = local / per, i = local - j * per;
   const int64_t head = xcd / group + groups * j, q = xcd % group;
-  return head * nb + (interleaved ? blk * group + q : q * per + blk);
+  return head * per_head + (interleaved ? i * group + q : q * per + i);
 }
 
 // K tile: 64 rows x D bf16 = 64 x (D/8) chunks of 16 bytes.
