@@ -284,3 +284,16 @@ def test_full_size_semantic_layer_sampled():
     perm_q = kq["perm"][0, hd].cpu().numpy()
     assert torch.equal(o[0, hd, torch.from_numpy(perm_q[rows]).to(DEV)],
                        info["op"][0, hd, torch.from_numpy(rows).to(DEV)])
+    # every query row of every head, into outputs filled with NaN beforehand:
+    # written once, bit for bit as in the layer (the pass runs in list order;
+    # its work items are spread over the XCDs by head groups)
+    seq = cabf.Seq(1, w.heads, w.head_dim, w.n)
+    op2 = torch.full_like(info["op"], float("nan"))
+    lse2 = torch.full_like(info["lse"], float("nan"))
+    ws = cabf._ws(cabf._lib.cabf_cluster_attention_workspace_bytes(cabf.ctypes.byref(seq.c()), int(w.cq),
+                                                                    int(w.ck)), DEV)
+    cabf.cabf_cluster_attention(seq, w.cq, w.ck, info["qp"], info["kp"], info["vp"], kq["offsets"],
+                                kk["offsets"], info["kv_count"], info["kv_index"], scale, op2, lse2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(op2[:, :, :n], info["op"][:, :, :n]), "rows left unwritten or different"
+    assert torch.equal(lse2[:, :, :n], info["lse"][:, :, :n]), "lse rows left unwritten or different"
