@@ -228,6 +228,20 @@ def test_backward_full_size_sampled():
         big = float(a.float().abs().max())
         say(f"full-size {nm}: clock-phased vs list order max diff {diff:.3e} (max {big:.3e})")
         assert diff <= 1e-2 * big, nm
+    # into gradients filled with NaN beforehand, both orders: every row of
+    # every head is written (pad rows with 0), so the comparison above cannot
+    # pass on untouched memory
+    bws = cabf._ws(cabf._lib.cabf_bsa_backward_workspace_bytes(cabf.ctypes.byref(g.c())), DEV)
+    for flags, ref_grads in ((0, det), (cabf.BSA_DETERMINISTIC, det)):
+        grads = [torch.full_like(qp, float("nan")) for _ in range(3)]
+        cabf.cabf_bsa_backward(g, qp, kp, vp, op, lse, dop, cnt, idx, s, *grads, bws, flags)
+        torch.cuda.synchronize()
+        for nm, a, b in zip(("dq", "dk", "dv"), grads, ref_grads):
+            assert torch.isfinite(a.float()).all(), f"{nm} rows left unwritten (flags {flags})"
+            if flags:
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), nm
+            else:
+                assert float((a.float() - b.float()).abs().max()) <= 1e-2 * float(b.float().abs().max()), nm
     hd = 0
     c0, i0 = cnt[0, hd].cpu().numpy(), idx[0, hd].cpu().numpy()
     key_blocks = [0, og.nb - 1]
